@@ -1,0 +1,627 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Every test here runs on the CPU and checks the oracle against something other
+than itself: values printed in the pages' worked examples (tests/golden/),
+closed forms, library routines with the same definition (numpy transpose,
+reshape, float32 arithmetic), exhaustive enumeration, and exact rational
+arithmetic.  None of them re-types the oracle's own formula.
+"""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import Spec, quant_type, rng, normal_f32
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_examples.json")))
+
+
+def f32_bits(x):
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def ev(spec, params):
+    return oracle.evaluate(spec.nodes, params)
+
+
+# --------------------------------------------------------------------------
+# Layout (Shapes and layout)
+# --------------------------------------------------------------------------
+def test_layout_2x3_example():
+    g = GOLD["layout_2x3"]
+    names = [c for row in g["logical"] for c in row]
+    for m2m, key in (([0, 1], "m2m_0_1"), ([1, 0], "m2m_1_0")):
+        mem = [None] * 6
+        for i in range(2):
+            for j in range(3):
+                mem[oracle.linear_index([2, 3], m2m, [i, j])] = g["logical"][i][j]
+        assert mem == g[key]
+    # through evaluation: decode with {0,1}, re-encode with {1,0}
+    phys = np.array([names.index(c) for c in g["m2m_0_1"]], dtype=np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [2, 3], [0, 1])
+    s.transpose(p, [0, 1], "f32", [2, 3], m2m=[1, 0])
+    out = ev(s, [phys])
+    assert [names[int(v)] for v in out] == g["m2m_1_0"]
+
+
+def test_default_layout_is_major_to_minor():
+    s = Spec()
+    p = s.parameter(0, "f32", [2, 3, 4])
+    s.transpose(p, [0, 1, 2], "f32", [2, 3, 4])
+    x = np.arange(24, dtype=np.float32)
+    # numpy's C order is major-to-minor: the identity re-encoding is a no-op
+    assert np.array_equal(ev(s, [x]), x)
+
+
+def test_loop_emitter_map_equals_row_major_linearization():
+    """The loop emitter's (th_x, bl_x)[v] -> (i, j, k) map followed by the
+    linear index with the default layout equals the page's flattened map
+    th_x*4 + bl_x*512 + v, over the whole domain."""
+    g = GOLD["loop_map_gelu"]
+    th = np.arange(g["th_x"], dtype=np.int64)
+    for bl0 in range(0, g["bl_x"], 4096):
+        bl = np.arange(bl0, bl0 + 4096, dtype=np.int64)
+        T, B, V = np.meshgrid(th, bl, np.arange(g["vec"]), indexing="ij")
+        i, j = B // 4096, (B // 8) % 512
+        k = (B % 8) * 512 + T * 4 + V
+        idx = np.stack([i.ravel(), j.ravel(), k.ravel()], axis=1)
+        lin = oracle.linear_indices(g["dims"], [2, 1, 0], idx)
+        assert np.array_equal(lin, (T * 4 + B * 512 + V).ravel())
+
+
+def test_layout_bijective_all_small_shapes():
+    """For every shape of rank <= 3 with dims in {1,2,3} and every m2m, the
+    linear index is a bijection onto [0, n) and matches numpy's reading of a
+    buffer laid out major-to-minor in the order m2m reversed."""
+    import itertools
+    for rank in range(1, 4):
+        for dims in itertools.product([1, 2, 3], repeat=rank):
+            n = int(np.prod(dims))
+            idx = np.array(list(itertools.product(*[range(d) for d in dims])), dtype=np.int64)
+            for m2m in itertools.permutations(range(rank)):
+                lin = oracle.linear_indices(list(dims), list(m2m), idx)
+                assert sorted(lin.tolist()) == list(range(n))
+                # numpy: physical buffer reshaped major->minor = dims[m2m[::-1]]
+                buf = np.arange(n)
+                phys = buf.reshape([dims[d] for d in m2m[::-1]])
+                logical = np.transpose(phys, np.argsort(list(m2m[::-1])))
+                assert np.array_equal(logical.reshape(-1), lin)
+
+
+# --------------------------------------------------------------------------
+# Indexing transforms
+# --------------------------------------------------------------------------
+def test_transpose_map_20x40():
+    g = GOLD["transpose_map_20x40"]
+    s = Spec()
+    p = s.parameter(0, "f32", g["in_dims"], [1, 0])
+    s.transpose(p, [1, 0], "f32", g["out_dims"], m2m=[1, 0])
+    x = np.arange(800, dtype=np.float32)
+    out = ev(s, [x]).reshape(g["out_dims"])
+    xin = x.reshape(g["in_dims"])
+    for d0 in range(40):
+        for d1 in range(20):
+            assert out[d0, d1] == xin[d1, d0]
+
+
+def test_transpose_3d_shapes_and_non_involutions():
+    """Transpose against numpy.transpose (same definition: result dim d is
+    operand dim perm[d]) for every permutation of rank 3 and 4, including the
+    non-involutions that distinguish a permutation from its inverse."""
+    import itertools
+    for dims in ([2, 3, 4], [2, 1, 3, 2]):
+        x = np.arange(int(np.prod(dims)), dtype=np.float32)
+        for perm in itertools.permutations(range(len(dims))):
+            out_dims = [dims[p] for p in perm]
+            s = Spec()
+            p = s.parameter(0, "f32", dims)
+            s.transpose(p, perm, "f32", out_dims)
+            got = ev(s, [x]).reshape(out_dims)
+            assert np.array_equal(got, np.transpose(x.reshape(dims), perm))
+    g = GOLD["transpose_shapes_20x160x170"]
+    assert [g["in_dims"][p] for p in (2, 1, 0)] == g["out_dims"]
+
+
+def test_broadcast_in_dim_example():
+    g = GOLD["broadcast_in_dim"]
+    s = Spec()
+    p = s.parameter(0, "f32", [1, 3])
+    s.broadcast_in_dim(p, g["broadcast_dimensions"], "f32", g["result_dims"])
+    out = ev(s, [np.array(g["operand"], dtype=np.float32).ravel()])
+    assert out.reshape(g["result_dims"]).tolist() == g["result"]
+
+
+def test_broadcast_against_numpy():
+    """broadcast_in_dim of [3,1] into [2,3,4] with dims {1,2}: numpy broadcasting."""
+    s = Spec()
+    p = s.parameter(0, "f32", [3, 1])
+    s.broadcast_in_dim(p, [1, 2], "f32", [2, 3, 4])
+    x = np.array([7, 8, 9], dtype=np.float32)
+    got = ev(s, [x]).reshape(2, 3, 4)
+    assert np.array_equal(got, np.broadcast_to(x.reshape(1, 3, 1), (2, 3, 4)))
+
+
+def test_reshape_examples():
+    g = GOLD["reshape_2x3_to_3x2"]
+    s = Spec()
+    p = s.parameter(0, "f32", [2, 3])
+    s.reshape(p, "f32", [3, 2])
+    assert ev(s, [np.array(g["operand"], np.float32).ravel()]).reshape(3, 2).tolist() == g["result"]
+    c = GOLD["collapse"]
+    v = np.array(c["v"], dtype=np.float32).ravel()
+    for key, dims in (("v012", [24]), ("v01", [4, 6]), ("v12", [8, 3])):
+        s = Spec()
+        p = s.parameter(0, "f32", [4, 2, 3])
+        s.reshape(p, "f32", dims)
+        assert ev(s, [v]).reshape(dims).tolist() == c[key]
+
+
+def test_reshape_with_layouts_against_numpy():
+    """Reshape is defined on logical order: with a column-major operand the
+    result still follows numpy's C-order reshape of the logical array."""
+    x = np.arange(24, dtype=np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [4, 6], [0, 1])       # column-major storage
+    s.reshape(p, "f32", [2, 12], m2m=[1, 0])
+    logical = x.reshape(6, 4).T                     # numpy reading of {0,1}
+    assert np.array_equal(ev(s, [x]).reshape(2, 12), logical.reshape(2, 12))
+
+
+# --------------------------------------------------------------------------
+# Elementwise arithmetic
+# --------------------------------------------------------------------------
+def _binary(op, lhs, rhs, dtype="f32"):
+    lhs = np.asarray(lhs, dtype=np.float32)
+    s = Spec()
+    a = s.parameter(0, dtype, list(lhs.shape))
+    b = s.parameter(1, dtype, list(lhs.shape))
+    s.binary(op, a, b, dtype, list(lhs.shape))
+    return ev(s, [lhs.ravel(), np.asarray(rhs, dtype=np.float32).ravel()]).reshape(lhs.shape)
+
+
+@pytest.mark.parametrize("op", ["add", "multiply", "maximum"])
+def test_integer_examples(op):
+    g = GOLD[op]
+    assert _binary(op, g["lhs"], g["rhs"]).tolist() == g["result"]
+
+
+def test_f32_add_mul_match_ieee_float32():
+    """f32 add/multiply/divide/subtract equal numpy's IEEE binary32 ops on random
+    operands spanning many binades (including subnormal results)."""
+    g = rng(11)
+    a = (g.standard_normal(20000) * np.exp2(g.integers(-140, 100, 20000))).astype(np.float32)
+    b = (g.standard_normal(20000) * np.exp2(g.integers(-140, 100, 20000))).astype(np.float32)
+    with np.errstate(all="ignore"):
+        for op, ref in (("add", a + b), ("multiply", a * b), ("subtract", a - b),
+                        ("divide", a / b)):
+            s = Spec()
+            x = s.parameter(0, "f32", [a.size])
+            y = s.parameter(1, "f32", [a.size])
+            s.binary(op, x, y, "f32", [a.size])
+            got = ev(s, [a, b])
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), op
+
+
+def test_convert_s32_to_f32_and_rounding():
+    g = GOLD["convert_s32_f32"]
+    s = Spec()
+    p = s.parameter(0, "s32", [3])
+    s.convert(p, "f32", [3])
+    assert ev(s, [np.array(g["input"], np.int32)]).tolist() == g["result"]
+    # int -> float rounds to nearest even: 2^24+1 -> 2^24, 2^24+3 -> 2^24+4
+    big = np.array([2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 24) - 1], np.int32)
+    s = Spec()
+    p = s.parameter(0, "s32", [3])
+    s.convert(p, "f32", [3])
+    assert ev(s, [big]).tolist() == [2.0 ** 24, 2.0 ** 24 + 4, -(2.0 ** 24)]
+
+
+def _bf16_value(bits):
+    return float(oracle.bf16_bits_to_f32(np.array([bits], np.uint16))[0])
+
+
+def _is_rne(exact: Fraction, r: float, p: int, emin: int) -> bool:
+    """Property check of round-to-nearest-even to a p-bit format, with exact
+    rationals: r is representable, no representable value is nearer, and at a
+    tie r has an even last significand bit."""
+    if r == 0:
+        e = emin
+    else:
+        e = max(math.frexp(abs(r))[1] - 1, emin)
+    q = Fraction(2) ** (e - (p - 1))
+    fr = Fraction(r)
+    m = fr / q
+    if m.denominator != 1:
+        return False
+    err = abs(exact - fr)
+    if err > q / 2:
+        # r may sit at the bottom of a binade where the spacing below halves
+        return False
+    if err == q / 2 and int(m) % 2 != 0:
+        return False
+    # the lower neighbour inside a binade boundary has spacing q/2
+    if r != 0 and abs(fr) == Fraction(2) ** e and e > emin:
+        lower = abs(fr) - q / 2
+        if abs(abs(exact) - lower) < err:
+            return False
+    return True
+
+
+def test_f32_to_bf16_rne_pages_constants():
+    """The GELU constants of the reproducer HLO round to the bf16 constants
+    printed in the emitted function (XLA:GPU Emitters)."""
+    g = GOLD["gelu_bf16_constants"]
+    for v, printed in zip(g["hlo"], g["mlir_bf16_printed"]):
+        s = Spec()
+        s.constant(v, "bf16", [1])
+        bits = int(ev(s, [])[0])
+        val = _bf16_value(bits)
+        # the printed 6-significant-digit value identifies a unique bf16
+        assert abs(val - printed) <= 5e-7 * max(1.0, abs(printed)) + 1e-12, (v, val, printed)
+        assert _is_rne(Fraction(np.float32(v).item()), val, 8, -126)
+    # exact bit patterns implied by the printed values
+    bits = []
+    for v in g["hlo"]:
+        s = Spec()
+        s.constant(v, "bf16", [1])
+        bits.append(int(ev(s, [])[0]))
+    assert bits == [0x3F00, 0x3F80, 0x3F4C, 0x3D37]
+
+
+def test_f32_to_bf16_convert_property_sample():
+    """convert f32 -> bf16 is RNE: exact-rational property check on a sample
+    of f32 patterns, including ties, subnormals and the overflow boundary."""
+    g = rng(12)
+    bits = g.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32)
+    extra = np.array([0x3F808000, 0x3F818000, 0x3F80C000, 0x00008000, 0x00018000,
+                      0x7F7F7FFF, 0x7F7F8000, 0x80008000], np.uint32)
+    bits = np.concatenate([bits, extra])
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    s = Spec()
+    p = s.parameter(0, "f32", [f.size])
+    s.convert(p, "bf16", [f.size])
+    out = ev(s, [f])
+    vals = oracle.bf16_bits_to_f32(out)
+    maxbf = Fraction(2) ** 127 * (2 - Fraction(1, 128))
+    for x, r in zip(f.tolist(), vals.tolist()):
+        ex = Fraction(x)
+        if math.isinf(r):
+            assert abs(ex) >= maxbf + Fraction(2) ** (127 - 8), x
+        else:
+            assert _is_rne(ex, r, 8, -126), (x, r)
+
+
+def test_reduce_precision_example():
+    g = GOLD["reduce_precision_e5m10"]
+    vals = [struct.unpack("<d", struct.pack("<Q", int(h, 16)))[0] if h.startswith("0x") else float(h)
+            for h in g["input_hex"]]
+    got = [oracle.round_format(v, 11, -14, 15) for v in vals]
+    for x, want in zip(got, g["output"]):
+        if want == "inf":
+            assert math.isinf(x) and x > 0
+        elif want == "nan":
+            assert math.isnan(x)
+        else:
+            assert x == want
+
+
+def test_exp_log_page_values():
+    """exp and log of the printed examples: the oracle's f32 results are the
+    f32 roundings of the page's f64 values."""
+    for op, key in (("exponential", "exponential_f64"), ("log", "log_f64")):
+        g = GOLD[key]
+        x = np.array(g["input"], np.float32)
+        s = Spec()
+        p = s.parameter(0, "f32", [4])
+        s.unary(op, p, "f32", [4])
+        out = ev(s, [x])
+        want = np.array(g["output"], dtype=np.float64).astype(np.float32)
+        assert np.array_equal(out.view(np.uint32), want.view(np.uint32)), op
+    assert [f32_bits(v) for v in np.array(GOLD["exponential_f64"]["output"]).astype(np.float32)] == \
+        [0x3F800000, 0x402DF854, 0x40EC7326, 0x41A0AF2E]
+
+
+def test_exp_bf16_exhaustive():
+    """bf16 exp over all 65536 inputs is the RNE of exp(x): checked against
+    numpy's float64 exp with a bound far below half a bf16 ulp."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = oracle.bf16_bits_to_f32(allbits)
+    fin = np.isfinite(x)
+    s = Spec()
+    p = s.parameter(0, "bf16", [65536])
+    s.unary("exponential", p, "bf16", [65536])
+    out = oracle.bf16_bits_to_f32(ev(s, [allbits]))
+    with np.errstate(over="ignore"):
+        ref = np.exp(x.astype(np.float64))
+    for xi, r, e in zip(x[fin].tolist(), out[fin].tolist(), ref[fin].tolist()):
+        if math.isinf(e) or e > 3.3e38:
+            assert math.isinf(r) or r >= 3.3e38
+            continue
+        if r == 0.0:
+            assert e < 2.0 ** -133, xi
+            continue
+        ulp = 2.0 ** (max(math.frexp(r)[1] - 1, -126) - 7)
+        assert abs(e - r) <= ulp * (0.5 + 1e-6), (xi, r, e)
+    assert np.all(np.isnan(out[~fin & np.isnan(x)]))
+
+
+def test_special_values():
+    """IEEE 754-2019 maximum and the special values of exp and log."""
+    vals = [float("nan"), -0.0, 0.0, float("-inf"), float("inf"), 1.5]
+    a = np.array([v for v in vals for _ in vals], np.float32)
+    b = np.array([w for _ in vals for w in vals], np.float32)
+    got = _binary("maximum", a.reshape(6, 6), b.reshape(6, 6)).ravel()
+    for x, y, r in zip(a.tolist(), b.tolist(), got.tolist()):
+        if math.isnan(x) or math.isnan(y):
+            assert math.isnan(r)
+        elif x == 0 and y == 0:
+            want_neg = math.copysign(1, x) < 0 and math.copysign(1, y) < 0
+            assert r == 0 and (math.copysign(1, r) < 0) == want_neg
+        else:
+            assert r == max(x, y)
+    x = np.array([1.0, 0.0, -0.0, -1.0, float("inf"), float("nan")], np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [6])
+    s.unary("log", p, "f32", [6])
+    lg = ev(s, [x])
+    assert lg[0] == 0 and math.copysign(1, lg[0]) > 0
+    assert lg[1] == -np.inf and lg[2] == -np.inf and np.isnan(lg[3])
+    assert lg[4] == np.inf and np.isnan(lg[5])
+    x = np.array([float("-inf"), float("inf"), float("nan"), 0.0, -200.0, 100.0], np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [6])
+    s.unary("exponential", p, "f32", [6])
+    ex = ev(s, [x])
+    assert ex[0] == 0 and math.copysign(1, ex[0]) > 0 and ex[1] == np.inf
+    assert np.isnan(ex[2]) and ex[3] == 1.0 and ex[4] == 0.0 and ex[5] == np.inf
+
+
+# --------------------------------------------------------------------------
+# Reduce
+# --------------------------------------------------------------------------
+def test_reduce_examples():
+    g = GOLD["reduce_sum_1x6"]
+    s = Spec()
+    p = s.parameter(0, "f32", [1, 6])
+    s.reduce(p, g["dimensions"], "add", g["init"], "f32", [1])
+    assert ev(s, [np.array(g["input"], np.float32).ravel()]).tolist() == g["result"]
+    g = GOLD["reduce_3d"]
+    x = np.tile(np.array(g["slice"], np.float32).ravel(), 4)
+    for dims, out_dims, key in (([0], [2, 3], "dim0"), ([2], [4, 2], "dim2"),
+                                ([0, 1], [3], "dims01"), ([0, 1, 2], [], "all")):
+        s = Spec()
+        p = s.parameter(0, "f32", [4, 2, 3])
+        s.reduce(p, dims, "add", 0.0, "f32", out_dims)
+        got = ev(s, [x])
+        want = g[key]
+        assert (got.reshape(out_dims).tolist() if out_dims else got[0]) == want
+
+
+def test_reduce_exact_on_integers_any_layout():
+    """Integer-valued inputs: sums are exact, so the oracle equals numpy's
+    integer sum for every reduced-dimension choice and input layout."""
+    import itertools
+    g = rng(13)
+    dims = [3, 4, 5]
+    xi = g.integers(-4, 5, 60)
+    x = xi.astype(np.float32)
+    for m2m in itertools.permutations(range(3)):
+        # physical buffer for layout m2m of the logical array xi.reshape(dims)
+        phys = np.transpose(xi.reshape(dims), list(m2m[::-1])).ravel().astype(np.float32)
+        for red in ([0], [1], [2], [0, 2], [1, 2]):
+            kept = [d for d in range(3) if d not in red]
+            s = Spec()
+            p = s.parameter(0, "f32", dims, list(m2m))
+            s.reduce(p, red, "add", 0.0, "f32", [dims[d] for d in kept])
+            got = ev(s, [phys])
+            assert np.array_equal(got, xi.reshape(dims).sum(axis=tuple(red)).ravel())
+    assert x.size == 60
+
+
+def test_reduce_max_any_order():
+    g = rng(14)
+    x = g.uniform(-100, 100, 3 * 50).astype(np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [50, 3])
+    s.reduce(p, [0], "max", float("-inf"), "f32", [3])
+    assert np.array_equal(ev(s, [x]), x.reshape(50, 3).max(axis=0))
+
+
+def test_reduce_sum_close_to_fsum():
+    """f32 reduce-add equals math.fsum of the operands rounded to f32."""
+    g = rng(15)
+    x = normal_f32(g, 5000)
+    s = Spec()
+    p = s.parameter(0, "f32", [5000])
+    s.reduce(p, [0], "add", 0.0, "f32", [])
+    assert ev(s, [x])[0] == np.float32(math.fsum(x.astype(np.float64).tolist()))
+
+
+# --------------------------------------------------------------------------
+# Quantization (StableHLO Specification "Types"; StableHLO Quantization)
+# --------------------------------------------------------------------------
+def _dequant_spec(dims, q):
+    s = Spec()
+    p = s.parameter(0, "s8", dims, quant=q)
+    s.op("uniform_dequantize", [p], "f32", dims)
+    return s
+
+
+def test_per_axis_dequantize_slices():
+    g = GOLD["per_axis_type"]
+    q = quant_type("s8", g["scales"], g["zero_points"], qdim=g["qdim"])
+    allq = np.arange(-128, 128, dtype=np.int8)
+    # every q value appears in every slice t[:, j, :]
+    x = np.resize(allq, 4 * 3 * 2 * 11)[: 4 * 3 * 2]
+    for shift in range(0, 256, 24):
+        xs = np.roll(allq, shift)[:24].astype(np.int8)
+        out = ev(_dequant_spec(g["dims"], q), [xs]).reshape(g["dims"])
+        xl = xs.reshape(g["dims"])
+        for j in range(3):
+            sc = np.float32(g["scales"][j])
+            want = sc * (xl[:, j, :].astype(np.float32) - np.float32(g["zero_points"][j]))
+            assert np.array_equal(out[:, j, :].view(np.uint32), want.astype(np.float32).view(np.uint32))
+    assert x.size == 24
+    # specific values: each slice's zero point maps to 0.0
+    xs = np.broadcast_to(np.array([20, 10, 30], np.int8).reshape(1, 3, 1), (4, 3, 2)).copy()
+    assert np.all(ev(_dequant_spec(g["dims"], q), [xs.ravel()]) == 0.0)
+
+
+def test_per_tensor_dequantize_example_type():
+    g = GOLD["per_tensor_type"]
+    q = quant_type("s8", [g["scale"]], [g["zero_point"]])
+    xs = np.array([50, 0, 127, -128], np.int8)
+    out = ev(_dequant_spec([4], q), [xs])
+    want = np.float32(g["scale"]) * (xs.astype(np.float32) - np.float32(g["zero_point"]))
+    assert np.array_equal(out, want.astype(np.float32))
+    assert out[0] == 0.0 and out[1] == np.float32(-0.5)
+
+
+def _quant_spec(n, q, src="f32"):
+    s = Spec()
+    p = s.parameter(0, src, [n])
+    s.op("uniform_quantize", [p], "s8", [n], quant=q)
+    return s
+
+
+def test_quantize_ties_to_even():
+    g = GOLD["round_nearest_even"]
+    q = quant_type("s8", [1.0], [0])
+    out = ev(_quant_spec(5, q), [np.array(g["input"], np.float32)])
+    assert out.tolist() == [int(v) for v in g["even"]]
+    assert out.tolist() != [int(v) for v in g["afz"]]
+
+
+def test_quantize_clamp_example():
+    g = GOLD["clamp"]
+    q = quant_type("s8", [1.0], [0], storage_min=g["min"], storage_max=g["max"])
+    out = ev(_quant_spec(3, q), [np.array(g["operand"], np.float32)])
+    assert out.tolist() == g["result"]
+
+
+def test_quantize_divides_then_rounds_then_adds_zero_point():
+    """Reading adopted for uniform_quantize: t = f32(y / scale) by IEEE
+    division, ties-to-even, zero point added as an integer, then clamp.
+    Checked against numpy's float32 division and rint on many values, and on
+    the cases where dividing and multiplying by the reciprocal differ."""
+    g = rng(16)
+    y = (g.standard_normal(200000) * 2.0).astype(np.float32)
+    for scale, zp in ((0.02, 0), (0.02, 7), (0.0137, -20)):
+        q = quant_type("s8", [scale], [zp])
+        got = ev(_quant_spec(y.size, q), [y]).astype(np.int64)
+        t = (y / np.float32(scale)).astype(np.float32)
+        want = np.clip(np.rint(t).astype(np.int64) + zp, -128, 127)
+        assert np.array_equal(got, want)
+    # zero point after rounding: 0.5 + 7 -> rint(0.5) + 7 = 7, not rint(7.5) = 8
+    q = quant_type("s8", [1.0], [7])
+    assert ev(_quant_spec(1, q), [np.array([0.5], np.float32)]).tolist() == [7]
+    # Near the rounding ties, dividing by the scale and multiplying by its
+    # rounded reciprocal give different integers; the oracle must divide.
+    sc = np.float32(0.02)
+    centers = ((np.arange(-130, 130) + 0.5) * 0.02).astype(np.float32).view(np.int32)
+    yt = np.concatenate([(centers + off).view(np.float32) for off in range(-40, 41)])
+    recip = (yt * (np.float32(1.0) / sc)).astype(np.float32)
+    diff = np.rint(yt / sc) != np.rint(recip)
+    assert diff.sum() > 10
+    q = quant_type("s8", [0.02], [0])
+    got = ev(_quant_spec(yt.size, q), [yt]).astype(np.int64)
+    assert np.array_equal(got, np.clip(np.rint(yt / sc).astype(np.int64), -128, 127))
+
+
+def test_requantize_identity_per_axis():
+    """quantize(dequantize(q)) == q for every storage value and slice of the
+    pages' per-axis type (t[4,3,2], qdim 1, {0.2:20, 0.1:10, 0.3:30})."""
+    g = GOLD["per_axis_type"]
+    qa = quant_type("s8", g["scales"], g["zero_points"], qdim=1)
+    allq = np.arange(-128, 128, dtype=np.int8)
+    for j in range(3):
+        dims = [256, 3, 1]
+        x = np.zeros((256, 3, 1), np.int8)
+        x[:, :, 0] = allq[:, None]
+        s = Spec()
+        p = s.parameter(0, "s8", dims, quant=qa)
+        d = s.op("uniform_dequantize", [p], "f32", dims)
+        s.op("uniform_quantize", [d], "s8", dims, quant=qa)
+        out = ev(s, [x.ravel()])
+        assert np.array_equal(out, x.ravel()), j
+
+
+def test_requantize_direct():
+    """uniform_quantize of a quantized operand (requantize) dequantizes first."""
+    qi = quant_type("s8", [0.1], [3])
+    qo = quant_type("s8", [0.05], [-2])
+    x = np.arange(-128, 128, dtype=np.int8)
+    s = Spec()
+    p = s.parameter(0, "s8", [256], quant=qi)
+    s.op("uniform_quantize", [p], "s8", [256], quant=qo)
+    got = ev(s, [x]).astype(np.int64)
+    deq = (np.float32(0.1) * (x.astype(np.float32) - np.float32(3))).astype(np.float32)
+    want = np.clip(np.rint((deq / np.float32(0.05)).astype(np.float32)).astype(np.int64) - 2, -128, 127)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# The pages' example program (StableHLO Specification, "Programs")
+# --------------------------------------------------------------------------
+def test_program_28x28_selection_weights():
+    g = rng(17)
+    image = g.uniform(-1, 1, 784).astype(np.float32)
+    bias = g.uniform(-1, 1, 10).astype(np.float32)
+    sel = g.choice(784, 10, replace=False)
+    w = np.zeros((784, 10), np.float32)
+    w[sel, np.arange(10)] = 1.0
+    s = Spec()
+    im = s.parameter(0, "f32", [28, 28])
+    wt = s.parameter(1, "f32", [784, 10])
+    bs = s.parameter(2, "f32", [1, 10])
+    r = s.reshape(im, "f32", [1, 784])
+    d = s.op("dot", [r, wt], "f32", [1, 10])
+    a = s.binary("add", d, bs, "f32", [1, 10])
+    z = s.constant(0.0, "f32", [1, 10])
+    s.binary("maximum", a, z, "f32", [1, 10])
+    out = ev(s, [image, w.ravel(), bias])
+    want = np.maximum(image[sel] + bias, np.float32(0))
+    assert np.array_equal(out, want)
+
+
+def test_evaluate_points_matches_whole():
+    s = Spec()
+    p = s.parameter(0, "f32", [5, 7], [0, 1])
+    e = s.unary("exponential", p, "f32", [5, 7])
+    s.reduce(e, [1], "add", 0.0, "f32", [5])
+    x = normal_f32(rng(18), 35)
+    whole = ev(s, [x])
+    vals, aux = oracle.evaluate_points(s.nodes, [x], [[i] for i in range(5)])
+    assert np.array_equal(vals.astype(np.float32), whole)
+    xl = x.reshape(7, 5).T.astype(np.float64)
+    assert np.allclose(aux[:, 0], np.abs(np.exp(xl.astype(np.float32))).sum(axis=1), rtol=1e-6)
+
+
+def test_exp_log_f32_correctly_rounded_sample():
+    """f32 exp and log are correctly rounded: equal to numpy's float64 result
+    rounded to f32 wherever that f64 value is not within 1e-12 (relative) of
+    an f32 rounding boundary."""
+    g = rng(19)
+    for op, x, ref in (
+        ("exponential", g.uniform(-87, 88, 100000).astype(np.float32), np.exp),
+        ("log", np.exp2(g.uniform(-140, 127, 100000)).astype(np.float32), np.log),
+    ):
+        s = Spec()
+        p = s.parameter(0, "f32", [x.size])
+        s.unary(op, p, "f32", [x.size])
+        got = ev(s, [x])
+        r64 = ref(x.astype(np.float64))
+        want = r64.astype(np.float32)
+        # distance of the f64 value to the midpoint between want and its neighbour
+        nb = np.nextafter(want, np.where(r64 > want, np.inf, -np.inf).astype(np.float32))
+        mid = (want.astype(np.float64) + nb.astype(np.float64)) / 2
+        safe = np.abs(r64 - mid) > 1e-12 * np.abs(r64)
+        assert safe.mean() > 0.999
+        assert np.array_equal(got[safe].view(np.uint32), want[safe].view(np.uint32)), op

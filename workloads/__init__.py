@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs and neutral fusion descriptions.
+
+This module is shared by the tests, the benchmark, the oracle binding and the
+product binding.  It holds NO arithmetic of the method: no layout mapping, no
+rounding, no op semantics.  It only
+
+  * draws random buffers from numpy's PCG64 with fixed seeds, directly in
+    physical (storage) order -- the values are i.i.d., so their distribution
+    does not depend on the layout the fusion declares for them; and
+  * writes fusions down as plain node lists (dicts), each node stating its own
+    result type the way HLO text does.
+
+bf16 inputs are drawn as float32 and keep the upper 16 bits of the float32
+pattern (truncation), which defines a bf16 distribution without using the
+method's round-to-nearest-even conversion.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# generators
+# --------------------------------------------------------------------------
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def uniform_f32(g: np.random.Generator, n: int, lo: float, hi: float) -> np.ndarray:
+    return g.uniform(lo, hi, size=n).astype(np.float32)
+
+
+def normal_f32(g: np.random.Generator, n: int, sigma: float = 1.0) -> np.ndarray:
+    return (g.standard_normal(size=n) * sigma).astype(np.float32)
+
+
+def normal_bf16(g: np.random.Generator, n: int, sigma: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns (uint16): upper half of a float32 normal draw."""
+    f = normal_f32(g, n, sigma)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def integers(g: np.random.Generator, n: int, lo: int, hi: int, dtype) -> np.ndarray:
+    """Uniform integers in [lo, hi] inclusive."""
+    return g.integers(lo, hi, size=n, endpoint=True).astype(dtype)
+
+
+# --------------------------------------------------------------------------
+# node-list recorder (no shape inference: every node states its type)
+# --------------------------------------------------------------------------
+class Spec:
+    def __init__(self):
+        self.nodes: list[dict] = []
+
+    def _add(self, **nd) -> int:
+        self.nodes.append(nd)
+        return len(self.nodes) - 1
+
+    def parameter(self, index, dtype, dims, m2m=None, quant=None) -> int:
+        return self._add(op="parameter", param=index, operands=[], dtype=dtype,
+                         dims=list(dims), m2m=m2m, quant=quant)
+
+    def constant(self, value, dtype, dims) -> int:
+        return self._add(op="constant", operands=[], value=float(value), dtype=dtype,
+                         dims=list(dims))
+
+    def op(self, name, operands, dtype, dims, m2m=None, quant=None, **attrs) -> int:
+        return self._add(op=name, operands=list(operands), dtype=dtype, dims=list(dims),
+                         m2m=m2m, quant=quant, **attrs)
+
+    def unary(self, name, x, dtype, dims, m2m=None) -> int:
+        return self.op(name, [x], dtype, dims, m2m)
+
+    def binary(self, name, a, b, dtype, dims, m2m=None) -> int:
+        return self.op(name, [a, b], dtype, dims, m2m)
+
+    def transpose(self, x, perm, dtype, dims, m2m=None) -> int:
+        return self.op("transpose", [x], dtype, dims, m2m, permutation=list(perm))
+
+    def broadcast_in_dim(self, x, bdims, dtype, dims, m2m=None) -> int:
+        return self.op("broadcast_in_dim", [x], dtype, dims, m2m,
+                       broadcast_dimensions=list(bdims))
+
+    def reshape(self, x, dtype, dims, m2m=None) -> int:
+        return self.op("reshape", [x], dtype, dims, m2m)
+
+    def reduce(self, x, dims_to_reduce, reducer, init, dtype, dims, m2m=None) -> int:
+        return self.op("reduce", [x], dtype, dims, m2m, dimensions=list(dims_to_reduce),
+                       reducer=reducer, init=float(init))
+
+    def convert(self, x, dtype, dims, m2m=None) -> int:
+        return self.op("convert", [x], dtype, dims, m2m)
+
+    def set_root_layout(self, m2m) -> None:
+        self.nodes[-1]["m2m"] = list(m2m)
+
+
+def quant_type(storage, scales, zero_points, qdim=None, storage_min=None,
+               storage_max=None) -> dict:
+    q = {"storage": storage, "expressed": "f32", "qdim": qdim,
+         "scales": np.asarray(scales, dtype=np.float32),
+         "zero_points": np.asarray(zero_points, dtype=np.int64)}
+    if storage_min is not None:
+        q["storage_min"] = int(storage_min)
+    if storage_max is not None:
+        q["storage_max"] = int(storage_max)
+    return q
+
+
+def nbytes_of(dtype: str) -> int:
+    return {"f32": 4, "bf16": 2, "f16": 2, "s8": 1, "u8": 1, "s32": 4}[dtype]
+
+
+def numel(dims) -> int:
+    n = 1
+    for d in dims:
+        n *= int(d)
+    return n
+
+
+# --------------------------------------------------------------------------
+# The five workloads.  Each builder takes its shape so the tests can run the
+# same fusion at small, ragged sizes; the defaults are the full sizes.
+# A workload is (spec, params, meta) with params as flat physical buffers.
+# --------------------------------------------------------------------------
+def loop_log_transpose_add(n0=64, n1=None, seed=1):
+    """p = param; l = log(p); t = transpose(l, {1,0}); out = add(l, t).
+
+    Square f32[n,n], row-major; p ~ U(0.1, 10).  `l` is read through two index
+    maps (identity and transposed)."""
+    n1 = n0 if n1 is None else n1
+    assert n0 == n1, "add(l, transpose(l)) needs a square operand"
+    g = rng(seed)
+    s = Spec()
+    p = s.parameter(0, "f32", [n0, n1], [1, 0])
+    l = s.unary("log", p, "f32", [n0, n1])
+    t = s.transpose(l, [1, 0], "f32", [n1, n0])
+    s.binary("add", l, t, "f32", [n0, n1], m2m=[1, 0])
+    x = uniform_f32(g, n0 * n1, 0.1, 10.0)
+    return s, [x], {"name": "loop_log_transpose_add", "elements": n0 * n1,
+                    "bytes": 2 * 4 * n0 * n1}
+
+
+def transpose_exp_f32(n0=4096, n1=4096, seed=2):
+    """out = transpose(exp(x), {1,0}); x f32[n0,n1] ~ N(0,1), row-major in and out."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [n0, n1], [1, 0])
+    e = s.unary("exponential", x, "f32", [n0, n1])
+    s.transpose(e, [1, 0], "f32", [n1, n0], m2m=[1, 0])
+    return s, [normal_f32(g, n0 * n1)], {"name": "transpose_exp_f32",
+                                         "elements": n0 * n1, "bytes": 8 * n0 * n1}
+
+
+def transpose_bf16_021(b=64, m=512, n=1024, seed=3):
+    """out = transpose(x, {0,2,1}); x bf16[b,m,n] ~ N(0,1), row-major in and out."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "bf16", [b, m, n], [2, 1, 0])
+    s.transpose(x, [0, 2, 1], "bf16", [b, n, m], m2m=[2, 1, 0])
+    return s, [normal_bf16(g, b * m * n)], {"name": "transpose_bf16_021",
+                                             "elements": b * m * n, "bytes": 4 * b * m * n}
+
+
+def row_reduce_exp_add_bf16(d0=8, d2=1280, d3=16384, m2m=(3, 2, 1, 0), seed=4):
+    """y = add(exp(x), broadcast(b, dims={3})) in bf16; out f32[d0,1,d2] =
+    reduce-sum over dim 3 of convert(y, f32), init 0."""
+    g = rng(seed)
+    s = Spec()
+    dims = [d0, 1, d2, d3]
+    x = s.parameter(0, "bf16", dims, list(m2m))
+    bb = s.parameter(1, "bf16", [d3], [0])
+    e = s.unary("exponential", x, "bf16", dims)
+    bc = s.broadcast_in_dim(bb, [3], "bf16", dims)
+    y = s.binary("add", e, bc, "bf16", dims)
+    c = s.convert(y, "f32", dims)
+    s.reduce(c, [3], "add", 0.0, "f32", [d0, 1, d2], m2m=[2, 1, 0])
+    xs = normal_bf16(g, d0 * d2 * d3)
+    bs = normal_bf16(g, d3)
+    n = d0 * d2 * d3
+    return s, [xs, bs], {"name": "row_reduce_exp_add_bf16", "elements": n,
+                         "bytes": 2 * n + 2 * d3 + 4 * d0 * d2}
+
+
+def column_reduce_max_f32(r=16384, c=4096, m2m=(1, 0), seed=5):
+    """out f32[c] = reduce-max over dim 0 of x f32[r,c], init -inf.
+    x ~ U(-100, 100).  With m2m (0,1) the buffer holds the column-major
+    storage; the test derives it from the row-major draw."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [r, c], list(m2m))
+    s.reduce(x, [0], "max", float("-inf"), "f32", [c], m2m=[0])
+    return s, [uniform_f32(g, r * c, -100.0, 100.0)], {
+        "name": "column_reduce_max_f32", "elements": r * c, "bytes": 4 * r * c + 4 * c}
+
+
+def quant_dequant_bias_requant(r=4096, c=4096, seed=6, out_scale=0.02, out_zp=0):
+    """Per-axis dequantize (qdim=1) of q i8[r,c], add f32 bias[c] broadcast on
+    dim 1, requantize per-tensor i8 (scale 0.02, zero point 0)."""
+    g = rng(seed)
+    q = integers(g, r * c, -128, 127, np.int8)
+    scales = uniform_f32(g, c, 0.001, 0.05)
+    zps = integers(g, c, -20, 20, np.int64)
+    bias = normal_f32(g, c, 0.1)
+    s = Spec()
+    qin = quant_type("s8", scales, zps, qdim=1)
+    qout = quant_type("s8", [out_scale], [out_zp])
+    p = s.parameter(0, "s8", [r, c], [1, 0], quant=qin)
+    bb = s.parameter(1, "f32", [c], [0])
+    d = s.op("uniform_dequantize", [p], "f32", [r, c])
+    bc = s.broadcast_in_dim(bb, [1], "f32", [r, c])
+    y = s.binary("add", d, bc, "f32", [r, c])
+    s.op("uniform_quantize", [y], "s8", [r, c], m2m=[1, 0], quant=qout)
+    return s, [q, bias], {"name": "quant_dequant_bias_requant", "elements": r * c,
+                          "bytes": 2 * r * c + 4 * c + 4 * c + 4 * c}
+
+
+def gelu_bf16(d0=6, d1=512, d2=4096, seed=7):
+    """The GELU loop fusion in bf16 (tanh form), every op rounding to bf16."""
+    g = rng(seed)
+    s = Spec()
+    dims = [d0, d1, d2]
+    x = s.parameter(0, "bf16", dims, [2, 1, 0])
+    c05 = s.constant(0.5, "bf16", dims)
+    c1 = s.constant(1.0, "bf16", dims)
+    c2 = s.constant(0.79785, "bf16", dims)
+    c3 = s.constant(0.044708, "bf16", dims)
+    sq = s.binary("multiply", x, x, "bf16", dims)
+    cube = s.binary("multiply", sq, x, "bf16", dims)
+    m3 = s.binary("multiply", cube, c3, "bf16", dims)
+    a1 = s.binary("add", x, m3, "bf16", dims)
+    m2 = s.binary("multiply", a1, c2, "bf16", dims)
+    th = s.unary("tanh", m2, "bf16", dims)
+    a0 = s.binary("add", th, c1, "bf16", dims)
+    m1 = s.binary("multiply", a0, c05, "bf16", dims)
+    s.binary("multiply", x, m1, "bf16", dims, m2m=[2, 1, 0])
+    n = d0 * d1 * d2
+    return s, [normal_bf16(g, n)], {"name": "gelu_bf16", "elements": n, "bytes": 4 * n}
