@@ -1,0 +1,348 @@
+// intake.cpp -- descriptor intake and validation.
+//
+// Each check below is a constraint of the op as the StableHLO Specification
+// ("Ops", the Constraints list of each op) or the "Types" section states it;
+// a broken constraint is HF_ERR_INVALID.  Valid fusions outside what the
+// library implements are HF_ERR_UNSUPPORTED.  All of it runs on the host.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <sstream>
+
+#include "ir.h"
+
+namespace hf {
+
+void fail(hf_status st, const std::string &msg) { throw Error{st, msg}; }
+
+int dtype_bytes(hf_dtype dt) {
+  switch (dt) {
+    case HF_F32: case HF_S32: return 4;
+    case HF_BF16: case HF_F16: return 2;
+    case HF_S8: case HF_U8: return 1;
+  }
+  return 0;
+}
+
+bool is_float(hf_dtype dt) { return dt == HF_F32 || dt == HF_BF16 || dt == HF_F16; }
+
+const char *dtype_name(hf_dtype dt) {
+  switch (dt) {
+    case HF_F32: return "f32";
+    case HF_BF16: return "bf16";
+    case HF_F16: return "f16";
+    case HF_S8: return "s8";
+    case HF_U8: return "u8";
+    case HF_S32: return "s32";
+  }
+  return "?";
+}
+
+const char *op_name(hf_op op) {
+  switch (op) {
+    case HF_PARAMETER: return "parameter";
+    case HF_CONSTANT: return "constant";
+    case HF_ADD: return "add";
+    case HF_SUBTRACT: return "subtract";
+    case HF_MULTIPLY: return "multiply";
+    case HF_DIVIDE: return "divide";
+    case HF_MAXIMUM: return "maximum";
+    case HF_MINIMUM: return "minimum";
+    case HF_LOG: return "log";
+    case HF_EXP: return "exponential";
+    case HF_TANH: return "tanh";
+    case HF_NEGATE: return "negate";
+    case HF_ABS: return "abs";
+    case HF_CONVERT: return "convert";
+    case HF_BROADCAST_IN_DIM: return "broadcast_in_dim";
+    case HF_RESHAPE: return "reshape";
+    case HF_TRANSPOSE: return "transpose";
+    case HF_UNIFORM_DEQUANTIZE: return "uniform_dequantize";
+    case HF_UNIFORM_QUANTIZE: return "uniform_quantize";
+    case HF_REDUCE: return "reduce";
+  }
+  return "?";
+}
+
+namespace {
+
+struct Ctx {
+  int node;
+  hf_op op;
+  std::string where() const {
+    std::ostringstream s;
+    s << "node " << node << " (" << op_name(op) << "): ";
+    return s.str();
+  }
+  [[noreturn]] void invalid(const std::string &m) const { fail(HF_ERR_INVALID, where() + m); }
+  [[noreturn]] void unsupported(const std::string &m) const { fail(HF_ERR_UNSUPPORTED, where() + m); }
+};
+
+bool valid_dtype(int dt) { return dt >= HF_F32 && dt <= HF_S32; }
+
+std::string dims_str(const Type &t) {
+  std::ostringstream s;
+  s << dtype_name(t.dt) << "[";
+  for (int d = 0; d < t.rank; ++d) s << (d ? "," : "") << t.dims[d];
+  s << "]";
+  return s.str();
+}
+
+// Type intake: shape, layout (a permutation of [0, rank)), quantization
+// constraints C1-C13 of quantized element types.
+Type take_type(const hf_type &src, Graph &g, const Ctx &c) {
+  Type t;
+  if (!valid_dtype(src.dtype)) c.invalid("unknown element type");
+  t.dt = src.dtype;
+  if (src.rank < 0 || src.rank > HF_MAX_RANK) c.invalid("rank out of range [0, 8]");
+  t.rank = src.rank;
+  for (int d = 0; d < t.rank; ++d) {
+    if (src.dims[d] < 0) c.invalid("negative dimension size");
+    t.dims[d] = src.dims[d];
+  }
+  if (src.has_layout) {
+    bool seen[HF_MAX_RANK] = {false};
+    for (int k = 0; k < t.rank; ++k) {
+      int d = src.minor_to_major[k];
+      if (d < 0 || d >= t.rank || seen[d]) {
+        std::ostringstream s;
+        s << "minor_to_major is not a permutation of [0," << t.rank << ")";
+        c.invalid(s.str());
+      }
+      seen[d] = true;
+      t.m2m[k] = d;
+    }
+  } else {
+    for (int k = 0; k < t.rank; ++k) t.m2m[k] = t.rank - 1 - k;  // default: major to minor
+  }
+  // kernels index with 32-bit offsets
+  int64_t n = 1;
+  for (int d = 0; d < t.rank; ++d) {
+    if (t.dims[d] > 0 && n > (int64_t(1) << 40) / t.dims[d]) c.unsupported("array too large");
+    n *= t.dims[d];
+  }
+  if (n * dtype_bytes(t.dt) >= (int64_t(1) << 31)) c.unsupported("array of 2 GiB or more");
+  if (src.quant) {
+    const hf_quant &q = *src.quant;
+    if (t.dt != HF_S8 && t.dt != HF_U8)
+      c.unsupported("quantized storage type must be s8 or u8");
+    Quant qq;
+    qq.storage = t.dt;
+    int32_t tmin = t.dt == HF_S8 ? -128 : 0, tmax = t.dt == HF_S8 ? 127 : 255;
+    qq.smin = q.has_storage_range ? q.storage_min : tmin;
+    qq.smax = q.has_storage_range ? q.storage_max : tmax;
+    if (!(tmin <= qq.smin && qq.smin < qq.smax && qq.smax <= tmax))
+      c.invalid("storage_min/storage_max break min(storage) <= storage_min < storage_max <= max(storage) (C4)");
+    if (q.n < 1 || !q.scales || !q.zero_points) c.invalid("quantization parameters missing");
+    if (q.quantization_dimension < 0) {
+      if (q.quantization_dimension != -1) c.invalid("quantization_dimension must be >= 0 (C12) or -1");
+      if (q.n != 1) c.invalid("per-tensor quantization needs exactly one scale (C11)");
+    } else {
+      if (q.quantization_dimension >= t.rank) c.invalid("quantization_dimension < rank violated (C12)");
+      if (q.n != t.dims[q.quantization_dimension])
+        c.invalid("dim(quantization_dimension) = size(scales) violated (C13)");
+    }
+    qq.qdim = q.quantization_dimension;
+    for (int i = 0; i < q.n; ++i) {
+      float s = q.scales[i];
+      if (!std::isfinite(s)) c.invalid("scales must be finite (C7)");
+      if (!(s > 0.0f)) c.invalid("scales must be > 0 (C6)");
+      if (q.zero_points[i] < qq.smin || q.zero_points[i] > qq.smax)
+        c.invalid("storage_min <= zero_points <= storage_max violated (C8)");
+      qq.scales.push_back(s);
+      qq.zero_points.push_back(q.zero_points[i]);
+    }
+    t.quant = (int)g.quants.size();
+    g.quants.push_back(std::move(qq));
+  }
+  return t;
+}
+
+void need_operands(const hf_node &n, int k, const Ctx &c) {
+  if (n.n_operands != k) {
+    std::ostringstream s;
+    s << "expects " << k << " operand(s), got " << n.n_operands;
+    c.invalid(s.str());
+  }
+}
+
+}  // namespace
+
+Graph intake(const hf_fusion_desc *desc) {
+  if (!desc) fail(HF_ERR_INVALID, "descriptor is NULL");
+  if (desc->abi_version != HF_ABI_VERSION) fail(HF_ERR_INVALID, "abi_version mismatch");
+  if (desc->n_nodes < 1 || desc->n_nodes > HF_MAX_NODES || !desc->nodes)
+    fail(HF_ERR_INVALID, "n_nodes out of range [1, 256] or nodes NULL");
+  if (desc->n_params < 0 || desc->n_params > HF_MAX_PARAMS)
+    fail(HF_ERR_INVALID, "n_params out of range [0, 16]");
+  if (desc->root < 0 || desc->root >= desc->n_nodes) fail(HF_ERR_INVALID, "root out of range");
+
+  Graph g;
+  g.n_params = desc->n_params;
+  g.root = desc->root;
+  g.param_node.assign(g.n_params, -1);
+  g.nodes.resize(desc->n_nodes);
+
+  for (int i = 0; i < desc->n_nodes; ++i) {
+    const hf_node &src = desc->nodes[i];
+    Ctx c{i, src.op};
+    if (src.op < HF_PARAMETER || src.op > HF_REDUCE) fail(HF_ERR_INVALID, "node " + std::to_string(i) + ": unknown op");
+    Node &n = g.nodes[i];
+    n.op = src.op;
+    if (src.n_operands < 0 || src.n_operands > 2) c.invalid("n_operands out of range");
+    for (int k = 0; k < src.n_operands; ++k) {
+      int o = src.operands[k];
+      if (o < 0 || o >= i) c.invalid("operand must be an earlier node");
+      n.opd.push_back(o);
+    }
+    n.t = take_type(src.type, g, c);
+    if (src.n_attr < 0 || src.n_attr > HF_MAX_RANK) c.invalid("n_attr out of range");
+    for (int k = 0; k < src.n_attr; ++k) n.attr.push_back(src.attr[k]);
+    n.param = src.parameter_number;
+    n.cst = src.constant;
+    n.reducer = src.reducer;
+    n.init = src.init_value;
+
+    const Type &t = n.t;
+    auto opt = [&](int k) -> const Type & { return g.nodes[n.opd[k]].t; };
+    bool quantized = t.quant >= 0;
+
+    switch (src.op) {
+      case HF_PARAMETER:
+        need_operands(src, 0, c);
+        if (n.param < 0 || n.param >= g.n_params) c.invalid("parameter_number out of range [0, n_params)");
+        if (g.param_node[n.param] >= 0) c.invalid("parameter_number used twice");
+        g.param_node[n.param] = i;
+        break;
+      case HF_CONSTANT:
+        need_operands(src, 0, c);
+        if (!is_float(t.dt) || quantized) c.unsupported("only floating-point constants are supported");
+        break;
+      case HF_LOG: case HF_EXP: case HF_TANH: case HF_NEGATE: case HF_ABS:
+        need_operands(src, 1, c);
+        if (!t.same_shape(opt(0)) || t.dt != opt(0).dt)
+          c.invalid("baseline_type(operand) = baseline_type(result) violated (C1): " +
+                    dims_str(opt(0)) + " vs " + dims_str(t));
+        if (!is_float(t.dt) || quantized || opt(0).quant >= 0)
+          c.unsupported("only non-quantized floating-point element types are supported");
+        break;
+      case HF_ADD: case HF_SUBTRACT: case HF_MULTIPLY: case HF_DIVIDE:
+      case HF_MAXIMUM: case HF_MINIMUM:
+        need_operands(src, 2, c);
+        if (!t.same_shape(opt(0)) || !t.same_shape(opt(1)) || t.dt != opt(0).dt || t.dt != opt(1).dt)
+          c.invalid("baseline_type(lhs) = baseline_type(rhs) = baseline_type(result) violated (C1): " +
+                    dims_str(opt(0)) + ", " + dims_str(opt(1)) + " -> " + dims_str(t));
+        if (!is_float(t.dt) || quantized || opt(0).quant >= 0 || opt(1).quant >= 0)
+          c.unsupported("only non-quantized floating-point element types are supported");
+        break;
+      case HF_CONVERT:
+        need_operands(src, 1, c);
+        if (!t.same_shape(opt(0))) c.invalid("shape(operand) = shape(result) violated (C1)");
+        if (quantized || opt(0).quant >= 0)
+          c.unsupported("convert of quantized types: use uniform_quantize/uniform_dequantize");
+        if (!is_float(t.dt)) c.unsupported("conversion to an integer type is not supported");
+        if (opt(0).dt == HF_S32 && t.dt != HF_F32)
+          c.unsupported("s32 converts to f32 only");
+        break;
+      case HF_BROADCAST_IN_DIM: {
+        need_operands(src, 1, c);
+        const Type &o = opt(0);
+        if (t.dt != o.dt) c.invalid("element_type(operand) = element_type(result) violated (C1)");
+        if (quantized || o.quant >= 0) c.unsupported("broadcast of quantized values");
+        if ((int)n.attr.size() != o.rank) c.invalid("size(broadcast_dimensions) = rank(operand) violated (C2)");
+        bool seen[HF_MAX_RANK] = {false};
+        for (int d = 0; d < o.rank; ++d) {
+          int64_t bd = n.attr[d];
+          if (bd < 0 || bd >= t.rank) c.invalid("0 <= broadcast_dimensions < rank(result) violated (C3)");
+          if (seen[bd]) c.invalid("is_unique(broadcast_dimensions) violated (C4)");
+          seen[bd] = true;
+          if (o.dims[d] != 1 && o.dims[d] != t.dims[bd])
+            c.invalid("dim(operand, d) = 1 or dim(result, broadcast_dimensions[d]) violated (C5)");
+        }
+        break;
+      }
+      case HF_RESHAPE:
+        need_operands(src, 1, c);
+        if (t.dt != opt(0).dt) c.invalid("element types differ (C1)");
+        if (t.numel() != opt(0).numel()) c.invalid("size(operand) = size(result) violated (C2)");
+        if (quantized || opt(0).quant >= 0) c.unsupported("reshape of quantized values");
+        break;
+      case HF_TRANSPOSE: {
+        need_operands(src, 1, c);
+        const Type &o = opt(0);
+        if (t.dt != o.dt) c.invalid("element types differ");
+        if (quantized || o.quant >= 0) c.unsupported("transpose of quantized values");
+        if ((int)n.attr.size() != t.rank || o.rank != t.rank) c.invalid("permutation length must equal rank");
+        bool seen[HF_MAX_RANK] = {false};
+        for (int d = 0; d < t.rank; ++d) {
+          int64_t p = n.attr[d];
+          if (p < 0 || p >= t.rank || seen[p]) {
+            std::ostringstream s;
+            s << "attr is not a permutation of [0," << t.rank << ")";
+            c.invalid(s.str());
+          }
+          seen[p] = true;
+          if (t.dims[d] != o.dims[p]) c.invalid("dim(result, d) = dim(operand, permutation[d]) violated");
+        }
+        break;
+      }
+      case HF_UNIFORM_DEQUANTIZE:
+        need_operands(src, 1, c);
+        if (opt(0).quant < 0) c.invalid("operand must have a quantized element type");
+        if (quantized || t.dt != HF_F32) c.unsupported("the expressed type must be f32");
+        if (!t.same_shape(opt(0))) c.invalid("shape(operand) = shape(result) violated");
+        break;
+      case HF_UNIFORM_QUANTIZE:
+        need_operands(src, 1, c);
+        if (!quantized) c.invalid("result must have a quantized element type");
+        if (!t.same_shape(opt(0))) c.invalid("shape(operand) = shape(result) violated");
+        if (opt(0).quant < 0 && opt(0).dt != HF_F32) c.unsupported("operand must be f32 or quantized");
+        break;
+      case HF_REDUCE: {
+        need_operands(src, 1, c);
+        const Type &o = opt(0);
+        if (t.dt != o.dt) c.invalid("element_type(inputs) = element_type(init_values) = result type violated (C2, C8)");
+        if (!is_float(t.dt) || o.quant >= 0) c.unsupported("only floating-point reductions are supported");
+        if (src.reducer < HF_REDUCER_ADD || src.reducer > HF_REDUCER_MIN) c.invalid("unknown reducer");
+        bool red[HF_MAX_RANK] = {false};
+        for (int64_t d : n.attr) {
+          if (d < 0 || d >= o.rank) c.invalid("0 <= dimensions < rank(inputs[0]) violated (C4)");
+          if (red[d]) c.invalid("is_unique(dimensions) violated (C5)");
+          red[d] = true;
+        }
+        int r = 0;
+        for (int d = 0; d < o.rank; ++d) {
+          if (red[d]) continue;
+          if (r >= t.rank || t.dims[r] != o.dims[d])
+            c.invalid("shape(results) = shape(inputs) without dimensions violated (C7)");
+          ++r;
+        }
+        if (r != t.rank) c.invalid("shape(results) = shape(inputs) without dimensions violated (C7)");
+        if (std::isnan(n.init)) c.unsupported("NaN init value");
+        break;
+      }
+    }
+  }
+
+  // reachability from the root and user lists
+  std::vector<int> stack{g.root};
+  g.nodes[g.root].live = true;
+  while (!stack.empty()) {
+    int i = stack.back();
+    stack.pop_back();
+    for (int o : g.nodes[i].opd)
+      if (!g.nodes[o].live) {
+        g.nodes[o].live = true;
+        stack.push_back(o);
+      }
+  }
+  for (int i = 0; i < (int)g.nodes.size(); ++i) {
+    if (!g.nodes[i].live) continue;
+    for (int o : g.nodes[i].opd) g.nodes[o].users.push_back(i);
+    if (g.nodes[i].op == HF_REDUCE && i != g.root)
+      fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (reduce): a reduce must be the fusion root");
+  }
+  return g;
+}
+
+}  // namespace hf

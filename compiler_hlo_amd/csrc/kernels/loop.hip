@@ -1,0 +1,39 @@
+// loop.hip -- loop hero (XLA:GPU Emitters, "Loop emitter").
+//
+// The output is walked linearly in PHYSICAL order so that stores coalesce:
+// the physical output is viewed as HF_ROWS rows of HF_COLS_V vectors of
+// HF_V elements along the physically minor dimension (128-bit stores).
+// Each thread keeps ONE column vector for its whole life and strides over
+// rows, so every value that depends only on the column (per-axis scales,
+// zero points, a bias broadcast along the rows) is loop-invariant and is
+// loaded once per thread.  HF_UNROLL rows are evaluated before their stores so
+// that the loads of several rows are in flight together.
+//
+// Provided by the generated code in front of this text:
+//   HF_BLOCK, HF_V, HF_ROWS, HF_COLS_V, HF_TPR (threads per row segment),
+//   HF_RPB (rows per block step), HF_NCH (column chunks), HF_UNROLL,
+//   hf_val_t, hf_loop_eval(A, row, colv, r), hf_loop_store(A, row, colv, r).
+extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAMS) {
+  const HfArgs A = HF_ARGS_INIT;
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x % HF_NCH;
+  const int group = blockIdx.x / HF_NCH;
+  const int ngroups = gridDim.x / HF_NCH;
+  const int colv = chunk * HF_TPR + tid % HF_TPR;
+  const int rsub = tid / HF_TPR;
+  if (colv >= HF_COLS_V || rsub >= HF_RPB) return;
+  const int rstep = ngroups * HF_RPB;
+  int row = group * HF_RPB + rsub;
+  for (; row + (HF_UNROLL - 1) * rstep < HF_ROWS; row += HF_UNROLL * rstep) {
+    hf_val_t r[HF_UNROLL][HF_V];
+#pragma unroll
+    for (int u = 0; u < HF_UNROLL; ++u) hf_loop_eval(A, row + u * rstep, colv, r[u]);
+#pragma unroll
+    for (int u = 0; u < HF_UNROLL; ++u) hf_loop_store(A, row + u * rstep, colv, r[u]);
+  }
+  for (; row < HF_ROWS; row += rstep) {
+    hf_val_t r[HF_V];
+    hf_loop_eval(A, row, colv, r);
+    hf_loop_store(A, row, colv, r);
+  }
+}

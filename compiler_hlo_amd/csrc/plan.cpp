@@ -1,0 +1,625 @@
+// plan.cpp -- hero selection, index-map propagation, partitioning, geometry.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <sstream>
+
+namespace hf {
+
+// ------------------------------------------------------------ index terms
+std::string term_str(const Term &t) {
+  switch (t.k) {
+    case Term::ZERO: return "0";
+    case Term::VAR: return "i" + std::to_string(t.var);
+    case Term::EXPR: return "(" + t.e + ")";
+  }
+  return "0";
+}
+
+std::string index_key(const Index &E) {
+  std::string s;
+  for (const Term &t : E) {
+    s += term_str(t);
+    s += ',';
+  }
+  return s;
+}
+
+Index identity_index(int rank) {
+  Index E(rank);
+  for (int d = 0; d < rank; ++d) {
+    E[d].k = Term::VAR;
+    E[d].var = d;
+  }
+  return E;
+}
+
+std::vector<long long> phys_strides(const Type &t) {
+  std::vector<long long> s(t.rank, 0);
+  long long st = 1;
+  for (int k = 0; k < t.rank; ++k) {
+    s[t.m2m[k]] = st;
+    st *= t.dims[t.m2m[k]];
+  }
+  return s;
+}
+
+int phys_minor(const Type &t) {
+  for (int k = 0; k < t.rank; ++k)
+    if (t.dims[t.m2m[k]] > 1) return t.m2m[k];
+  return -1;
+}
+
+Index operand_index(const Graph &g, int n, const Index &E, bool *general) {
+  const Node &nd = g.nodes[n];
+  const Type &ot = g.nodes[nd.opd[0]].t;
+  switch (nd.op) {
+    case HF_TRANSPOSE: {
+      // result dim d is operand dim perm[d]
+      Index O(ot.rank);
+      for (int d = 0; d < nd.t.rank; ++d) O[nd.attr[d]] = E[d];
+      return O;
+    }
+    case HF_BROADCAST_IN_DIM: {
+      // operand_index[d] = 0 if dim(operand, d) = 1 else result_index[bdims[d]]
+      Index O(ot.rank);
+      for (int d = 0; d < ot.rank; ++d)
+        if (ot.dims[d] != 1) O[d] = E[nd.attr[d]];
+      return O;
+    }
+    case HF_RESHAPE: {
+      // same position in the lexicographic order of both index spaces
+      std::vector<int> rn, on;
+      for (int d = 0; d < nd.t.rank; ++d)
+        if (nd.t.dims[d] != 1) rn.push_back(d);
+      for (int d = 0; d < ot.rank; ++d)
+        if (ot.dims[d] != 1) on.push_back(d);
+      bool same = rn.size() == on.size();
+      for (size_t k = 0; same && k < rn.size(); ++k) same = nd.t.dims[rn[k]] == ot.dims[on[k]];
+      Index O(ot.rank);
+      if (same) {  // only size-1 dims inserted or removed
+        for (size_t k = 0; k < on.size(); ++k) O[on[k]] = E[rn[k]];
+        return O;
+      }
+      if (ot.numel() == 0) return O;
+      *general = true;
+      std::string pos = "0";
+      for (int d : rn) pos = "(" + pos + ")*" + std::to_string(nd.t.dims[d]) + "+" + term_str(E[d]);
+      long long after = 1;
+      for (int k = (int)on.size() - 1; k >= 0; --k) {
+        int d = on[k];
+        Term t;
+        t.k = Term::EXPR;
+        t.e = "((" + pos + ")/" + std::to_string(after) + ")%" + std::to_string(ot.dims[d]);
+        O[d] = t;
+        after *= ot.dims[d];
+      }
+      return O;
+    }
+    default:
+      return E;  // elementwise ops, convert, quantize, dequantize
+  }
+}
+
+// ------------------------------------------------------------ analysis
+namespace {
+
+void visit(const Graph &g, Ctx &c, int n, const Index &E) {
+  if (!c.maps[n].insert(index_key(E)).second) return;
+  c.in_ctx[n] = 1;
+  if (n == c.leaf) return;
+  const Node &nd = g.nodes[n];
+  if (nd.op == HF_PARAMETER) {
+    c.param_reads.push_back({n, E});
+    return;
+  }
+  if (nd.op == HF_CONSTANT) return;
+  for (int o : nd.opd) visit(g, c, o, operand_index(g, n, E, &c.general));
+}
+
+// Partitioning (XLA:GPU Emitters, "Partitioning").  A node with one user is
+// emitted with that user.  A node with several users is emitted with them
+// when they all read it at the same indices.  When its users read it at
+// different indices it becomes its own function, evaluated once per index,
+// and each of those users heads a function of its own (the page splits
+// param -> log -> {transpose, add} into three one-instruction functions).
+void partition(const Graph &g, Ctx &c) {
+  const int N = (int)g.nodes.size();
+  c.part.assign(N, -1);
+  c.part_root.clear();
+  std::vector<std::vector<int>> users(N);
+  for (int u = 0; u < N; ++u) {
+    if (!c.in_ctx[u] || u == c.leaf) continue;
+    if (g.nodes[u].op == HF_PARAMETER || g.nodes[u].op == HF_CONSTANT) continue;
+    for (int o : g.nodes[u].opd)
+      if (std::find(users[o].begin(), users[o].end(), u) == users[o].end()) users[o].push_back(u);
+  }
+  std::vector<char> split(N, 0);
+  for (int n = 0; n < N; ++n)
+    split[n] = c.in_ctx[n] && users[n].size() >= 2 && c.maps[n].size() >= 2;
+  for (int n = N - 1; n >= 0; --n) {
+    if (!c.in_ctx[n] || n == c.leaf) continue;
+    const Node &nd = g.nodes[n];
+    if (nd.op == HF_PARAMETER || nd.op == HF_CONSTANT) continue;
+    bool head = n == c.root || split[n];
+    for (int o : nd.opd)
+      if (split[o]) head = true;
+    if (!head) {
+      int p = -1;
+      for (int u : users[n]) {
+        if (p < 0) p = c.part[u];
+        else if (c.part[u] != p) head = true;
+      }
+      if (p < 0) head = true;
+      if (!head) c.part[n] = p;
+    }
+    if (head) {
+      c.part[n] = (int)c.part_root.size();
+      c.part_root.push_back(n);
+    }
+  }
+}
+
+Ctx make_ctx(const Graph &g, int root, int lane, int leaf = -1) {
+  Ctx c;
+  c.root = root;
+  c.lane = lane;
+  c.leaf = leaf;
+  c.maps.assign(g.nodes.size(), {});
+  c.in_ctx.assign(g.nodes.size(), 0);
+  visit(g, c, root, identity_index(g.nodes[root].t.rank));
+  partition(g, c);
+  return c;
+}
+
+int pow2_floor(long long x) {
+  int p = 1;
+  while ((long long)p * 2 <= x && p < (1 << 30)) p *= 2;
+  return p;
+}
+int pow2_ceil(long long x) {
+  int p = 1;
+  while (p < x && p < (1 << 30)) p *= 2;
+  return p;
+}
+// largest power of two <= cap dividing n (n > 0)
+int vec_width(long long n, int cap) {
+  int v = 1;
+  while (v * 2 <= cap && n % (v * 2) == 0) v *= 2;
+  return v;
+}
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+long long env_ll(const char *name, long long dflt) {
+  const char *s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoll(s);
+}
+
+enum Access { CONTIG, UNIFORM, STRIDED, GATHER };
+
+// How a param read at E moves when the lane variable `lane` advances.
+Access classify(const Graph &g, int p, const Index &E, int lane) {
+  const Type &t = g.nodes[p].t;
+  if (lane < 0) return UNIFORM;
+  int at = -1;
+  for (int d = 0; d < t.rank; ++d) {
+    if (E[d].k == Term::VAR && E[d].var == lane) at = d;
+    if (E[d].k == Term::EXPR) return GATHER;
+  }
+  if (at < 0) return UNIFORM;
+  return at == phys_minor(t) ? CONTIG : STRIDED;
+}
+
+bool large(const Graph &g, int p) {
+  long long n = g.nodes[p].t.numel();
+  long long out = g.nodes[g.root].t.numel();
+  return n >= 1024 && n * 4 >= out;
+}
+
+// largest element size among large params read contiguously along the lane
+int stream_elem_bytes(const Graph &g, const Ctx &c, int dflt) {
+  int b = 0;
+  for (auto &pr : c.param_reads)
+    if (large(g, pr.first) && classify(g, pr.first, pr.second, c.lane) == CONTIG)
+      b = std::max(b, dtype_bytes(g.nodes[pr.first].t.dt));
+  return b ? b : dflt;
+}
+
+bool all_coalesced(const Graph &g, const Ctx &c) {
+  for (auto &pr : c.param_reads) {
+    if (!large(g, pr.first)) continue;
+    Access a = classify(g, pr.first, pr.second, c.lane);
+    if (a == STRIDED || a == GATHER) return false;
+  }
+  return true;
+}
+
+// nodes of n's operand tree, params and constants excluded
+void subtree(const Graph &g, int n, std::vector<char> &in) {
+  if (in[n]) return;
+  const Node &nd = g.nodes[n];
+  if (nd.op == HF_PARAMETER || nd.op == HF_CONSTANT) return;
+  in[n] = 1;
+  for (int o : nd.opd) subtree(g, o, in);
+}
+
+bool exclusive(const Graph &g, int s) {
+  std::vector<char> in(g.nodes.size(), 0);
+  subtree(g, s, in);
+  for (int x = 0; x < (int)g.nodes.size(); ++x) {
+    if (!in[x] || x == s) continue;
+    for (int u : g.nodes[x].users)
+      if (!in[u]) return false;
+  }
+  return true;
+}
+
+void algorithmic(const Graph &g, Plan &P) {
+  long long bytes = 0;
+  std::vector<char> used(g.nodes.size(), 0), qused(g.quants.size(), 0);
+  for (Ctx &c : P.ctx)
+    for (int n = 0; n < (int)g.nodes.size(); ++n)
+      if (c.in_ctx[n]) used[n] = 1;
+  for (int n = 0; n < (int)g.nodes.size(); ++n) {
+    if (!used[n]) continue;
+    const Node &nd = g.nodes[n];
+    if (nd.op == HF_PARAMETER) bytes += nd.t.numel() * dtype_bytes(nd.t.dt);
+    if (nd.t.quant >= 0 && (nd.op == HF_UNIFORM_QUANTIZE || nd.op == HF_PARAMETER)) qused[nd.t.quant] = 1;
+  }
+  for (size_t q = 0; q < g.quants.size(); ++q)
+    if (qused[q] && g.quants[q].qdim >= 0)
+      bytes += (long long)g.quants[q].scales.size() * (4 + dtype_bytes(g.quants[q].storage));
+  const Type &rt = g.nodes[g.root].t;
+  bytes += rt.numel() * dtype_bytes(rt.dt);
+  P.info.algorithmic_bytes = bytes;
+}
+
+void common_info(const Graph &g, Plan &P) {
+  P.info.hero = P.hero;
+  int np = 0;
+  for (Ctx &c : P.ctx) np += (int)c.part_root.size();
+  P.info.n_partitions = np;
+  P.info.block_threads = P.block;
+  P.info.grid_blocks = P.grid;
+  P.info.lds_bytes = P.lds_bytes;
+  P.info.workspace_bytes = P.ws_bytes;
+  algorithmic(g, P);
+  for (size_t q = 0; q < g.quants.size(); ++q)
+    if (g.quants[q].qdim >= 0) P.quant_args.push_back((int)q);
+}
+
+// ------------------------------------------------------------ heroes
+Plan plan_loop(const Graph &g, Ctx c) {
+  Plan P;
+  P.hero = HF_HERO_LOOP;
+  const Type &rt = g.nodes[g.root].t;
+  long long DL = c.lane >= 0 ? rt.dims[c.lane] : 1;
+  int V = 1;
+  if (c.lane >= 0 && !c.general) V = vec_width(DL, std::max(1, 16 / dtype_bytes(rt.dt)));
+  c.V = V;
+  long long cols_v = DL / V;
+  long long rows = DL > 0 ? rt.numel() / DL : 0;
+  int block = 256;
+  long long tpr, rpb, nch;
+  if (cols_v >= block) {
+    tpr = block;
+    rpb = 1;
+    nch = ceil_div(cols_v, block);
+  } else {
+    tpr = std::max<long long>(1, cols_v);
+    rpb = block / tpr;
+    nch = 1;
+  }
+  long long target = env_ll("HF_LOOP_WGS", 2048);
+  long long ngroups = std::max<long long>(1, std::min(ceil_div(rows, rpb), std::max<long long>(1, target / nch)));
+  P.ctx.push_back(c);
+  P.block = block;
+  P.grid = nch * ngroups;
+  P.empty = rt.numel() == 0;
+  P.macros = {{"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", rows}, {"HF_COLS_V", cols_v},
+              {"HF_TPR", tpr}, {"HF_RPB", rpb}, {"HF_NCH", nch},
+              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", 2)}};
+  P.info.vector_elems = V;
+  P.info.elements = rt.numel();
+  P.info.rows = rows;
+  P.info.cols = DL;
+  common_info(g, P);
+  return P;
+}
+
+bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
+  const Type &rt = g.nodes[g.root].t;
+  int lout = loop.lane;
+  if (lout < 0 || loop.general) return false;
+  int lin = -1;
+  bool any = false;
+  for (auto &pr : loop.param_reads) {
+    if (!large(g, pr.first)) continue;
+    if (classify(g, pr.first, pr.second, lout) == GATHER) return false;
+    int pm = phys_minor(g.nodes[pr.first].t);
+    if (pm < 0) continue;
+    const Term &t = pr.second[pm];
+    if (t.k != Term::VAR || t.var == lout) continue;
+    if (lin >= 0 && lin != t.var) return false;  // two different transposed directions
+    lin = t.var;
+    any = true;
+  }
+  if (!any || lin < 0 || lin == lout || rt.dims[lin] <= 1) return false;
+  // candidate staged nodes: transposes read at identity from the root, then the root
+  std::vector<int> cands;
+  std::string id = index_key(identity_index(rt.rank));
+  for (int n = 0; n < (int)g.nodes.size(); ++n)
+    if (g.nodes[n].live && g.nodes[n].op == HF_TRANSPOSE && n != g.root && loop.maps[n].size() == 1 &&
+        *loop.maps[n].begin() == id)
+      cands.push_back(n);
+  cands.push_back(g.root);
+  for (int s : cands) {
+    if (!exclusive(g, s)) continue;
+    Ctx ld = make_ctx(g, s, lin);
+    Ctx st = make_ctx(g, g.root, lout, s == g.root ? -1 : s);
+    if (s == g.root) {
+      // staging the root: the store phase only copies from LDS
+      st = Ctx();
+      st.root = g.root;
+      st.leaf = g.root;
+      st.lane = lout;
+      st.maps.assign(g.nodes.size(), {});
+      st.in_ctx.assign(g.nodes.size(), 0);
+      st.in_ctx[g.root] = 1;
+      st.part.assign(g.nodes.size(), -1);
+    }
+    if (ld.general || st.general) continue;
+    if (!all_coalesced(g, ld) || !all_coalesced(g, st)) continue;
+    Plan P;
+    P.hero = HF_HERO_TRANSPOSE;
+    P.staged = s;
+    P.lane_in = lin;
+    P.lane_out = lout;
+    long long DU = rt.dims[lout], DW = rt.dims[lin];
+    int vout = vec_width(DU, std::max(1, 16 / dtype_bytes(rt.dt)));
+    int vin = vec_width(DW, std::max(1, 16 / stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt))));
+    ld.V = vin;
+    st.V = vout;
+    int tu = (int)std::min<long long>(env_ll("HF_TR_TU", 64), pow2_ceil(DU));
+    int tw = (int)std::min<long long>(env_ll("HF_TR_TW", 64), pow2_ceil(DW));
+    tu = std::max(tu, vout);
+    tw = std::max(tw, vin);
+    long long ntu = ceil_div(DU, tu), ntw = ceil_div(DW, tw);
+    long long nb = rt.numel() / (DU * DW);
+    int pitch = tu + 1;
+    P.ctx.push_back(ld);
+    P.ctx.push_back(st);
+    P.block = 256;
+    P.grid = nb * ntu * ntw;
+    P.lds_bytes = tw * pitch * 4;
+    P.empty = rt.numel() == 0;
+    P.macros = {{"HF_BLOCK", 256}, {"HF_TU", tu}, {"HF_TW", tw}, {"HF_PITCH", pitch},
+                {"HF_VIN", vin}, {"HF_VOUT", vout}, {"HF_DU", DU}, {"HF_DW", DW},
+                {"HF_NTU", ntu}, {"HF_NTW", ntw}};
+    P.info.vector_elems = vout;
+    P.info.elements = rt.numel();
+    P.info.rows = DW;
+    P.info.cols = DU;
+    P.info.tile_rows = tw;
+    P.info.tile_cols = tu;
+    common_info(g, P);
+    *out = P;
+    return true;
+  }
+  return false;
+}
+
+Plan plan_reduce(const Graph &g) {
+  const Node &R = g.nodes[g.root];
+  int rin = R.opd[0];
+  const Type &it = g.nodes[rin].t;
+  Ctx c = make_ctx(g, rin, -1);
+  // Physical order of the reduce input: taken from the largest parameter that
+  // reads the input space through a pure permutation of its dims.
+  std::vector<int> order;
+  long long best = -1;
+  for (auto &pr : c.param_reads) {
+    const Type &pt = g.nodes[pr.first].t;
+    std::vector<int> o;
+    bool ok = true;
+    std::vector<char> seen(it.rank, 0);
+    for (int k = 0; k < pt.rank && ok; ++k) {
+      int d = pt.m2m[k];
+      if (pt.dims[d] <= 1) continue;
+      const Term &t = pr.second[d];
+      if (t.k != Term::VAR || seen[t.var]) ok = false;
+      else {
+        seen[t.var] = 1;
+        o.push_back(t.var);
+      }
+    }
+    for (int d = 0; d < it.rank && ok; ++d)
+      if (it.dims[d] > 1 && !seen[d]) ok = false;
+    if (ok && pt.numel() > best) {
+      best = pt.numel();
+      order = o;
+    }
+  }
+  if (best < 0) {
+    order.clear();
+    for (int d = it.rank - 1; d >= 0; --d)
+      if (it.dims[d] > 1) order.push_back(d);
+  }
+  std::vector<char> red(it.rank, 0);
+  for (int64_t d : R.attr) red[d] = 1;
+  size_t nk = 0, nj = 0;
+  for (int d : order) (red[d] ? nk : nj)++;
+  bool row = true;
+  if (nk > 0 && nj > 0) {
+    bool minor_red = true, minor_kept = true;
+    for (size_t k = 0; k < order.size(); ++k) {
+      if (k < nk && !red[order[k]]) minor_red = false;
+      if (k < nj && red[order[k]]) minor_kept = false;
+    }
+    if (minor_red) row = true;
+    else if (minor_kept) row = false;
+    else
+      fail(HF_ERR_UNSUPPORTED,
+           "node " + std::to_string(g.root) +
+               " (reduce): reduced dimensions are neither the physically minor nor the physically major ones");
+  }
+  long long K = 1, J = 1;
+  for (int d = 0; d < it.rank; ++d) (red[d] ? K : J) *= it.dims[d];
+  if (it.numel() == 0) K = J = 0;
+  for (int d = 0; d < it.rank; ++d)
+    if (it.dims[d] == 0) (red[d] ? K : J) = 0;
+
+  Plan P;
+  P.rin = rin;
+  P.order = order;
+  P.empty = R.t.numel() == 0;
+  const int op = (int)R.reducer;
+  if (row) {
+    P.hero = HF_HERO_ROW_REDUCE;
+    c.lane = nk > 0 ? order[0] : -1;
+    c = make_ctx(g, rin, c.lane);
+    int V = 1;
+    if (c.lane >= 0 && !c.general)
+      V = vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4)));
+    c.V = V;
+    long long kv = K / V;
+    int block, tpr;
+    if (kv >= 64) {
+      block = (int)std::min<long long>(256, pow2_floor(kv));
+      tpr = block;
+    } else {
+      block = 256;
+      tpr = pow2_ceil(std::max<long long>(1, kv));
+    }
+    long long rpb = tpr == block ? 1 : block / tpr;
+    long long target = env_ll("HF_ROW_WGS", 1024);
+    P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb), target));
+    P.block = block;
+    P.lds_bytes = (block / 64) * 4;
+    P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", J},
+                {"HF_KV", kv}, {"HF_TPR", tpr}};
+    P.info.vector_elems = V;
+    P.info.rows = J;
+    P.info.cols = K;
+  } else {
+    P.hero = HF_HERO_COLUMN_REDUCE;
+    c = make_ctx(g, rin, order[0]);
+    int V = c.general ? 1 : vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4)));
+    c.V = V;
+    long long Cc = J, Rr = K;
+    int cl = (int)std::min<long long>(env_ll("HF_COL_CL", 64), pow2_ceil(ceil_div(Cc, V)));
+    int block = 256;
+    int rl = block / cl;
+    long long cb = (long long)cl * V;
+    long long ncb = ceil_div(Cc, cb);
+    long long target = env_ll("HF_COL_WGS", 2048);
+    long long segs = std::max<long long>(1, std::min(target / ncb, ceil_div(Rr, rl)));
+    long long rs = Rr > 0 ? ceil_div(Rr, segs) : 0;
+    segs = rs > 0 ? ceil_div(Rr, rs) : 1;
+    P.grid = ncb * segs;
+    P.block = block;
+    P.lds_bytes = (int)(rl * cb * 4 + 4);
+    if (segs > 1) {
+      P.ws_counter_off = ((segs * Cc * 4 + 255) / 256) * 256;
+      P.ws_counters = (int)ncb;
+      P.ws_bytes = P.ws_counter_off + ncb * 4;
+    }
+    P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_C", Cc}, {"HF_R", Rr},
+                {"HF_CL", cl}, {"HF_RL", rl}, {"HF_CB", cb}, {"HF_NCB", ncb}, {"HF_S", segs},
+                {"HF_RS", rs}};
+    P.info.vector_elems = V;
+    P.info.rows = Rr;
+    P.info.cols = Cc;
+    P.info.tile_rows = (int)rs;
+    P.info.tile_cols = (int)cb;
+  }
+  P.ctx.push_back(c);
+  P.info.elements = it.numel();
+  common_info(g, P);
+  return P;
+}
+
+}  // namespace
+
+const char *hero_template_name(hf_hero h) {
+  switch (h) {
+    case HF_HERO_LOOP: return "loop";
+    case HF_HERO_TRANSPOSE: return "transpose";
+    case HF_HERO_ROW_REDUCE: return "reduce_row";
+    case HF_HERO_COLUMN_REDUCE: return "reduce_col";
+  }
+  return "?";
+}
+
+// Hero selection (XLA:GPU Emitters, "Hero-based codegen"): a reduce root
+// selects a reduction emitter, row or column by the physical layout of its
+// input; a transpose whose reads are not coalesced in the output order
+// selects the transpose emitter (shared memory fixes the read and write
+// patterns); everything else is the loop emitter.
+Plan make_plan(const Graph &g) {
+  const Node &R = g.nodes[g.root];
+  if (R.op == HF_REDUCE) return plan_reduce(g);
+  Ctx loop = make_ctx(g, g.root, phys_minor(R.t));
+  if (!env_ll("HF_NO_TRANSPOSE_HERO", 0)) {
+    Plan P;
+    if (try_transpose(g, loop, &P)) return P;
+  }
+  return plan_loop(g, loop);
+}
+
+// ------------------------------------------------------------ constants
+// Round-to-nearest-even of a double to a binary format with p significand
+// bits and minimum normal exponent emin, working on the IEEE-754 binary64
+// bit pattern; overflow goes to infinity.
+static double round_bits(double x, int p, int emin, int emax) {
+  if (std::isnan(x) || std::isinf(x) || x == 0.0) return x;
+  uint64_t b;
+  std::memcpy(&b, &x, 8);
+  const uint64_t sign = b & (uint64_t(1) << 63);
+  int e = (int)((b >> 52) & 0x7FF);
+  uint64_t m = b & ((uint64_t(1) << 52) - 1);
+  int ue;  // unbiased exponent of the leading bit
+  if (e == 0) {  // double subnormal: normalise
+    ue = -1022;
+    while (!(m & (uint64_t(1) << 52))) {
+      m <<= 1;
+      --ue;
+    }
+  } else {
+    m |= uint64_t(1) << 52;
+    ue = e - 1023;
+  }
+  // keep p bits below and including the leading bit, fewer in the subnormal range
+  int keep = p;
+  if (ue < emin) keep = p - (emin - ue);
+  if (keep <= 0) {
+    // below half the smallest subnormal, or exactly half (ties to even -> 0)
+    if (keep == 0 && m > (uint64_t(1) << 52)) {
+      double r = std::ldexp(1.0, emin - (p - 1));
+      return sign ? -r : r;
+    }
+    return sign ? -0.0 : 0.0;
+  }
+  int drop = 53 - keep;
+  uint64_t q = m >> drop, rem = m & ((uint64_t(1) << drop) - 1), half = uint64_t(1) << (drop - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  double r = std::ldexp((double)q, ue - keep + 1);
+  double maxf = std::ldexp(2.0 - std::ldexp(1.0, 1 - p), emax);
+  if (r > maxf) r = INFINITY;
+  return sign ? -r : r;
+}
+
+double round_to_dtype(double x, hf_dtype dt) {
+  switch (dt) {
+    case HF_F32: return (double)(float)x;
+    case HF_BF16: return round_bits(x, 8, -126, 127);
+    case HF_F16: return round_bits(x, 11, -14, 15);
+    default: return std::nearbyint(x);
+  }
+}
+
+}  // namespace hf

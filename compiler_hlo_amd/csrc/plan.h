@@ -1,0 +1,83 @@
+// plan.h -- hero selection, partitioning, index maps and kernel geometry.
+#pragma once
+
+#include <map>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "ir.h"
+
+namespace hf {
+
+// One component of an index vector, as a function of the variables of the
+// space it is expressed in (i0, i1, ...): a variable, the constant 0 (a
+// broadcast or size-1 dimension), or a general expression (after a reshape
+// that is not a pure insertion/removal of size-1 dimensions).
+struct Term {
+  enum Kind { ZERO, VAR, EXPR } k = ZERO;
+  int var = -1;
+  std::string e;
+};
+using Index = std::vector<Term>;
+
+std::string term_str(const Term &t);
+std::string index_key(const Index &E);
+Index identity_index(int rank);
+
+// Output-to-input index map of operand `k` of node `n` read at E
+// (XLA:GPU Emitters, "Indexing transforms").  Sets *general when a reshape
+// needed div/mod arithmetic.
+Index operand_index(const Graph &g, int n, const Index &E, bool *general);
+
+// Physical stride (in elements) of every logical dim of t.
+std::vector<long long> phys_strides(const Type &t);
+// Most minor dim with extent > 1, or -1.
+int phys_minor(const Type &t);
+
+// One evaluation phase of a hero: `root` is evaluated at the identity index
+// of its own space, lanes run along `lane`, `leaf` (if any) is read from LDS.
+struct Ctx {
+  int root = -1;
+  int leaf = -1;
+  int lane = -1;
+  int V = 1;
+  bool general = false;                       // a div/mod reshape was met
+  std::vector<std::set<std::string>> maps;    // distinct index maps per node
+  std::vector<char> in_ctx;
+  std::vector<std::pair<int, Index>> param_reads;
+  std::vector<int> part;                      // node -> partition
+  std::vector<int> part_root;                 // partition -> root node
+};
+
+struct Plan {
+  hf_hero hero = HF_HERO_LOOP;
+  std::vector<Ctx> ctx;       // loop/reduce: 1; transpose: [0] load, [1] store
+  int staged = -1;            // transpose: staged node
+  int lane_in = -1, lane_out = -1;
+  // reduce
+  int rin = -1;               // reduce operand node
+  std::vector<int> order;     // input dims with extent > 1, physical minor -> major
+  // geometry
+  std::vector<std::pair<std::string, long long>> macros;
+  int block = 256;
+  long long grid = 1;
+  int lds_bytes = 0;
+  long long ws_bytes = 0;     // workspace (column reduce)
+  long long ws_counter_off = 0;
+  int ws_counters = 0;
+  bool empty = false;         // nothing to launch (zero-size result)
+  hf_plan_info info{};
+  std::vector<int> quant_args;  // quant indices passed as per-axis arrays
+};
+
+Plan make_plan(const Graph &g);
+std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
+                            const std::string &hero_text);
+const char *hero_template_name(hf_hero h);
+
+// Constants: round a double to an element type (RNE), the way a constant of
+// that type holds it.
+double round_to_dtype(double x, hf_dtype dt);
+
+}  // namespace hf

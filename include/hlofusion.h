@@ -1,0 +1,236 @@
+/*
+ * hlofusion.h -- C ABI of the hero-fusion library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library executes ONE HLO fusion on one GPU: an elementwise prologue over
+ * N-d arrays whose memory order is given by minor_to_major layouts, feeding
+ * one "hero" -- a plain loop, a transpose, or a reduce -- that decides how the
+ * whole fusion is emitted (XLA:GPU Emitters, "Hero-based codegen").
+ *
+ * Life cycle:
+ *   hf_fusion_create   validate the descriptor, plan it (partition the DAG,
+ *                      compose index maps, pick the hero and its tiling),
+ *                      generate HIP source for it, compile it for gfx950 and
+ *                      load it on the current device.  All validation happens
+ *                      here, on the host, before any GPU call.
+ *   hf_fusion_launch   run it on a caller-supplied stream; asynchronous; no
+ *                      allocation, no synchronisation.
+ *   hf_fusion_destroy  release what create allocated.
+ *
+ * Conventions:
+ *   - Every function has C linkage and takes plain pointers and sizes only.
+ *   - Device buffers and streams belong to the caller.  Buffers are dense and
+ *     stored exactly in the declared layout (strided views are not accepted).
+ *   - Errors: every call returns an hf_status; hf_last_error() gives a
+ *     message for the last failing call on the calling thread.
+ *   - A fusion handle is immutable after create and bound to the device that
+ *     was current at create.  Launches of ONE handle must not overlap in time
+ *     (same stream, or synchronised), because a column-reduce plan keeps its
+ *     cross-workgroup partials and counters in the handle's workspace.
+ */
+#ifndef HLOFUSION_H
+#define HLOFUSION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HF_ABI_VERSION 1
+#define HF_MAX_RANK 8
+#define HF_MAX_PARAMS 16
+#define HF_MAX_NODES 256
+
+typedef enum {
+  HF_OK = 0,
+  HF_ERR_INVALID = 1,      /* the descriptor or a launch argument breaks a rule */
+  HF_ERR_UNSUPPORTED = 2,  /* valid, but outside what this library implements */
+  HF_ERR_COMPILE = 3,      /* the generated kernel did not compile */
+  HF_ERR_HIP = 4,          /* a HIP runtime call failed */
+  HF_ERR_NOMEM = 5
+} hf_status;
+
+/* Element types (StableHLO Specification, "Types": element types). */
+typedef enum {
+  HF_F32 = 0,
+  HF_BF16 = 1,
+  HF_F16 = 2,
+  HF_S8 = 3,
+  HF_U8 = 4,
+  HF_S32 = 5
+} hf_dtype;
+
+/* Ops.  Semantics are those of the StableHLO Specification ("Ops") and of
+ * Operation semantics (XlaBuilder), one section each:
+ *   HF_PARAMETER          Parameter: fusion input number `parameter_number`.
+ *   HF_CONSTANT           constant: the scalar `constant`, broadcast over the
+ *                         node's type and rounded to its element type.
+ *   HF_LOG, HF_EXP, HF_TANH          log, exponential, tanh (IEEE-754).
+ *   HF_NEGATE, HF_ABS                negate, abs.
+ *   HF_ADD, HF_SUBTRACT, HF_MULTIPLY, HF_DIVIDE   IEEE-754 arithmetic.
+ *   HF_MAXIMUM, HF_MINIMUM           IEEE-754 maximum / minimum.
+ *   HF_CONVERT            convert: int->float and float->float round to
+ *                         nearest even; float->int truncates.
+ *   HF_BROADCAST_IN_DIM   broadcast_in_dim, attr = broadcast_dimensions.
+ *   HF_RESHAPE            reshape (same position in lexicographic order).
+ *   HF_TRANSPOSE          transpose, attr = permutation: result dim d is
+ *                         operand dim attr[d].
+ *   HF_UNIFORM_DEQUANTIZE real = scale * (q - zero_point) (StableHLO
+ *                         Quantization; per-tensor or per-axis).
+ *   HF_UNIFORM_QUANTIZE   q = clamp(round_half_even(real / scale) +
+ *                         zero_point, storage_min, storage_max).
+ *   HF_REDUCE             reduce over attr = dimensions with `reducer` and
+ *                         `init_value`; must be the root.
+ */
+typedef enum {
+  HF_PARAMETER = 0,
+  HF_CONSTANT = 1,
+  HF_ADD = 2,
+  HF_SUBTRACT = 3,
+  HF_MULTIPLY = 4,
+  HF_DIVIDE = 5,
+  HF_MAXIMUM = 6,
+  HF_MINIMUM = 7,
+  HF_LOG = 8,
+  HF_EXP = 9,
+  HF_TANH = 10,
+  HF_NEGATE = 11,
+  HF_ABS = 12,
+  HF_CONVERT = 13,
+  HF_BROADCAST_IN_DIM = 14,
+  HF_RESHAPE = 15,
+  HF_TRANSPOSE = 16,
+  HF_UNIFORM_DEQUANTIZE = 17,
+  HF_UNIFORM_QUANTIZE = 18,
+  HF_REDUCE = 19
+} hf_op;
+
+typedef enum { HF_REDUCER_ADD = 0, HF_REDUCER_MAX = 1, HF_REDUCER_MIN = 2 } hf_reducer;
+
+/* Uniform quantization parameters of a quantized element type (StableHLO
+ * Specification, "Types": QuantizedTensorElementType, constraints C1-C13;
+ * StableHLO Quantization, "Per-tensor quantization", "Per-axis
+ * quantization").  The expressed type is f32; the storage type is the
+ * hf_type's dtype (HF_S8 or HF_U8).  All arrays are HOST pointers read during
+ * hf_fusion_create only; the library keeps its own copies. */
+typedef struct {
+  int32_t quantization_dimension;  /* -1: per-tensor; else the sliced dim */
+  int32_t n;                       /* pairs: 1 (per-tensor) or dim(qdim) */
+  const float *scales;             /* n values, each finite and > 0 */
+  const int32_t *zero_points;      /* n values, storage_min <= zp <= storage_max */
+  int32_t has_storage_range;       /* 0: storage range = range of dtype */
+  int32_t storage_min, storage_max;
+} hf_quant;
+
+/* An array type: element type, dims (ascending dimension numbers), layout
+ * (Shapes and layout, "Minor-to-major dimension ordering"; the first entry is
+ * the most minor, fastest-varying dim).  has_layout = 0 selects the default
+ * layout {rank-1, ..., 0} ("Default minor-to-major ordering").  Layouts are
+ * physical only for parameters and the root; other nodes are virtual. */
+typedef struct {
+  hf_dtype dtype;
+  int32_t rank;                           /* 0 .. HF_MAX_RANK */
+  int64_t dims[HF_MAX_RANK];              /* >= 0; size 0 is valid */
+  int32_t has_layout;
+  int32_t minor_to_major[HF_MAX_RANK];
+  const hf_quant *quant;                  /* NULL unless a quantized type */
+} hf_type;
+
+/* One node of the fusion computation.  Operands are indices of EARLIER nodes
+ * (the array is in topological order). */
+typedef struct {
+  hf_op op;
+  int32_t n_operands;
+  int32_t operands[2];
+  hf_type type;                 /* result type, stated explicitly */
+  int32_t parameter_number;     /* HF_PARAMETER */
+  double constant;              /* HF_CONSTANT */
+  int32_t n_attr;
+  int64_t attr[HF_MAX_RANK];    /* permutation | broadcast_dimensions | dimensions */
+  hf_reducer reducer;           /* HF_REDUCE */
+  double init_value;            /* HF_REDUCE */
+} hf_node;
+
+typedef struct {
+  int32_t abi_version;          /* HF_ABI_VERSION */
+  int32_t n_nodes;              /* 1 .. HF_MAX_NODES */
+  const hf_node *nodes;
+  int32_t root;                 /* index of the root node */
+  int32_t n_params;             /* parameters are numbered 0 .. n_params-1 */
+} hf_fusion_desc;
+
+typedef struct hf_fusion hf_fusion;
+
+typedef enum {
+  HF_HERO_LOOP = 0,
+  HF_HERO_TRANSPOSE = 1,
+  HF_HERO_ROW_REDUCE = 2,
+  HF_HERO_COLUMN_REDUCE = 3
+} hf_hero;
+
+/* What the planner chose.  Bytes are ALGORITHMIC: every parameter and the
+ * per-axis quantization arrays read once, the result written once. */
+typedef struct {
+  hf_hero hero;
+  int32_t n_partitions;         /* subgraph functions (XLA:GPU Emitters, "Partitioning") */
+  int32_t vector_elems;         /* elements per lane per streaming access */
+  int32_t block_threads;
+  int64_t grid_blocks;
+  int32_t lds_bytes;
+  int64_t workspace_bytes;
+  int64_t algorithmic_bytes;
+  int64_t elements;             /* output elements (loop, transpose) or reduced inputs */
+  int64_t rows, cols;           /* the normalised physical problem */
+  int32_t tile_rows, tile_cols; /* transpose tile / reduce segment shape */
+} hf_plan_info;
+
+/* flags for hf_fusion_create */
+#define HF_CREATE_PLAN_ONLY 1u     /* validate and plan; no code, no GPU */
+#define HF_CREATE_COMPILE_ONLY 2u  /* also generate and compile; no GPU */
+
+/* Validate, plan, generate, compile and load.  On success *out owns a handle
+ * to free with hf_fusion_destroy.  Errors: HF_ERR_INVALID for a descriptor
+ * that breaks an op's constraints (message names the node), HF_ERR_UNSUPPORTED
+ * for a valid fusion this library does not implement, HF_ERR_COMPILE,
+ * HF_ERR_HIP.  Nothing is left allocated on failure. */
+hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion **out);
+
+/* Copy the plan into *info. */
+hf_status hf_fusion_plan(const hf_fusion *f, hf_plan_info *info);
+
+/* Copy the generated HIP source (NUL-terminated) into buf if cap suffices;
+ * *len receives the length without the NUL.  HF_ERR_INVALID if the handle
+ * was created with HF_CREATE_PLAN_ONLY. */
+hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *len);
+
+/* Run the fusion.  params[i] is the DEVICE pointer of parameter i (dense, in
+ * its declared layout, 16-byte aligned); result is the device pointer of the
+ * root buffer (dense, root layout, 16-byte aligned, not overlapping any
+ * parameter).  The same parameter pointer may be passed twice.  stream is a
+ * hipStream_t (NULL = the null stream).  The launch is asynchronous and
+ * allocates nothing; a fault inside the kernel surfaces at the caller's next
+ * synchronisation.  Errors: HF_ERR_INVALID (count, NULL, alignment, overlap,
+ * plan-only handle, wrong device), HF_ERR_HIP. */
+hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params,
+                           void *result, void *stream);
+
+/* Release the handle (NULL is allowed). */
+void hf_fusion_destroy(hf_fusion *f);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *hf_last_error(void);
+
+int32_t hf_abi_version(void);
+
+/* Host helper: linear index of a logical multi-index under a layout
+ * (Shapes and layout, "Array indexing").  Returns -1 on invalid input. */
+int64_t hf_linear_index(int32_t rank, const int64_t *dims, const int32_t *minor_to_major,
+                        const int64_t *index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLOFUSION_H */

@@ -1,0 +1,421 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case draws seeded synthetic inputs (workloads), runs the fusion on the
+GPU through compiler_hlo_amd (ctypes -> libhlofusion.so -> hiprtc-compiled
+gfx950 kernels) and compares element by element with the oracle, to the
+tolerance of the operation:
+  * data movement, integer and quantized results: bit-exact;
+  * f32 exp/log: within 2 ulp (ordinal distance on f32 bit patterns);
+  * bf16 results of transcendentals: within 1 bf16 ulp;
+  * float sums: |gpu - S| <= 1e-5 * sum|y| with S the oracle's long-double sum;
+  * max/min reductions: bit-exact.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from harness import (assert_bitexact, assert_ulp, run_gpu, to_device, from_device,
+                     ulp_dist_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import compiler_hlo_amd  # noqa: F401  (fails loudly without the library)
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------------
+# loop hero: per-axis dequantize + bias + requantize (bit-exact int8)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("r,c", [(37, 160), (5, 48), (3, 24), (7, 33), (1, 1), (300, 4096)])
+def test_quant_small(r, c):
+    say("quant", r, c)
+    spec, params, _ = W.quant_dequant_bias_requant(r, c, seed=60 + r)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "loop"
+    want = oracle.evaluate(spec.nodes, params)
+    assert_bitexact(got, want, "s8")
+
+
+def test_quant_full():
+    spec, params, _ = W.quant_dequant_bias_requant()
+    say("quant full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    want = oracle.evaluate(spec.nodes, params)
+    assert_bitexact(got, want, "s8")
+    clamped = np.mean((want == 127) | (want == -128))
+    say("clamped fraction", clamped)
+
+
+def test_quant_zero_point_and_ties():
+    """Per-tensor requantize with a non-zero output zero point, on values
+    placed next to the rounding ties of y / scale."""
+    sc = np.float32(0.02)
+    centers = ((np.arange(-130, 130) + 0.5) * 0.02).astype(np.float32).view(np.int32)
+    y = np.concatenate([(centers + off).view(np.float32) for off in range(-8, 8)])
+    y = y[: (y.size // 16) * 16]
+    for zp in (0, 7, -20):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [y.size])
+        s.op("uniform_quantize", [p], "s8", [y.size], quant=W.quant_type("s8", [sc], [zp]))
+        got, _ = run_gpu(s.nodes, [y])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [y]), "s8")
+
+
+# --------------------------------------------------------------------------
+# loop hero with a transposed read: add(log p, transpose(log p))
+# --------------------------------------------------------------------------
+def _log_pair_bound(x, n, got):
+    s = W.Spec()
+    p = s.parameter(0, "f32", [n, n], [1, 0])
+    s.unary("log", p, "f32", [n, n])
+    L = oracle.evaluate(s.nodes, [x]).reshape(n, n)
+    g = got.reshape(n, n)
+    exact = L.astype(np.float64) + L.T.astype(np.float64)
+    ulp = lambda v: np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)
+    bound = 2 * ulp(L) + 2 * ulp(L.T) + 0.5 * ulp(g)
+    assert np.all(np.abs(g.astype(np.float64) - exact) <= bound)
+    assert np.array_equal(g.view(np.uint32), g.T.view(np.uint32)), "not symmetric"
+
+
+@pytest.mark.parametrize("n", [64, 5, 33, 100, 128])
+def test_loop_log_transpose_add(n):
+    say("log-transpose-add", n)
+    spec, params, _ = W.loop_log_transpose_add(n, seed=10 + n)
+    got, f = run_gpu(spec.nodes, params)
+    pl = f.plan()
+    assert pl["hero"] == "loop" and pl["n_partitions"] == 3
+    _log_pair_bound(params[0], n, got)
+
+
+# --------------------------------------------------------------------------
+# transpose hero
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n0,n1", [(200, 300), (130, 70), (64, 64), (1, 5), (5, 1), (3, 1000), (257, 129)])
+def test_transpose_exp_small(n0, n1):
+    say("transpose exp", n0, n1)
+    spec, params, _ = W.transpose_exp_f32(n0, n1, seed=20 + n0)
+    got, f = run_gpu(spec.nodes, params)
+    want = oracle.evaluate(spec.nodes, params)
+    assert_ulp(got, want, "f32", 2)
+
+
+def test_transpose_exp_full_and_loop_invariant():
+    spec, params, _ = W.transpose_exp_f32()
+    say("transpose exp full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    assert f.plan()["hero"] == "transpose"
+    want = oracle.evaluate(spec.nodes, params)
+    d = assert_ulp(got, want, "f32", 2)
+    say("ulp histogram", np.bincount(d.astype(np.int64)))
+    # the same exp through the loop hero, transposed on the host: bitwise equal
+    s = W.Spec()
+    x = s.parameter(0, "f32", [4096, 4096], [1, 0])
+    s.unary("exponential", x, "f32", [4096, 4096])
+    e, fl = run_gpu(s.nodes, params)
+    assert fl.plan()["hero"] == "loop"
+    assert np.array_equal(got.reshape(4096, 4096).view(np.uint32), e.reshape(4096, 4096).T.view(np.uint32))
+
+
+@pytest.mark.parametrize("b,m,n", [(3, 40, 72), (2, 130, 64), (4, 17, 9), (1, 1, 8), (5, 64, 1)])
+def test_transpose_bf16_small(b, m, n):
+    say("transpose bf16", b, m, n)
+    spec, params, _ = W.transpose_bf16_021(b, m, n, seed=30 + m)
+    got, _ = run_gpu(spec.nodes, params)
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "bf16")
+
+
+def test_transpose_bf16_full():
+    spec, params, _ = W.transpose_bf16_021()
+    say("transpose bf16 full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    assert f.plan()["hero"] == "transpose"
+    want = np.transpose(params[0].reshape(64, 512, 1024), (0, 2, 1)).ravel()
+    assert_bitexact(got, want, "bf16")
+    pts = np.stack([np.random.default_rng(1).integers(0, d, 4000) for d in (64, 1024, 512)], axis=1)
+    vals, _ = oracle.evaluate_points(spec.nodes, params, pts)
+    lin = (pts[:, 0] * 1024 + pts[:, 1]) * 512 + pts[:, 2]
+    gv = oracle.bf16_bits_to_f32(got[lin]).astype(np.float64)
+    assert np.array_equal(gv, vals)
+
+
+# --------------------------------------------------------------------------
+# row reduce: sum over the minor dim of convert(add(exp x, broadcast b)) in bf16
+# --------------------------------------------------------------------------
+def _check_sum(got, spec, params, rows_idx):
+    pts = np.asarray(rows_idx, dtype=np.int64)
+    vals, aux = oracle.evaluate_points(spec.nodes, params, pts)
+    rn = spec.nodes[-1]
+    lin = np.array([oracle.linear_index(rn["dims"], rn["m2m"] or oracle.default_m2m(len(rn["dims"])), p)
+                    for p in pts])
+    g = got[lin].astype(np.float64)
+    err = np.abs(g - aux[:, 1])
+    assert np.all(err <= 1e-5 * aux[:, 0]), "max err/bound %g" % np.max(err / np.maximum(aux[:, 0], 1e-300))
+
+
+@pytest.mark.parametrize("d0,d2,d3", [(2, 5, 1000), (1, 3, 2048 + 8), (3, 7, 24), (2, 2, 5), (1, 1, 16384)])
+def test_row_reduce_small(d0, d2, d3):
+    say("row reduce", d0, d2, d3)
+    spec, params, _ = W.row_reduce_exp_add_bf16(d0, d2, d3, seed=40 + d3)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "row_reduce"
+    _check_sum(got, spec, params, [[a, 0, c] for a in range(d0) for c in range(d2)])
+
+
+def test_row_reduce_full_sampled_and_layout_invariant():
+    spec, params, _ = W.row_reduce_exp_add_bf16()
+    say("row reduce full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    rng = np.random.default_rng(4)
+    rows = [[int(a), 0, int(c)] for a, c in zip(rng.integers(0, 8, 40), rng.integers(0, 1280, 40))]
+    rows += [[0, 0, 0], [7, 0, 1279]]
+    _check_sum(got, spec, params, rows)
+    # {3,2,0,1} stores the same bytes (dim 1 has size 1): bitwise equal results
+    spec2, params2, _ = W.row_reduce_exp_add_bf16(m2m=(3, 2, 0, 1))
+    got2, _ = run_gpu(spec2.nodes, params2)
+    assert np.array_equal(got.view(np.uint32), got2.view(np.uint32))
+
+
+def test_row_reduce_bf16_intermediates_loop():
+    """The reduce operand y = add(exp x, b) itself (a bf16 loop fusion) is
+    within 1 bf16 ulp of the oracle elementwise."""
+    s = W.Spec()
+    dims = [2, 1, 16, 512]
+    x = s.parameter(0, "bf16", dims)
+    b = s.parameter(1, "bf16", [512], [0])
+    e = s.unary("exponential", x, "bf16", dims)
+    bc = s.broadcast_in_dim(b, [3], "bf16", dims)
+    s.binary("add", e, bc, "bf16", dims)
+    g = W.rng(41)
+    params = [W.normal_bf16(g, 2 * 16 * 512), W.normal_bf16(g, 512)]
+    got, _ = run_gpu(s.nodes, params)
+    d = assert_ulp(got, oracle.evaluate(s.nodes, params), "bf16", 1)
+    say("1-ulp fraction", float(np.mean(d > 0)))
+
+
+def test_reductions_exact_on_integers():
+    """Integer-valued inputs make every summation order exact: row and column
+    sums are bit-exact."""
+    g = W.rng(42)
+    for dims, red, m2m in (([64, 300], [1], [1, 0]), ([300, 64], [0], [1, 0]), ([33, 70], [0], [0, 1]),
+                           ([5, 6, 40], [0, 1], [2, 1, 0]), ([40, 5, 6], [1, 2], [2, 1, 0])):
+        x = g.integers(-4, 5, int(np.prod(dims))).astype(np.float32)
+        s = W.Spec()
+        p = s.parameter(0, "f32", dims, m2m)
+        kept = [dims[d] for d in range(len(dims)) if d not in red]
+        s.reduce(p, red, "add", 0.0, "f32", kept)
+        got, f = run_gpu(s.nodes, [x])
+        say("exact sum", dims, red, m2m, f.plan()["hero"])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
+# --------------------------------------------------------------------------
+# column reduce (max) and its column-major twin
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("r,c", [(100, 48), (1000, 4096), (7, 3), (513, 260), (16384, 40)])
+def test_column_reduce_small(r, c):
+    say("column reduce", r, c)
+    spec, params, _ = W.column_reduce_max_f32(r, c, seed=50 + c)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] in ("column_reduce", "row_reduce")
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "f32")
+
+
+def test_column_reduce_full_both_layouts():
+    spec, params, _ = W.column_reduce_max_f32()
+    say("column reduce full")
+    got, f = run_gpu(spec.nodes, params, reps=3)  # repeated launches reuse the counters
+    assert f.plan()["hero"] == "column_reduce"
+    want = params[0].reshape(16384, 4096).max(axis=0)
+    assert_bitexact(got, want, "f32")
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "f32")
+    spec_c, _, _ = W.column_reduce_max_f32(m2m=(0, 1))
+    colmajor = np.ascontiguousarray(params[0].reshape(16384, 4096).T).ravel()
+    got_c, fc = run_gpu(spec_c.nodes, [colmajor])
+    assert fc.plan()["hero"] == "row_reduce"
+    assert np.array_equal(got.view(np.uint32), got_c.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# special values and exhaustive bf16 exp
+# --------------------------------------------------------------------------
+def test_special_values_max_min_exp_log():
+    vals = [float("nan"), -0.0, 0.0, float("-inf"), float("inf"), 1.5, -2.0, 1e-40]
+    a = np.array([v for v in vals for _ in vals] * 2, np.float32)
+    b = np.array([w for _ in vals for w in vals] * 2, np.float32)
+    n = a.size
+    for op in ("maximum", "minimum"):
+        s = W.Spec()
+        x = s.parameter(0, "f32", [n])
+        y = s.parameter(1, "f32", [n])
+        s.binary(op, x, y, "f32", [n])
+        got, _ = run_gpu(s.nodes, [a, b])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [a, b]), "f32")
+    x = np.array([1.0, 0.0, -0.0, -1.0, np.inf, np.nan, 1e-45, 3.4e38, -np.inf, 88.7, -103.0, 0.5] * 4,
+                 np.float32)
+    for op in ("log", "exponential"):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [x.size])
+        s.unary(op, p, "f32", [x.size])
+        got, _ = run_gpu(s.nodes, [x])
+        assert_ulp(got, oracle.evaluate(s.nodes, [x]), "f32", 2)
+
+
+def test_exp_bf16_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = W.Spec()
+    p = s.parameter(0, "bf16", [65536])
+    s.unary("exponential", p, "bf16", [65536])
+    got, _ = run_gpu(s.nodes, [allbits])
+    d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), "bf16", 1)
+    say("bf16 exp: %d of 65536 inputs 1 ulp off" % int((d > 0).sum()))
+
+
+def test_exp_log_f32_sample():
+    g = W.rng(43)
+    for op, x in (("exponential", g.uniform(-103, 89, 1 << 20).astype(np.float32)),
+                  ("log", np.exp2(g.uniform(-149, 128, 1 << 20)).astype(np.float32))):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [x.size])
+        s.unary(op, p, "f32", [x.size])
+        got, _ = run_gpu(s.nodes, [x])
+        d = assert_ulp(got, oracle.evaluate(s.nodes, [x]), "f32", 2)
+        say(op, "ulp histogram", np.bincount(d.astype(np.int64)))
+
+
+# --------------------------------------------------------------------------
+# brute force over tiny shapes: transposes, broadcasts, layouts, reduces
+# --------------------------------------------------------------------------
+def _rand_perm_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        rank = int(rng.integers(2, 5))
+        dims = [int(v) for v in rng.integers(1, 4, rank)]
+        perm = [int(v) for v in rng.permutation(rank)]
+        m_in = [int(v) for v in rng.permutation(rank)]
+        m_out = [int(v) for v in rng.permutation(rank)]
+        dt = ["f32", "bf16"][int(rng.integers(0, 2))]
+        cases.append((dims, perm, m_in, m_out, dt))
+    return cases
+
+
+def test_brute_force_transpose_layouts():
+    for dims, perm, m_in, m_out, dt in _rand_perm_cases(44, 60):
+        n = int(np.prod(dims))
+        x = (np.arange(n, dtype=np.uint32) * 2654435761 % 65521).astype(np.float32)
+        if dt == "bf16":
+            x = (x.view(np.uint32) >> 16).astype(np.uint16)
+        s = W.Spec()
+        p = s.parameter(0, dt, dims, m_in)
+        s.transpose(p, perm, dt, [dims[q] for q in perm], m2m=m_out)
+        got, _ = run_gpu(s.nodes, [x])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), dt)
+
+
+def test_brute_force_broadcast():
+    rng = np.random.default_rng(45)
+    for _ in range(40):
+        rank = int(rng.integers(1, 4))
+        out_dims = [int(v) for v in rng.integers(1, 5, rank)]
+        k = int(rng.integers(0, rank + 1))
+        bd = sorted(int(v) for v in rng.choice(rank, k, replace=False))
+        if rng.integers(0, 2):
+            bd = bd[::-1]
+        od = [out_dims[d] if rng.integers(0, 3) else 1 for d in bd]
+        x = rng.standard_normal(max(1, int(np.prod(od)))).astype(np.float32)[: int(np.prod(od))]
+        m_out = [int(v) for v in rng.permutation(rank)]
+        s = W.Spec()
+        p = s.parameter(0, "f32", od)
+        b = s.broadcast_in_dim(p, bd, "f32", out_dims)
+        y = s.parameter(1, "f32", out_dims, m_out)
+        s.binary("add", b, y, "f32", out_dims, m2m=m_out)
+        yy = rng.standard_normal(int(np.prod(out_dims))).astype(np.float32)
+        got, _ = run_gpu(s.nodes, [x, yy])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x, yy]), "f32")
+
+
+def test_brute_force_reduce():
+    import compiler_hlo_amd as H
+    rng = np.random.default_rng(46)
+    done = 0
+    for _ in range(50):
+        rank = int(rng.integers(1, 4))
+        dims = [int(v) for v in rng.integers(1, 6, rank)]
+        k = int(rng.integers(1, rank + 1))
+        red = sorted(int(v) for v in rng.choice(rank, k, replace=False))
+        m2m = [int(v) for v in rng.permutation(rank)]
+        op = ["add", "max", "min"][int(rng.integers(0, 3))]
+        init = {"add": 0.0, "max": float("-inf"), "min": float("inf")}[op]
+        x = rng.integers(-8, 9, int(np.prod(dims))).astype(np.float32)
+        s = W.Spec()
+        p = s.parameter(0, "f32", dims, m2m)
+        s.reduce(p, red, op, init, "f32", [dims[d] for d in range(rank) if d not in red])
+        try:
+            got, _ = run_gpu(s.nodes, [x])
+        except H.FusionError as e:
+            assert e.status == "HF_ERR_UNSUPPORTED", str(e)
+            continue
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+        done += 1
+    assert done >= 30
+
+
+def test_reshape_bitcast_and_general():
+    g = W.rng(47)
+    x = g.standard_normal(24 * 16).astype(np.float32)
+    for out_dims in ([24, 16], [4, 6, 16], [1, 384], [6, 64], [16, 24]):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [24, 16])
+        e = s.unary("exponential", p, "f32", [24, 16])
+        s.reshape(e, "f32", out_dims)
+        got, _ = run_gpu(s.nodes, [x])
+        assert_ulp(got, oracle.evaluate(s.nodes, [x]), "f32", 2)
+
+
+# --------------------------------------------------------------------------
+# GELU (bf16, tanh form)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(2, 8, 64), (6, 512, 4096)])
+def test_gelu_bf16(shape):
+    say("gelu", shape)
+    spec, params, _ = W.gelu_bf16(*shape)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "loop"
+    d = assert_ulp(got, oracle.evaluate(spec.nodes, params), "bf16", 2)
+    say("gelu ulp histogram", np.bincount(d.astype(np.int64)))
+
+
+# --------------------------------------------------------------------------
+# launch-time argument checks (host side, before any kernel runs)
+# --------------------------------------------------------------------------
+def test_launch_argument_errors():
+    import torch
+    import compiler_hlo_amd as H
+    spec, params, _ = W.transpose_exp_f32(64, 64)
+    f = H.Fusion(spec.nodes)
+    x = to_device(params[0])
+    out = torch.empty(64 * 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(H.FusionError) as e:
+        f.launch_ptrs([], out.data_ptr())
+    assert e.value.status == "HF_ERR_INVALID"
+    with pytest.raises(H.FusionError) as e:
+        f.launch_ptrs([x.data_ptr() + 4], out.data_ptr())
+    assert e.value.status == "HF_ERR_INVALID"
+    with pytest.raises(H.FusionError) as e:
+        f.launch_ptrs([x.data_ptr()], x.data_ptr())
+    assert e.value.status == "HF_ERR_INVALID" and "overlaps" in e.value.message
+    f(x, out=out)
+    torch.cuda.synchronize()
+    assert from_device(out, "f32").size == 4096
