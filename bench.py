@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the hero-fusion library on one MI355X.
+
+Workload (one "step"): the transpose fusion pair
+  * out = transpose(exp(x), {1,0}), x f32[4096,4096] ~ N(0,1), row-major in/out;
+  * out = transpose(x, {0,2,1}),    x bf16[64,512,1024] ~ N(0,1), row-major in/out;
+each executed once, through the C ABI, on torch's current stream.
+
+Inputs are generated on the host (seeded), copied to HBM before timing, and
+rotated over several buffer sets so that no launch finds its operands in the
+256 MB Infinity Cache left there by the previous launch.  The timed region
+is bracketed by torch.cuda.synchronize(); inside it the launches of each
+fusion run back to back between one pair of HIP events on the launch stream,
+which gives each kernel's average launch time.
+
+Prints ONE JSON line (metric, value in GB/s of algorithmic bytes, roofline
+of the dominant kernel, the oracle's CPU baseline).  Per-config hero numbers
+for the other workloads go into "heroes" (and to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_params(params):
+    import numpy as np
+    import torch
+    out = []
+    for p in params:
+        b = p.view(np.int16) if p.dtype == np.uint16 else p
+        out.append(torch.from_numpy(np.ascontiguousarray(b)).cuda())
+    return out
+
+
+class Case:
+    """One compiled fusion with rotating resident buffer sets."""
+
+    def __init__(self, make, args=(), kwargs=None, sets=None, transform=None):
+        import torch
+        import compiler_hlo_amd as H
+        self.spec, self.params, self.meta = make(*args, **(kwargs or {}))
+        if transform:
+            self.params = transform(self.params)
+        self.fusion = H.Fusion(self.spec.nodes)
+        self.plan = self.fusion.plan()
+        self.bytes = self.plan["algorithmic_bytes"]
+        work = self.bytes
+        if sets is None:
+            sets = max(2, min(64, math.ceil(3 * MALL_BYTES / max(work, 1))))
+        self.sets = []
+        base = device_params(self.params)
+        for s in range(sets):
+            ins = base if s == 0 else [t.clone() for t in base]
+            out = self.fusion(*ins)
+            self.sets.append((ins, out))
+        torch.cuda.synchronize()
+        self.k = 0
+
+    def launch(self, stream):
+        ins, out = self.sets[self.k % len(self.sets)]
+        self.k += 1
+        self.fusion.launch_ptrs([t.data_ptr() for t in ins], out.data_ptr(), stream.cuda_stream)
+
+
+def time_cases(cases, steps, warmup):
+    """Time `steps` steps; a step launches every case once.  Inside the timed
+    region the launches are grouped by case (all of case 0, then all of case
+    1, ...) with one HIP event pair around each group on the launch stream, so
+    the per-case average launch time carries no per-launch event overhead.
+    Returns (wall seconds per step, [mean seconds per launch of each case])."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for c in cases:
+            c.launch(stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i, c in enumerate(cases):
+        for _ in range(steps):
+            c.launch(stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = [evs[i].elapsed_time(evs[i + 1]) / steps / 1e3 for i in range(len(cases))]
+    return wall, per
+
+
+def cpu_baseline(makers):
+    """The oracle, as it stands, single-threaded, on the full workload of one
+    step (about 6-7 s of CPU work here).  Only evaluation is timed."""
+    import oracle
+    total_bytes, total_t = 0, 0.0
+    for make in makers:
+        spec, params, meta = make()
+        t0 = time.perf_counter()
+        oracle.evaluate(spec.nodes, params)
+        total_t += time.perf_counter() - t0
+        total_bytes += meta["bytes"]
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "one full step: exp-transpose f32[4096,4096] + transpose bf16[64,512,1024]; "
+                      "%.2f s single-threaded on the host" % total_t}
+
+
+def load_traffic(name, source_hash):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE,
+    WRITE_SIZE), kept in profiles/traffic.json with the hash of the kernel
+    source it was taken on; None once the kernel has changed."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        t = json.load(open(path))[name]
+    except Exception:
+        return None
+    if t.get("source_fnv1a") != source_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def fnv1a(s: str) -> str:
+    h = 1469598103934665603
+    for c in s.encode():
+        h ^= c
+        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return "%016x" % h
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-heroes", action="store_true", help="skip the per-config hero table")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", default=None, help="time one named workload alone (profiling)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the fusion is a single-device hot path); "
+              "--gpus %d is not supported" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+
+    if a.only:
+        makers = {
+            "transpose_exp_f32": (W.transpose_exp_f32, {}),
+            "transpose_bf16_021": (W.transpose_bf16_021, {}),
+            "row_reduce_exp_add_bf16": (W.row_reduce_exp_add_bf16, {}),
+            "column_reduce_max_f32": (W.column_reduce_max_f32, {}),
+            "quant_dequant_bias_requant": (W.quant_dequant_bias_requant, {}),
+            "loop_log_transpose_add": (W.loop_log_transpose_add, {}),
+            "gelu_bf16": (W.gelu_bf16, {}),
+        }
+        mk, kw = makers[a.only]
+        c = Case(mk, kwargs=kw)
+        wall, per = time_cases([c], a.steps, a.warmup)
+        log("%s: %.2f us/launch (events), %.1f GB/s" % (a.only, per[0] * 1e6, c.bytes / per[0] / 1e9))
+        return
+
+    log("building workloads ...")
+    c2a = Case(W.transpose_exp_f32)
+    c2b = Case(W.transpose_bf16_021)
+    cases = [c2a, c2b]
+    wall, per = time_cases(cases, a.steps, a.warmup)
+    step_bytes = c2a.bytes + c2b.bytes
+    value = step_bytes / wall / 1e9
+    dom = max(range(2), key=lambda i: per[i])
+    dc = cases[dom]
+    achieved = dc.bytes / per[dom] / 1e9
+    name = dc.meta["name"]
+    traffic = load_traffic(name, fnv1a(dc.fusion.source()))
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": name, "algorithmic_bytes": dc.bytes,
+            "avg_launch_us": round(per[dom] * 1e6, 3)}
+    log("step: %.2f us wall; %s %.2f us (%.1f GB/s), %s %.2f us (%.1f GB/s)" % (
+        wall * 1e6, c2a.meta["name"], per[0] * 1e6, c2a.bytes / per[0] / 1e9,
+        c2b.meta["name"], per[1] * 1e6, c2b.bytes / per[1] / 1e9))
+
+    sets_used = {c.meta["name"]: len(c.sets) for c in cases}
+    heroes = {}
+    for i, c in enumerate(cases):
+        heroes[c.meta["name"]] = {
+            "hero": c.plan["hero"], "us": round(per[i] * 1e6, 3),
+            "GBps": round(c.bytes / per[i] / 1e9, 1), "frac": round(c.bytes / per[i] / 1e9 / PEAK_HBM_GBS, 4),
+            "elements_per_s": float("%.4g" % (c.plan["elements"] / per[i]))}
+    del cases, c2a, c2b
+    torch.cuda.empty_cache()
+    if not a.no_heroes:
+        def copy_case(dtype, dims):
+            def make():
+                spec = W.Spec()
+                spec.parameter(0, dtype, dims)
+                n = W.numel(dims)
+                g = W.rng(99)
+                x = W.normal_f32(g, n) if dtype == "f32" else W.normal_bf16(g, n)
+                return spec, [x], {"name": "copy", "elements": n, "bytes": 2 * n * W.nbytes_of(dtype)}
+            return make
+        others = [("copy_f32_4096x4096 (calibration)", copy_case("f32", [4096, 4096]), {}, None),
+                  ("copy_bf16_64x512x1024 (calibration)", copy_case("bf16", [64, 512, 1024]), {}, None),
+                  ("loop_log_transpose_add", W.loop_log_transpose_add, {}, None),
+                  ("row_reduce_exp_add_bf16", W.row_reduce_exp_add_bf16, {}, None),
+                  ("column_reduce_max_f32", W.column_reduce_max_f32, {}, None),
+                  ("column_reduce_max_f32_colmajor", W.column_reduce_max_f32, {"m2m": (0, 1)},
+                   lambda ps: [ps[0].reshape(16384, 4096).T.copy().ravel()]),
+                  ("quant_dequant_bias_requant", W.quant_dequant_bias_requant, {}, None),
+                  ("gelu_bf16", W.gelu_bf16, {}, None)]
+        for key, mk, kw, tr in others:
+            c = Case(mk, kwargs=kw, transform=tr)
+            _, p = time_cases([c], 100, 10)
+            heroes[key] = {"hero": c.plan["hero"], "us": round(p[0] * 1e6, 3),
+                           "GBps": round(c.bytes / p[0] / 1e9, 1),
+                           "frac": round(c.bytes / p[0] / 1e9 / PEAK_HBM_GBS, 4),
+                           "elements_per_s": float("%.4g" % (c.plan["elements"] / p[0]))}
+            log("%-32s %-13s %9.2f us %8.1f GB/s  %5.1f%% of peak" % (
+                key, c.plan["hero"], p[0] * 1e6, c.bytes / p[0] / 1e9, 100 * c.bytes / p[0] / 1e9 / PEAK_HBM_GBS))
+            del c
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline([W.transpose_exp_f32, W.transpose_bf16_021])
+
+    line = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) per fusion hero; elements/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "transpose fusion: transpose(exp(x),{1,0}) f32[4096,4096] + "
+                               "transpose(x,{0,2,1}) bf16[64,512,1024], row-major in and out",
+                   "step_bytes": step_bytes, "buffer_sets": sets_used},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "heroes": heroes,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

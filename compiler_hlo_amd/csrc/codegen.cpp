@@ -2,16 +2,21 @@
 //
 // Each partition becomes one __device__ function of its root node's index
 // (XLA:GPU Emitters, "Subgraph functions": one index argument per dimension,
-// one result), computing HF_V lanes that advance along the function's lane
+// one result), computing V lanes that advance along the function's lane
 // dimension.  Parameters are read through the composed output-to-input index
 // maps ("Indexing transforms"); a read that is contiguous along the lane
-// becomes one vector load, a read that does not move with the lane one scalar
-// load, anything else one load per lane.  Functions of other partitions are
-// called with the mapped index.  The hero glue (hf_loop_eval, hf_tr_load, ...)
-// turns the hero's physical coordinates into logical indices and is followed
-// by the hand-written hero template.
+// becomes one raw vector load, a read that does not move with the lane one
+// scalar load, anything else one load per lane.
+//
+// Loads are split from compute: every partition function F comes with a
+// register struct hf_R_F and a fetch function F_fetch that issues all of F's
+// global loads (and those of the partitions F calls) into that struct.  The
+// hero templates call the fetch functions of a whole step (several rows,
+// tile rows or row chunks) before any compute, so all of the step's loads
+// are in flight together; the compute function F only unpacks registers.
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <sstream>
 
@@ -48,20 +53,38 @@ std::string rnd(hf_dtype dt, const std::string &x) {
   return x;
 }
 
+// register value of one stored element
+std::string elem_value(hf_dtype dt, const std::string &x) {
+  switch (dt) {
+    case HF_F32: return x;
+    case HF_BF16: return "hf_bf16_bits(" + x + ")";
+    case HF_F16: return "hf_f16_bits(" + x + ")";
+    default: return "(int)" + x;
+  }
+}
+
 struct Body {
-  std::ostringstream os;
+  std::ostringstream os;     // compute
+  std::ostringstream fetch;  // loads into R
+  std::ostringstream members;
   std::map<std::string, std::string> memo;
   int root = -1;
   int lane = -1;
   int V = 1;
   int tmp = 0;
+  int nmem = 0;
   bool tile = false;
 };
 
 class Gen {
  public:
-  Gen(const Graph &g, Plan &P) : g_(g), P_(P) {}
+  Gen(const Graph &g, Plan &P) : g_(g), P_(P) {
+    const char *nt = std::getenv("HF_NT");  // tuning knob: bit 0 loads, bit 1 stores
+    nt_loads_ = nt ? (std::atoi(nt) & 1) : true;
+  }
 
+  // Emits (once) the struct, fetch and compute functions of the partition
+  // rooted at `node` with lanes along `lane`; returns the function name.
   std::string fn(int ci, int node, int lane) {
     std::string name = "hf_c" + std::to_string(ci) + "_n" + std::to_string(node) + "_l" + std::to_string(lane + 1);
     if (done_.count(name)) return name;
@@ -74,15 +97,19 @@ class Gen {
     b.V = c.V;
     b.tile = c.leaf >= 0;
     std::string v = val(ci, b, node, identity_index(t.rank));
+    std::string idx;
+    for (int d = 0; d < t.rank; ++d) idx += ", int i" + std::to_string(d);
+    std::string tile = b.tile ? ", const " + tile_type() + " *__restrict__ hf_tile, int hf_w0, int hf_u0" : "";
     std::ostringstream f;
     f << "// partition of node " << node << " (" << op_name(g_.nodes[node].op) << "), lanes along "
       << (lane >= 0 ? "i" + std::to_string(lane) : std::string("nothing")) << "\n";
-    f << "__device__ __forceinline__ void " << name << "(const HfArgs &A";
-    if (b.tile) f << ", const " << tile_type() << " *__restrict__ hf_tile, int hf_w0, int hf_u0";
-    for (int d = 0; d < t.rank; ++d) f << ", int i" << d;
-    f << ", " << rtype(t) << " (&hf_out)[" << c.V << "]) {\n";
+    f << "struct hf_R_" << name << " {\n" << b.members.str() << "  char hf_pad;\n};\n";
+    f << "__device__ __forceinline__ void " << name << "_fetch(const HfArgs &A" << idx << ", hf_R_" << name
+      << " &R) {\n" << b.fetch.str() << "  (void)A; (void)R;\n}\n";
+    f << "__device__ __forceinline__ void " << name << "(const HfArgs &A" << tile << idx << ", const hf_R_" << name
+      << " &R, " << rtype(t) << " (&hf_out)[" << c.V << "]) {\n";
     f << b.os.str();
-    f << "#pragma unroll\n  for (int l = 0; l < " << c.V << "; ++l) hf_out[l] = " << v << "[l];\n}\n\n";
+    f << "#pragma unroll\n  for (int l = 0; l < " << c.V << "; ++l) hf_out[l] = " << v << "[l];\n  (void)A; (void)R;\n}\n\n";
     defs_ << f.str();
     return name;
   }
@@ -96,6 +123,7 @@ class Gen {
 
  private:
   std::string fresh(Body &b, int n) { return "v" + std::to_string(n) + "_" + std::to_string(b.tmp++); }
+  std::string member(Body &b) { return "s" + std::to_string(b.nmem++); }
 
   std::string offset(const Type &t, const Index &E) {
     std::vector<long long> st = phys_strides(t);
@@ -117,54 +145,76 @@ class Gen {
     return -1;
   }
 
-  std::string scalar_load(hf_dtype dt, const std::string &ptr, const std::string &off) {
-    std::string x = ptr + "[" + off + "]";
-    switch (dt) {
-      case HF_F32: return x;
-      case HF_BF16: return "hf_bf16_bits(" + x + ")";
-      case HF_F16: return "(float)__builtin_bit_cast(_Float16, " + x + ")";
-      default: return "(int)" + x;
-    }
-  }
-
-  std::string vector_load(hf_dtype dt, const std::string &ptr, const std::string &off, int V,
-                          const std::string &dst) {
-    switch (dt) {
-      case HF_F32: return "hf_ld_f32<" + std::to_string(V) + ">(" + ptr + ", " + off + ", " + dst + ");";
-      case HF_BF16: return "hf_ld_h<" + std::to_string(V) + ", false>(" + ptr + ", " + off + ", " + dst + ");";
-      case HF_F16: return "hf_ld_h<" + std::to_string(V) + ", true>(" + ptr + ", " + off + ", " + dst + ");";
-      case HF_S8: return "hf_ld_b<" + std::to_string(V) + ", true>(" + ptr + ", " + off + ", " + dst + ");";
-      case HF_U8: return "hf_ld_b<" + std::to_string(V) + ", false>(" + ptr + ", " + off + ", " + dst + ");";
-      case HF_S32: return "hf_ld_i32<" + std::to_string(V) + ">(" + ptr + ", " + off + ", " + dst + ");";
-    }
-    return "";
-  }
-
-  // Load of an array (parameter or per-axis quantization array) of type
-  // (dt, t) at index E into a new V-lane register array.
+  // Load of an array (parameter or per-axis quantization array) of element
+  // type dt and shape t, at index E: the raw load goes to the fetch function,
+  // the unpack to the compute function.  Returns the V-lane register array.
   std::string load(Body &b, int tag, const char *reg, hf_dtype dt, const Type &t, const std::string &ptr,
-                   const Index &E) {
+                   const Index &E, bool stream = false) {
     std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
+    std::string m = member(b);
     std::string off = offset(t, E);
-    int ld = b.V > 1 ? lane_dim(E, b.lane) : -1;
+    const int V = b.V;
+    const int es = dtype_bytes(dt);
+    int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     std::vector<long long> st = phys_strides(t);
-    b.os << "  " << reg << " " << v << "[" << b.V << "];\n";
+    b.os << "  " << reg << " " << v << "[" << V << "];\n";
+    if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
+      b.members << "  " << ctype(dt) << " " << m << ";\n";
+      b.fetch << "  R." << m << " = " << ptr << "[" << off << "];\n";
+      b.os << "  { const " << reg << " s = " << elem_value(dt, "R." + m) << ";\n";
+      b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
+    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V * es >= 4) {  // contiguous: raw vector load
+      const int nb = V * es;
+      b.members << "  hf_u32 " << m << "[" << nb / 4 << "];\n";
+      b.fetch << "  hf_raw_ld<" << nb << (stream ? ", true" : "") << ">(" << ptr << ", (long)(" << off << ") * " << es
+              << ", R." << m << ");\n";
+      switch (dt) {
+        case HF_F32: b.os << "  hf_unpack_f32<" << V << ">(R." << m << ", " << v << ");\n"; break;
+        case HF_S32: b.os << "  hf_unpack_i32<" << V << ">(R." << m << ", " << v << ");\n"; break;
+        case HF_BF16: b.os << "  hf_unpack_h<" << V << ", false>(R." << m << ", " << v << ");\n"; break;
+        case HF_F16: b.os << "  hf_unpack_h<" << V << ", true>(R." << m << ", " << v << ");\n"; break;
+        case HF_S8: b.os << "  hf_unpack_b<" << V << ", true>(R." << m << ", " << v << ");\n"; break;
+        case HF_U8: b.os << "  hf_unpack_b<" << V << ", false>(R." << m << ", " << v << ");\n"; break;
+      }
+    } else {  // one load per lane
+      b.members << "  " << ctype(dt) << " " << m << "[" << V << "];\n";
+      b.fetch << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) R." << m
+              << "[l] = " << ptr << "[o + l * " << st[ld] << "]; }\n";
+      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = "
+           << elem_value(dt, "R." + m + "[l]") << ";\n";
+    }
+    return v;
+  }
+
+  // Load of a double array (per-axis reciprocal scales) at index E.
+  std::string load_f64(Body &b, int tag, const Type &t, const std::string &ptr, const Index &E) {
+    std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
+    std::string m = member(b);
+    std::string off = offset(t, E);
+    const int V = b.V;
+    int ld = V > 1 ? lane_dim(E, b.lane) : -1;
+    b.os << "  double " << v << "[" << V << "];\n";
     if (ld < 0 || t.dims[ld] <= 1) {
-      b.os << "  { const " << reg << " s = " << scalar_load(dt, ptr, off) << ";\n";
-      b.os << "#pragma unroll\n    for (int l = 0; l < " << b.V << "; ++l) " << v << "[l] = s; }\n";
-    } else if (st[ld] == 1 && t.dims[ld] % b.V == 0) {
-      b.os << "  " << vector_load(dt, ptr, off, b.V, v) << "\n";
+      b.members << "  double " << m << ";\n";
+      b.fetch << "  R." << m << " = " << ptr << "[" << off << "];\n";
+      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = R." << m << ";\n";
+    } else if (t.dims[ld] % V == 0) {  // 1-D array: contiguous along the lane
+      b.members << "  hf_u32 " << m << "[" << 2 * V << "];\n";
+      b.fetch << "  hf_raw_ld<" << 8 * V << ">(" << ptr << ", (long)(" << off << ") * 8, R." << m << ");\n";
+      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v
+           << "[l] = __builtin_bit_cast(double, (hf_u64)R." << m << "[2 * l] | ((hf_u64)R." << m << "[2 * l + 1] << 32));\n";
     } else {
-      b.os << "  { const int o = " << off << ";\n";
-      b.os << "#pragma unroll\n    for (int l = 0; l < " << b.V << "; ++l) " << v << "[l] = "
-           << scalar_load(dt, ptr, "o + l * " + std::to_string(st[ld])) << "; }\n";
+      b.members << "  double " << m << "[" << V << "];\n";
+      b.fetch << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) R." << m
+              << "[l] = " << ptr << "[o + l]; }\n";
+      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = R." << m << "[l];\n";
     }
     return v;
   }
 
   // per-axis / per-tensor quantization parameters at index E: names of a
-  // scale array and a zero-point array (V lanes each)
-  void quant_params(Body &b, int q, const Index &E, std::string *sc, std::string *zp) {
+  // scale array, a zero-point array and (if rc) a reciprocal-scale array
+  void quant_params(Body &b, int q, const Index &E, std::string *sc, std::string *zp, std::string *rc = nullptr) {
     const Quant &Q = g_.quants[q];
     if (Q.qdim < 0) {
       *sc = "hf_qs" + std::to_string(b.tmp++);
@@ -172,6 +222,13 @@ class Gen {
       b.os << "  float " << *sc << "[" << b.V << "]; int " << *zp << "[" << b.V << "];\n";
       b.os << "#pragma unroll\n  for (int l = 0; l < " << b.V << "; ++l) { " << *sc << "[l] = " << flit(Q.scales[0])
            << "; " << *zp << "[l] = " << Q.zero_points[0] << "; }\n";
+      if (rc) {
+        *rc = "hf_qr" + std::to_string(b.tmp++);
+        char buf[64];
+        std::snprintf(buf, sizeof buf, "%a", reciprocal(Q.scales[0]));
+        b.os << "  double " << *rc << "[" << b.V << "];\n#pragma unroll\n  for (int l = 0; l < " << b.V << "; ++l) "
+             << *rc << "[l] = " << buf << ";\n";
+      }
       return;
     }
     Type vt;
@@ -181,6 +238,7 @@ class Gen {
     Index e1{E[Q.qdim]};
     vt.dt = HF_F32;
     *sc = load(b, 9000 + q, "float", HF_F32, vt, "A.qs" + std::to_string(q), e1);
+    if (rc) *rc = load_f64(b, 9200 + q, vt, "A.qr" + std::to_string(q), e1);
     vt.dt = Q.storage;
     *zp = load(b, 9100 + q, "int", Q.storage, vt, "A.qz" + std::to_string(q), e1);
   }
@@ -207,18 +265,22 @@ class Gen {
       b.os << "  { const int o = (" << term_str(tw) << " - hf_w0) * HF_PITCH + (" << term_str(tu) << " - hf_u0);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << b.V << "; ++l) " << v << "[l] = hf_tile[o + l]; }\n";
     } else if (nd.op == HF_PARAMETER) {
-      v = load(b, n, rtype(t), t.dt, t, "A.p" + std::to_string(nd.param), E);
+      v = load(b, n, rtype(t), t.dt, t, "A.p" + std::to_string(nd.param), E, is_streaming(g_, n) && nt_loads_);
     } else if (nd.op == HF_CONSTANT) {
       v = fresh(b, n);
       lanes(b, v, "float", flit(round_to_dtype(nd.cst, t.dt)));
     } else if (other_partition) {
       int ld = lane_dim(E, b.lane);
       std::string f = fn(ci, n, ld);
+      std::string m = member(b);
+      std::string args;
+      for (int d = 0; d < t.rank; ++d) args += ", " + term_str(E[d]);
+      b.members << "  hf_R_" << f << " " << m << ";\n";
+      b.fetch << "  " << f << "_fetch(A" << args << ", R." << m << ");\n";
       v = fresh(b, n);
       b.os << "  " << rtype(t) << " " << v << "[" << b.V << "];\n  " << f << "(A";
       if (b.tile) b.os << ", hf_tile, hf_w0, hf_u0";
-      for (int d = 0; d < t.rank; ++d) b.os << ", " << term_str(E[d]);
-      b.os << ", " << v << ");\n";
+      b.os << args << ", R." << m << ", " << v << ");\n";
     } else {
       std::vector<std::string> a;
       for (int o : nd.opd) {
@@ -272,11 +334,12 @@ class Gen {
             lanes(b, y0, "float", sc + "[l] * (float)(" + x + " - " + zp + "[l])");
           }
           const Quant &Q = g_.quants[t.quant];
-          std::string sc, zp;
-          quant_params(b, t.quant, E, &sc, &zp);
+          std::string sc, zp, rc;
+          quant_params(b, t.quant, E, &sc, &zp, &rc);
           v = fresh(b, n);
-          lanes(b, v, "int", "hf_quantize(" + y0 + "[l], " + sc + "[l], " + zp + "[l], " + std::to_string(Q.smin) +
-                                 ", " + std::to_string(Q.smax) + ")");
+          b.os << "  int " << v << "[" << b.V << "];\n  hf_quantize_v<" << b.V << ">(" << y0 << ", " << rc << ", " << zp
+               << ", " << Q.smin << ", " << Q.smax << ", " << v << ");\n";
+          (void)sc;
           break;
         }
         default:
@@ -289,11 +352,12 @@ class Gen {
 
   const Graph &g_;
   Plan &P_;
+  bool nt_loads_ = true;
   std::ostringstream defs_;
   std::map<std::string, bool> done_;
 };
 
-// "i<d> = t % D; t /= D" over dims (minor -> major), size-1 dims set to 0
+// "i<d> = t % D; t /= D" over dims (minor -> major)
 void delinearize(std::ostringstream &os, const Type &t, const std::vector<int> &dims, const std::string &from,
                  const char *tmp) {
   os << "  int " << tmp << " = " << from << ";\n";
@@ -342,11 +406,24 @@ std::string out_offset(const Type &t) {
   return s.empty() ? "0" : s;
 }
 
+// Glue pair: NAME_fetch(A, <coords>, REGS &R) and NAME(A, <coords>, const REGS &R, out)
+// that set up the index variables with `indices` and call the partition.
+void glue_pair(std::ostringstream &glue, const std::string &name, const std::string &coords,
+               const std::string &regs, const std::string &fn, const std::string &idx_code,
+               const std::string &args, const std::string &extra_params, const std::string &extra_args,
+               const std::string &out_decl) {
+  glue << "__device__ __forceinline__ void " << name << "_fetch(const HfArgs &A, " << coords << ", " << regs
+       << " &R) {\n" << idx_code << "  " << fn << "_fetch(A" << args << ", R);\n}\n";
+  glue << "__device__ __forceinline__ void " << name << "(const HfArgs &A" << extra_params << ", " << coords
+       << ", const " << regs << " &R, " << out_decl << ") {\n" << idx_code << "  " << fn << "(A" << extra_args << args
+       << ", R, hf_res);\n}\n";
+}
+
 }  // namespace
 
 std::string generate_source(const Graph &g, Plan &P, const std::string &prelude, const std::string &hero_text) {
   Gen gen(g, P);
-  std::ostringstream glue;
+  std::ostringstream glue, types;
   const Node &R = g.nodes[g.root];
   const Type &rt = R.t;
 
@@ -364,17 +441,19 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         }
       }
       long long DL = c.lane >= 0 ? rt.dims[c.lane] : 1;
-      glue << "__device__ __forceinline__ void hf_loop_eval(const HfArgs &A, int row, int colv, hf_val_t (&r)[HF_V]) {\n";
-      if (!rows.empty()) delinearize(glue, rt, rows, "row", "hf_t");
-      else glue << "  (void)row;\n";
+      std::ostringstream ix;
+      if (!rows.empty()) delinearize(ix, rt, rows, "row", "hf_t");
+      else ix << "  (void)row;\n";
       if (c.lane >= 0) {
         set[c.lane] = 1;
-        glue << "  const int i" << c.lane << " = colv * HF_V;\n";
+        ix << "  const int i" << c.lane << " = colv * HF_V;\n";
       } else {
-        glue << "  (void)colv;\n";
+        ix << "  (void)colv;\n";
       }
-      zero_dims(glue, rt, set);
-      glue << "  " << f << "(A" << call_args(rt) << ", r);\n}\n";
+      zero_dims(ix, rt, set);
+      types << "typedef hf_R_" << f << " hf_regs_t;\n";
+      glue_pair(glue, "hf_loop_eval", "int row, int colv", "hf_regs_t", f, ix.str(), call_args(rt), "", "",
+                "hf_val_t (&hf_res)[HF_V]");
       glue << "__device__ __forceinline__ void hf_loop_store(const HfArgs &A, int row, int colv, const hf_val_t (&r)[HF_V]) {\n";
       glue << "  " << store_call(rt.dt, c.V, "row * " + std::to_string(DL) + " + colv * HF_V", "r") << "\n}\n";
       break;
@@ -393,25 +472,30 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         }
       }
       set[P.lane_in] = set[P.lane_out] = 1;
-      auto indices = [&](std::ostringstream &os) {
-        if (!batch.empty()) delinearize(os, rt, batch, "b", "hf_t");
-        else os << "  (void)b;\n";
-        os << "  const int i" << P.lane_in << " = w;\n  const int i" << P.lane_out << " = u;\n";
-        zero_dims(os, rt, set);
-      };
-      glue << "__device__ __forceinline__ void hf_tr_load(const HfArgs &A, int b, int w, int u, hf_tile_t (&r)[HF_VIN]) {\n";
-      indices(glue);
-      glue << "  " << fl << "(A" << call_args(rt) << ", r);\n}\n";
-      glue << "__device__ __forceinline__ void hf_tr_eval(const HfArgs &A, const hf_tile_t *__restrict__ hf_tile, int hf_w0, int hf_u0, int b, int w, int u, hf_val_t (&r)[HF_VOUT]) {\n";
+      std::ostringstream ix;
+      if (!batch.empty()) delinearize(ix, rt, batch, "b", "hf_t");
+      else ix << "  (void)b;\n";
+      ix << "  const int i" << P.lane_in << " = w;\n  const int i" << P.lane_out << " = u;\n";
+      zero_dims(ix, rt, set);
+      types << "typedef hf_R_" << fl << " hf_ldregs_t;\n";
+      glue_pair(glue, "hf_tr_load", "int b, int w, int u", "hf_ldregs_t", fl, ix.str(), call_args(rt), "", "",
+                "hf_tile_t (&hf_res)[HF_VIN]");
       if (P.staged == g.root) {
-        glue << "  (void)A; (void)b;\n  const int o = (w - hf_w0) * HF_PITCH + (u - hf_u0);\n";
+        types << "struct hf_stregs_t { char hf_pad; };\n";
+        glue << "__device__ __forceinline__ void hf_tr_eval_fetch(const HfArgs &A, int b, int w, int u, hf_stregs_t &R) {"
+                " (void)A; (void)b; (void)w; (void)u; (void)R; }\n";
+        glue << "__device__ __forceinline__ void hf_tr_eval(const HfArgs &A, const hf_tile_t *__restrict__ hf_tile, "
+                "int hf_w0, int hf_u0, int b, int w, int u, const hf_stregs_t &R, hf_val_t (&r)[HF_VOUT]) {\n";
+        glue << "  (void)A; (void)b; (void)R;\n  const int o = (w - hf_w0) * HF_PITCH + (u - hf_u0);\n";
         glue << "#pragma unroll\n  for (int l = 0; l < HF_VOUT; ++l) r[l] = hf_tile[o + l];\n}\n";
       } else {
-        indices(glue);
-        glue << "  " << fs << "(A, hf_tile, hf_w0, hf_u0" << call_args(rt) << ", r);\n}\n";
+        types << "typedef hf_R_" << fs << " hf_stregs_t;\n";
+        glue_pair(glue, "hf_tr_eval", "int b, int w, int u", "hf_stregs_t", fs, ix.str(), call_args(rt),
+                  ", const hf_tile_t *__restrict__ hf_tile, int hf_w0, int hf_u0", ", hf_tile, hf_w0, hf_u0",
+                  "hf_val_t (&hf_res)[HF_VOUT]");
       }
       glue << "__device__ __forceinline__ void hf_tr_store(const HfArgs &A, int b, int w, int u, const hf_val_t (&r)[HF_VOUT]) {\n";
-      indices(glue);
+      glue << ix.str();
       glue << "  " << store_call(rt.dt, st.V, out_offset(rt), "r") << "\n}\n";
       break;
     }
@@ -429,56 +513,54 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
       std::vector<int> kept_inc;
       for (int d = 0; d < it.rank; ++d)
         if (!red[d]) kept_inc.push_back(d);
-      std::ostringstream outoff;
+      std::string outoff;
       {
         std::vector<long long> ost = phys_strides(rt);
-        std::string s;
         for (int r = 0; r < rt.rank; ++r) {
           if (rt.dims[r] <= 1) continue;
-          if (!s.empty()) s += " + ";
-          s += "i" + std::to_string(kept_inc[r]);
-          if (ost[r] != 1) s += " * " + std::to_string(ost[r]);
+          if (!outoff.empty()) outoff += " + ";
+          outoff += "i" + std::to_string(kept_inc[r]);
+          if (ost[r] != 1) outoff += " * " + std::to_string(ost[r]);
         }
-        outoff << (s.empty() ? "0" : s);
+        if (outoff.empty()) outoff = "0";
       }
-      std::string fin = "hf_red<HF_OP>(" + flit(round_to_dtype(R.init, rt.dt)) + ", acc)";
-      fin = rnd(rt.dt, fin);
-      std::string store = rt.dt == HF_F32 ? "  A.out[" + outoff.str() + "] = v;\n"
-                                          : "  { float s1[1] = {v}; " + store_call(rt.dt, 1, outoff.str(), "s1") + " }\n";
+      std::string fin = rnd(rt.dt, "hf_red<HF_OP>(" + flit(round_to_dtype(R.init, rt.dt)) + ", acc)");
+      std::string store = rt.dt == HF_F32 ? "  A.out[" + outoff + "] = v;\n"
+                                          : "  { float s1[1] = {v}; " + store_call(rt.dt, 1, outoff, "s1") + " }\n";
       bool is_row = P.hero == HF_HERO_ROW_REDUCE;
-      const char *ev = is_row ? "hf_rr_eval" : "hf_cr_eval";
-      glue << "__device__ __forceinline__ void " << ev << "(const HfArgs &A, int " << (is_row ? "row, int kv" : "r, int c")
-           << ", float (&x)[HF_V]) {\n";
-      std::vector<char> kset(it.rank, 0);
+      std::ostringstream ix;
+      const char *outer = is_row ? "row" : "c";
       if (is_row) {
-        if (!kept.empty()) delinearize(glue, it, kept, "row", "hf_t");
-        else glue << "  (void)row;\n";
-        if (!reduced.empty()) delinearize(glue, it, reduced, "kv * HF_V", "hf_k");
-        else glue << "  (void)kv;\n";
+        if (!kept.empty()) delinearize(ix, it, kept, "row", "hf_t");
+        else ix << "  (void)row;\n";
+        if (!reduced.empty()) delinearize(ix, it, reduced, "kv * HF_V", "hf_k");
+        else ix << "  (void)kv;\n";
       } else {
-        if (!kept.empty()) delinearize(glue, it, kept, "c", "hf_t");
-        else glue << "  (void)c;\n";
-        if (!reduced.empty()) delinearize(glue, it, reduced, "r", "hf_k");
-        else glue << "  (void)r;\n";
+        if (!kept.empty()) delinearize(ix, it, kept, "c", "hf_t");
+        else ix << "  (void)c;\n";
+        if (!reduced.empty()) delinearize(ix, it, reduced, "r", "hf_k");
+        else ix << "  (void)r;\n";
       }
-      zero_dims(glue, it, set);
-      glue << "  " << f << "(A" << call_args(it) << ", x);\n}\n";
-      const char *stn = is_row ? "hf_rr_store" : "hf_cr_store";
-      glue << "__device__ __forceinline__ void " << stn << "(const HfArgs &A, int " << (is_row ? "row" : "c")
-           << ", float acc) {\n";
-      if (!kept.empty()) delinearize(glue, it, kept, is_row ? "row" : "c", "hf_t");
-      else glue << "  (void)" << (is_row ? "row" : "c") << ";\n";
-      std::vector<char> kset2(it.rank, 0);
-      for (int d : kept) kset2[d] = 1;
+      zero_dims(ix, it, set);
+      types << "typedef hf_R_" << f << " hf_regs_t;\n";
+      glue_pair(glue, is_row ? "hf_rr_eval" : "hf_cr_eval", is_row ? "int row, int kv" : "int r, int c", "hf_regs_t",
+                f, ix.str(), call_args(it), "", "", "float (&hf_res)[HF_V]");
+      glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store" : "hf_cr_store") << "(const HfArgs &A, int "
+           << outer << ", float acc) {\n";
+      if (!kept.empty()) delinearize(glue, it, kept, outer, "hf_t");
+      else glue << "  (void)" << outer << ";\n";
+      std::vector<char> kset(it.rank, 0);
+      for (int d : kept) kset[d] = 1;
       for (int d : kept_inc)
-        if (!kset2[d]) glue << "  const int i" << d << " = 0;\n";
+        if (!kset[d]) glue << "  const int i" << d << " = 0;\n";
       glue << "  const float v = " << fin << ";\n" << store << "}\n";
-      (void)kset;
       break;
     }
   }
 
   std::ostringstream src;
+  if (const char *nt = std::getenv("HF_NT"))  // tuning knob: bit 0 loads, bit 1 stores
+    src << "#define HF_NT_STORES " << ((std::atoi(nt) >> 1) & 1) << "\n";
   src << prelude << "\n";
   // kernel parameters and the argument bundle
   std::ostringstream params, fields, init;
@@ -500,18 +582,34 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
   for (int q : P.quant_args) {
     add("const float *", "qs" + std::to_string(q));
     add(std::string("const ") + ctype(g.quants[q].storage) + " *", "qz" + std::to_string(q));
+    add("const double *", "qr" + std::to_string(q));
   }
   add("void *", "ws");
   src << "struct HfArgs {\n" << fields.str() << "};\n";
   src << "#define HF_KERNEL_PARAMS " << params.str() << "\n";
   src << "#define HF_ARGS_INIT {" << init.str() << "}\n";
   for (auto &m : P.macros) src << "#define " << m.first << " " << m.second << "\n";
-  if (P.hero == HF_HERO_TRANSPOSE) {
-    src << "typedef " << gen.tile_type() << " hf_tile_t;\n";
-  }
+
+  if (P.hero == HF_HERO_TRANSPOSE) src << "typedef " << gen.tile_type() << " hf_tile_t;\n";
   src << "typedef " << rtype(rt) << " hf_val_t;\n\n";
-  src << gen.defs() << glue.str() << "\n" << hero_text;
-  return src.str();
+  src << gen.defs() << types.str() << glue.str() << "\n" << hero_text;
+  // kernel name: hero, result type and shape, and a hash of the source, so
+  // profiles can tell fusions apart
+  std::string body = src.str();
+  uint64_t h = 1469598103934665603ull;
+  for (unsigned char ch : body) {
+    h ^= ch;
+    h *= 1099511628211ull;
+  }
+  std::ostringstream name;
+  name << "hf_" << hero_template_name(P.hero) << "_" << dtype_name(rt.dt);
+  for (int d = 0; d < rt.rank; ++d) name << (d ? "x" : "_") << rt.dims[d];
+  char hx[16];
+  std::snprintf(hx, sizeof hx, "_%08x", (unsigned)(h >> 32));
+  name << hx;
+  P.kernel_name = name.str();
+  P.fold_name = P.kernel_name + "_fold";
+  return "#define HF_KERNEL_NAME " + P.kernel_name + "\n#define HF_FOLD_NAME " + P.fold_name + "\n" + body;
 }
 
 }  // namespace hf

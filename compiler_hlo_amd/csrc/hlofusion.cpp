@@ -33,6 +33,7 @@ struct hf_fusion {
   int device = -1;
   hipModule_t mod = nullptr;
   hipFunction_t fn = nullptr;
+  hipFunction_t fold = nullptr;  // column reduce: segment fold kernel
   void *ws = nullptr;
   std::vector<void *> qdev;  // scales, zero points per per-axis quant type
 };
@@ -186,13 +187,15 @@ hf_status load_on_device(hf_fusion *f) {
   }
   e = hipModuleLoadData(&f->mod, f->code.data());
   if (e != hipSuccess) return hip_fail(e, "hipModuleLoadData");
-  e = hipModuleGetFunction(&f->fn, f->mod, "hf_kernel");
+  e = hipModuleGetFunction(&f->fn, f->mod, f->P.kernel_name.c_str());
   if (e != hipSuccess) return hip_fail(e, "hipModuleGetFunction");
+  if (f->P.fold_grid > 0) {
+    e = hipModuleGetFunction(&f->fold, f->mod, f->P.fold_name.c_str());
+    if (e != hipSuccess) return hip_fail(e, "hipModuleGetFunction(fold)");
+  }
   if (f->P.ws_bytes > 0) {
     e = hipMalloc(&f->ws, (size_t)f->P.ws_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    e = hipMemset(f->ws, 0, (size_t)f->P.ws_bytes);  // counters start at zero; kernels reset them
-    if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
   }
   for (int q : f->P.quant_args) {
     const hf::Quant &Q = f->g.quants[q];
@@ -204,12 +207,20 @@ hf_status load_on_device(hf_fusion *f) {
     e = hipMalloc(&z, n + 16);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(zero points)");
     f->qdev.push_back(z);
+    void *rc = nullptr;
+    e = hipMalloc(&rc, n * 8 + 16);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(reciprocal scales)");
+    f->qdev.push_back(rc);
     std::vector<signed char> zb(n);
     for (size_t i = 0; i < n; ++i) zb[i] = (signed char)Q.zero_points[i];  // u8 keeps its bit pattern
+    std::vector<double> rb(n);
+    for (size_t i = 0; i < n; ++i) rb[i] = hf::reciprocal(Q.scales[i]);
     if ((e = hipMemcpy(s, Q.scales.data(), n * 4, hipMemcpyHostToDevice)) != hipSuccess)
       return hip_fail(e, "hipMemcpy(scales)");
     if ((e = hipMemcpy(z, zb.data(), n, hipMemcpyHostToDevice)) != hipSuccess)
       return hip_fail(e, "hipMemcpy(zero points)");
+    if ((e = hipMemcpy(rc, rb.data(), n * 8, hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(reciprocal scales)");
   }
   return HF_OK;
 }
@@ -354,6 +365,11 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
   e = hipModuleLaunchKernel(f->fn, (unsigned)f->P.grid, 1, 1, (unsigned)f->P.block, 1, 1, 0, (hipStream_t)stream,
                             ptrs.data(), nullptr);
   if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+  if (f->fold) {
+    e = hipModuleLaunchKernel(f->fold, (unsigned)f->P.fold_grid, 1, 1, 256, 1, 1, 0, (hipStream_t)stream,
+                              ptrs.data(), nullptr);
+    if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(fold)");
+  }
   return HF_OK;
 }
 

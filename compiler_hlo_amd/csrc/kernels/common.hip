@@ -14,6 +14,8 @@
 typedef unsigned int hf_u32;
 typedef unsigned short hf_u16;
 typedef unsigned long long hf_u64;
+typedef unsigned int hf_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int hf_u32x2 __attribute__((ext_vector_type(2)));
 
 // The generated code defines the kernel's parameter list (HF_KERNEL_PARAMS:
 // one __restrict__ pointer per fusion parameter, the result, the per-axis
@@ -21,9 +23,14 @@ typedef unsigned long long hf_u64;
 // not alias), the struct HfArgs that bundles them and HF_ARGS_INIT.
 
 // ---------------------------------------------------------------- rounding
-// bf16 RNE through the hardware pack-convert (v_cvt_pk_bf16_f32), back to f32.
+// bf16 RNE in one instruction: v_cvt_pk_bf16_f32 of the pair (0, x) puts the
+// rounded bf16 of x in the upper half and zero in the lower half, which is
+// exactly the f32 bit pattern of the rounded value.
+typedef __bf16 hf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hf_f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float hf_rnd_bf16(float x) {
-  return __uint_as_float((hf_u32)__builtin_bit_cast(hf_u16, (__bf16)x) << 16);
+  const hf_f32x2 v = {0.0f, x};
+  return __builtin_bit_cast(float, __builtin_convertvector(v, hf_bf16x2));
 }
 __device__ __forceinline__ float hf_rnd_f16(float x) { return (float)(_Float16)x; }
 __device__ __forceinline__ float hf_bf16_bits(hf_u32 bits16) { return __uint_as_float(bits16 << 16); }
@@ -35,16 +42,16 @@ __device__ __forceinline__ float hf_max(float a, float b) { return __builtin_ele
 __device__ __forceinline__ float hf_min(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
 // ------------------------------------------------------- transcendentals
-// exp whose result is rounded to bf16 afterwards: 2^(x*log2 e) on the
-// hardware exp2 (v_exp_f32, about 1 ulp).  Relative error of the f32 value is
-// below 2^-16 over the whole bf16 range, far under half a bf16 ulp (2^-9), so
-// after rounding the bf16 result is within one bf16 ulp of the correctly
-// rounded one.  Arguments below -126 are scaled so the hardware sees a normal
-// result and the final multiply produces the subnormal.
+// exp whose result is rounded to bf16 afterwards: (2^(x*log2(e)/2))^2 on the
+// hardware exp2 (v_exp_f32, about 1 ulp).  The half-size argument keeps the
+// exp2 result normal down to final results of 2^-252, and the IEEE square
+// then produces subnormal results correctly -- no branch, no select.  The
+// f32 value's relative error stays below 2^-16 over the whole bf16 range,
+// far under half a bf16 ulp (2^-9), so after rounding the bf16 result is
+// within one bf16 ulp of the correctly rounded one.
 __device__ __forceinline__ float hf_exp_for_bf16(float x) {
-  float t = x * 1.44269504088896340736f;
-  if (t < -126.0f) return __builtin_amdgcn_exp2f(t + 64.0f) * 5.42101086242752217e-20f;
-  return __builtin_amdgcn_exp2f(t);
+  const float h = __builtin_amdgcn_exp2f(x * 0.72134752044448170368f);  // log2(e)/2
+  return h * h;
 }
 
 // ---------------------------------------------------------- reductions
@@ -91,91 +98,92 @@ __device__ __forceinline__ float hf_group_reduce(float v) {
 }
 
 // ------------------------------------------------------------ loads
-// Vector loads of V consecutive elements starting at element offset `off`
-// (off is a multiple of V, buffers are 16-byte aligned).
-template <int V>
-__device__ __forceinline__ void hf_ld_f32(const void *base, int off, float (&r)[V]) {
-  const float *p = (const float *)base + off;
-  if constexpr (V % 4 == 0) {
+// Global loads are split from their use: a fetch function issues the raw
+// loads of a whole hero step into registers (so every load of the step is in
+// flight at once), the compute function unpacks them.  Raw vector loads move
+// NB bytes (4..64) starting at a byte offset that is a multiple of NB.
+// Streaming operands (each byte used once) are loaded and stored with the
+// non-temporal hint: they stream through the caches instead of evicting
+// what is reused (per-axis parameters, biases).  HF_NT_STORES = 0 turns the
+// store hint off.
+#ifndef HF_NT_STORES
+#define HF_NT_STORES 1
+#endif
+template <int NB, bool NT = false>
+__device__ __forceinline__ void hf_raw_ld(const void *base, long byte_off, hf_u32 (&w)[NB / 4]) {
+  const char *p = (const char *)base + byte_off;
+  if constexpr (NB % 16 == 0) {
 #pragma unroll
-    for (int k = 0; k < V / 4; ++k) {
-      float4 t = ((const float4 *)p)[k];
-      r[4 * k] = t.x; r[4 * k + 1] = t.y; r[4 * k + 2] = t.z; r[4 * k + 3] = t.w;
+    for (int k = 0; k < NB / 16; ++k) {
+      hf_u32x4 t;
+      if constexpr (NT) t = __builtin_nontemporal_load((const hf_u32x4 *)p + k);
+      else t = ((const hf_u32x4 *)p)[k];
+      w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
     }
-  } else if constexpr (V == 2) {
-    float2 t = *(const float2 *)p;
-    r[0] = t.x; r[1] = t.y;
+  } else if constexpr (NB == 8) {
+    hf_u32x2 t;
+    if constexpr (NT) t = __builtin_nontemporal_load((const hf_u32x2 *)p);
+    else t = *(const hf_u32x2 *)p;
+    w[0] = t.x; w[1] = t.y;
   } else {
-    r[0] = p[0];
+    static_assert(NB == 4, "raw loads move 4, 8 or a multiple of 16 bytes");
+    if constexpr (NT) w[0] = __builtin_nontemporal_load((const hf_u32 *)p);
+    else w[0] = *(const hf_u32 *)p;
   }
 }
 template <int V>
-__device__ __forceinline__ void hf_ld_i32(const void *base, int off, int (&r)[V]) {
-  const int *p = (const int *)base + off;
+__device__ __forceinline__ void hf_unpack_f32(const hf_u32 (&w)[V], float (&r)[V]) {
 #pragma unroll
-  for (int k = 0; k < V; ++k) r[k] = p[k];
+  for (int k = 0; k < V; ++k) r[k] = __uint_as_float(w[k]);
 }
-// 16-bit floats: bf16 (F16=false) or f16 (F16=true)
+template <int V>
+__device__ __forceinline__ void hf_unpack_i32(const hf_u32 (&w)[V], int (&r)[V]) {
+#pragma unroll
+  for (int k = 0; k < V; ++k) r[k] = (int)w[k];
+}
+// 16-bit floats: bf16 (F16=false) or f16 (F16=true); V >= 2
 template <int V, bool F16>
-__device__ __forceinline__ void hf_ld_h(const void *base, int off, float (&r)[V]) {
-  const hf_u16 *p = (const hf_u16 *)base + off;
-  hf_u32 w[(V + 1) / 2];
-  if constexpr (V % 8 == 0) {
-#pragma unroll
-    for (int k = 0; k < V / 8; ++k) {
-      uint4 t = ((const uint4 *)p)[k];
-      w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
-    }
-  } else if constexpr (V == 4) {
-    uint2 t = *(const uint2 *)p;
-    w[0] = t.x; w[1] = t.y;
-  } else if constexpr (V == 2) {
-    w[0] = *(const hf_u32 *)p;
-  } else {
-    w[0] = p[0];
-  }
+__device__ __forceinline__ void hf_unpack_h(const hf_u32 (&w)[V / 2], float (&r)[V]) {
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    hf_u32 h = (k & 1) ? (w[k / 2] >> 16) : (w[k / 2] & 0xFFFFu);
-    if constexpr (F16) r[k] = (float)__builtin_bit_cast(_Float16, (hf_u16)h);
-    else r[k] = __uint_as_float(h << 16);
+    const hf_u32 x = w[k / 2];
+    if constexpr (F16) r[k] = (float)__builtin_bit_cast(_Float16, (hf_u16)((k & 1) ? (x >> 16) : (x & 0xFFFFu)));
+    else r[k] = __uint_as_float((k & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
 }
-// 8-bit integers, sign- or zero-extended
+// 8-bit integers, sign- or zero-extended; V >= 4
 template <int V, bool SIGNED>
-__device__ __forceinline__ void hf_ld_b(const void *base, int off, int (&r)[V]) {
-  const unsigned char *p = (const unsigned char *)base + off;
-  hf_u32 w[(V + 3) / 4];
-  if constexpr (V % 16 == 0) {
-#pragma unroll
-    for (int k = 0; k < V / 16; ++k) {
-      uint4 t = ((const uint4 *)p)[k];
-      w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
-    }
-  } else if constexpr (V == 8) {
-    uint2 t = *(const uint2 *)p;
-    w[0] = t.x; w[1] = t.y;
-  } else if constexpr (V == 4) {
-    w[0] = *(const hf_u32 *)p;
-  } else {
-#pragma unroll
-    for (int k = 0; k < V; ++k) w[0] = (k == 0 ? 0u : w[0]) | ((hf_u32)p[k] << (8 * k));
-  }
+__device__ __forceinline__ void hf_unpack_b(const hf_u32 (&w)[V / 4], int (&r)[V]) {
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    hf_u32 b = (w[k / 4] >> (8 * (k & 3))) & 0xFFu;
+    const hf_u32 b = (w[k / 4] >> (8 * (k & 3))) & 0xFFu;
     r[k] = SIGNED ? (int)(signed char)b : (int)b;
   }
 }
+// Keeps the machine scheduler from sinking the loads of a fetch phase below
+// the compute that follows it (it otherwise trades memory-level parallelism
+// for register pressure).
+#define HF_LOADS_ISSUED() __builtin_amdgcn_sched_barrier(0)
+
+__device__ __forceinline__ float hf_f16_bits(hf_u32 h) { return (float)__builtin_bit_cast(_Float16, (hf_u16)h); }
 
 // ------------------------------------------------------------ stores
+template <typename T>
+__device__ __forceinline__ void hf_vst(T *p, T v) {
+#if HF_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 template <int V>
 __device__ __forceinline__ void hf_st_f32(void *base, int off, const float (&r)[V]) {
   float *p = (float *)base + off;
   if constexpr (V % 4 == 0) {
 #pragma unroll
     for (int k = 0; k < V / 4; ++k)
-      ((float4 *)p)[k] = make_float4(r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]);
+      hf_vst((hf_u32x4 *)p + k, hf_u32x4{__float_as_uint(r[4 * k]), __float_as_uint(r[4 * k + 1]),
+                                         __float_as_uint(r[4 * k + 2]), __float_as_uint(r[4 * k + 3])});
   } else if constexpr (V == 2) {
     *(float2 *)p = make_float2(r[0], r[1]);
   } else {
@@ -203,7 +211,7 @@ __device__ __forceinline__ void hf_st_h(void *base, int off, const float (&r)[V]
     if constexpr (V % 8 == 0) {
 #pragma unroll
       for (int k = 0; k < V / 8; ++k)
-        ((uint4 *)p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+        hf_vst((hf_u32x4 *)p + k, hf_u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
     } else if constexpr (V == 4) {
       *(uint2 *)p = make_uint2(w[0], w[1]);
     } else {
@@ -225,7 +233,7 @@ __device__ __forceinline__ void hf_st_b(void *base, int off, const int (&r)[V]) 
     if constexpr (V % 16 == 0) {
 #pragma unroll
       for (int k = 0; k < V / 16; ++k)
-        ((uint4 *)p)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+        hf_vst((hf_u32x4 *)p + k, hf_u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
     } else if constexpr (V == 8) {
       *(uint2 *)p = make_uint2(w[0], w[1]);
     } else {
@@ -253,4 +261,24 @@ __device__ __forceinline__ int hf_quantize(float y, float scale, int zp, int smi
   float r = __builtin_rintf(t);
   r = __builtin_fminf(__builtin_fmaxf(r, (float)(smin - zp)), (float)(smax - zp));
   return (int)r + zp;
+}
+
+// The same result for V values without a division: rcp is 1/scale rounded
+// to the nearest double (computed on the host).  q = fl64(y * rcp) is within
+// 2^-52 (relative) of y/scale, while y/scale -- a quotient of two f32 values
+// -- is never closer than 2^-49 (relative) to the midpoint between two
+// adjacent f32 values: its distance to a 25-bit midpoint m is
+// |y - scale*m| / scale >= 2^(E-24)/2^24 for m in [2^E, 2^(E+1)).  So
+// (float)q is exactly fl32(y/scale), the IEEE quotient, for all finite
+// inputs, with no branch and four full-rate instructions.
+template <int V>
+__device__ __forceinline__ void hf_quantize_v(const float (&y)[V], const double (&rcp)[V], const int (&zp)[V],
+                                              int smin, int smax, int (&q)[V]) {
+#pragma unroll
+  for (int l = 0; l < V; ++l) {
+    const float t = (float)((double)y[l] * rcp[l]);
+    const float r = __builtin_rintf(t);
+    const float c = __builtin_fminf(__builtin_fmaxf(r, (float)(smin - zp[l])), (float)(smax - zp[l]));
+    q[l] = (int)c + zp[l];
+  }
 }

@@ -6,14 +6,16 @@
 // Each thread keeps ONE column vector for its whole life and strides over
 // rows, so every value that depends only on the column (per-axis scales,
 // zero points, a bias broadcast along the rows) is loop-invariant and is
-// loaded once per thread.  HF_UNROLL rows are evaluated before their stores so
-// that the loads of several rows are in flight together.
+// loaded once per thread.  Per step a thread first issues the loads of
+// HF_UNROLL rows (hf_loop_eval_fetch), then computes and stores them, so the
+// loads of all those rows are in flight together.
 //
 // Provided by the generated code in front of this text:
 //   HF_BLOCK, HF_V, HF_ROWS, HF_COLS_V, HF_TPR (threads per row segment),
 //   HF_RPB (rows per block step), HF_NCH (column chunks), HF_UNROLL,
-//   hf_val_t, hf_loop_eval(A, row, colv, r), hf_loop_store(A, row, colv, r).
-extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAMS) {
+//   hf_val_t, hf_regs_t, hf_loop_eval_fetch(A, row, colv, R),
+//   hf_loop_eval(A, row, colv, R, r), hf_loop_store(A, row, colv, r).
+extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x % HF_NCH;
@@ -25,15 +27,22 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAM
   const int rstep = ngroups * HF_RPB;
   int row = group * HF_RPB + rsub;
   for (; row + (HF_UNROLL - 1) * rstep < HF_ROWS; row += HF_UNROLL * rstep) {
-    hf_val_t r[HF_UNROLL][HF_V];
+    hf_regs_t R[HF_UNROLL];
 #pragma unroll
-    for (int u = 0; u < HF_UNROLL; ++u) hf_loop_eval(A, row + u * rstep, colv, r[u]);
+    for (int u = 0; u < HF_UNROLL; ++u) hf_loop_eval_fetch(A, row + u * rstep, colv, R[u]);
+    HF_LOADS_ISSUED();
 #pragma unroll
-    for (int u = 0; u < HF_UNROLL; ++u) hf_loop_store(A, row + u * rstep, colv, r[u]);
+    for (int u = 0; u < HF_UNROLL; ++u) {
+      hf_val_t r[HF_V];
+      hf_loop_eval(A, row + u * rstep, colv, R[u], r);
+      hf_loop_store(A, row + u * rstep, colv, r);
+    }
   }
   for (; row < HF_ROWS; row += rstep) {
+    hf_regs_t R1;
+    hf_loop_eval_fetch(A, row, colv, R1);
     hf_val_t r[HF_V];
-    hf_loop_eval(A, row, colv, r);
+    hf_loop_eval(A, row, colv, R1, r);
     hf_loop_store(A, row, colv, r);
   }
 }

@@ -4,16 +4,18 @@
 // memory).
 //
 // HF_TPR == HF_BLOCK: one workgroup per row (grid-strided over rows).  Each
-// lane accumulates HF_V lanes of 128-bit loads in registers, then the wave
-// reduces with DPP (hf_wave_reduce) and the waves combine through LDS.
-// Anything the prologue reads that depends only on the position in the row
-// (a bias broadcast along the rows) is loop-invariant across rows.
+// lane first issues the loads of all its chunks of the row (128-bit each),
+// then accumulates them in registers; the wave reduces with DPP
+// (hf_wave_reduce) and the waves combine through LDS.  Anything the prologue
+// reads that depends only on the position in the row (a bias broadcast
+// along the rows) is loop-invariant across rows.
 // HF_TPR < 64: short rows; HF_BLOCK/HF_TPR rows per workgroup step, reduced
 // within lane groups by cross-lane shuffles.
 //
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
-// (vectors per row), HF_TPR, hf_rr_eval(A, row, kv, x), hf_rr_store(A, row, acc).
-extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAMS) {
+// (vectors per row), HF_TPR, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
+// hf_rr_eval(A, row, kv, R, x), hf_rr_store(A, row, acc).
+extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
 #if HF_TPR == HF_BLOCK
   __shared__ float part[HF_BLOCK / 64];
@@ -23,12 +25,24 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAM
     float acc[HF_V];
 #pragma unroll
     for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
+    if constexpr (HF_KV % HF_BLOCK == 0) {
+      hf_regs_t R[ITERS];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int kv = it * HF_BLOCK + (int)threadIdx.x;
-      if (HF_KV % HF_BLOCK == 0 || kv < HF_KV) {
+      for (int it = 0; it < ITERS; ++it) hf_rr_eval_fetch(A, row, it * HF_BLOCK + (int)threadIdx.x, R[it]);
+      HF_LOADS_ISSUED();
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) {
         float x[HF_V];
-        hf_rr_eval(A, row, kv, x);
+        hf_rr_eval(A, row, it * HF_BLOCK + (int)threadIdx.x, R[it], x);
+#pragma unroll
+        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
+      }
+    } else {
+      for (int kv = threadIdx.x; kv < HF_KV; kv += HF_BLOCK) {
+        hf_regs_t R1;
+        hf_rr_eval_fetch(A, row, kv, R1);
+        float x[HF_V];
+        hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
         for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
       }
@@ -58,8 +72,10 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void hf_kernel(HF_KERNEL_PARAM
     for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
     if (row < HF_ROWS) {
       for (int kv = sub; kv < HF_KV; kv += HF_TPR) {
+        hf_regs_t R1;
+        hf_rr_eval_fetch(A, row, kv, R1);
         float x[HF_V];
-        hf_rr_eval(A, row, kv, x);
+        hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
         for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
       }

@@ -214,11 +214,7 @@ Access classify(const Graph &g, int p, const Index &E, int lane) {
   return at == phys_minor(t) ? CONTIG : STRIDED;
 }
 
-bool large(const Graph &g, int p) {
-  long long n = g.nodes[p].t.numel();
-  long long out = g.nodes[g.root].t.numel();
-  return n >= 1024 && n * 4 >= out;
-}
+bool large(const Graph &g, int p) { return is_streaming(g, p); }
 
 // largest element size among large params read contiguously along the lane
 int stream_elem_bytes(const Graph &g, const Ctx &c, int dflt) {
@@ -314,7 +310,16 @@ Plan plan_loop(const Graph &g, Ctx c) {
     rpb = block / tpr;
     nch = 1;
   }
-  long long target = env_ll("HF_LOOP_WGS", 2048);
+  // One row step per thread for pure streaming; four when the fusion also
+  // reads small arrays (per-axis parameters, broadcast biases), whose loads
+  // a thread then reuses across rows.
+  bool small = false;
+  for (auto &pr : c.param_reads)
+    if (!is_streaming(g, pr.first)) small = true;
+  for (const Quant &q : g.quants)
+    if (q.qdim >= 0) small = true;
+  long long per = small ? 4 : 1;
+  long long target = env_ll("HF_LOOP_WGS", nch * ceil_div(ceil_div(rows, rpb), per));
   long long ngroups = std::max<long long>(1, std::min(ceil_div(rows, rpb), std::max<long long>(1, target / nch)));
   P.ctx.push_back(c);
   P.block = block;
@@ -496,7 +501,7 @@ Plan plan_reduce(const Graph &g) {
       tpr = pow2_ceil(std::max<long long>(1, kv));
     }
     long long rpb = tpr == block ? 1 : block / tpr;
-    long long target = env_ll("HF_ROW_WGS", 1024);
+    long long target = env_ll("HF_ROW_WGS", 8192);
     P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb), target));
     P.block = block;
     P.lds_bytes = (block / 64) * 4;
@@ -516,7 +521,7 @@ Plan plan_reduce(const Graph &g) {
     int rl = block / cl;
     long long cb = (long long)cl * V;
     long long ncb = ceil_div(Cc, cb);
-    long long target = env_ll("HF_COL_WGS", 2048);
+    long long target = env_ll("HF_COL_WGS", 4096);
     long long segs = std::max<long long>(1, std::min(target / ncb, ceil_div(Rr, rl)));
     long long rs = Rr > 0 ? ceil_div(Rr, segs) : 0;
     segs = rs > 0 ? ceil_div(Rr, rs) : 1;
@@ -524,13 +529,12 @@ Plan plan_reduce(const Graph &g) {
     P.block = block;
     P.lds_bytes = (int)(rl * cb * 4 + 4);
     if (segs > 1) {
-      P.ws_counter_off = ((segs * Cc * 4 + 255) / 256) * 256;
-      P.ws_counters = (int)ncb;
-      P.ws_bytes = P.ws_counter_off + ncb * 4;
+      P.ws_bytes = segs * Cc * 4;
+      P.fold_grid = ceil_div(Cc, 64);
     }
     P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_C", Cc}, {"HF_R", Rr},
                 {"HF_CL", cl}, {"HF_RL", rl}, {"HF_CB", cb}, {"HF_NCB", ncb}, {"HF_S", segs},
-                {"HF_RS", rs}};
+                {"HF_RS", rs}, {"HF_CR_UNROLL", env_ll("HF_COL_UNROLL", 8)}};
     P.info.vector_elems = V;
     P.info.rows = Rr;
     P.info.cols = Cc;
@@ -544,6 +548,13 @@ Plan plan_reduce(const Graph &g) {
 }
 
 }  // namespace
+
+bool is_streaming(const Graph &g, int p) {
+  long long n = g.nodes[p].t.numel();
+  long long out = g.nodes[g.root].t.numel();
+  if (g.nodes[g.root].op == HF_REDUCE) out = g.nodes[g.nodes[g.root].opd[0]].t.numel();
+  return n >= 1024 && n * 4 >= out;
+}
 
 const char *hero_template_name(hf_hero h) {
   switch (h) {
@@ -612,6 +623,8 @@ static double round_bits(double x, int p, int emin, int emax) {
   if (r > maxf) r = INFINITY;
   return sign ? -r : r;
 }
+
+double reciprocal(float s) { return 1.0 / (double)s; }
 
 double round_to_dtype(double x, hf_dtype dt) {
   switch (dt) {

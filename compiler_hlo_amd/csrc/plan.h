@@ -69,9 +69,15 @@ struct Plan {
   bool empty = false;         // nothing to launch (zero-size result)
   hf_plan_info info{};
   std::vector<int> quant_args;  // quant indices passed as per-axis arrays
+  std::string kernel_name;      // set by generate_source
+  std::string fold_name;        // column reduce with segments: the fold kernel
+  long long fold_grid = 0;      // 0: no fold kernel
 };
 
 Plan make_plan(const Graph &g);
+// A parameter the fusion streams (comparable in size to the result): read
+// once, with the non-temporal hint.
+bool is_streaming(const Graph &g, int param_node);
 std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
                             const std::string &hero_text);
 const char *hero_template_name(hf_hero h);
@@ -79,5 +85,7 @@ const char *hero_template_name(hf_hero h);
 // Constants: round a double to an element type (RNE), the way a constant of
 // that type holds it.
 double round_to_dtype(double x, hf_dtype dt);
+// 1/s rounded to the nearest double (IEEE double division).
+double reciprocal(float s);
 
 }  // namespace hf

@@ -1,0 +1,297 @@
+"""Host-side tests of the C-ABI library (no GPU): exports, layout mapper,
+descriptor validation, planning decisions, code generation and compilation
+for gfx950, and the arithmetic claims the kernels rely on."""
+import itertools
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import compiler_hlo_amd as H
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def plan_of(spec):
+    return H.Fusion(spec.nodes, mode="plan").plan()
+
+
+# --------------------------------------------------------------------------
+# exports
+# --------------------------------------------------------------------------
+def test_exports_every_declared_function():
+    text = open(os.path.join(ROOT, "include", "hlofusion.h")).read()
+    declared = set(re.findall(r"\b(hf_[a-z_]+)\s*\(", text))
+    declared = {d for d in declared if not d.startswith("hf_fusion_desc")}
+    assert {"hf_fusion_create", "hf_fusion_launch", "hf_fusion_destroy"} <= declared
+    lib = H.library()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert lib.hf_abi_version() == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libhlofusion.so the package refuses to import: no fallback."""
+    pkg = tmp_path / "compiler_hlo_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "compiler_hlo_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run(["python", "-c", "import compiler_hlo_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "libhlofusion.so is missing" in r.stderr
+
+
+# --------------------------------------------------------------------------
+# layout mapper (Shapes and layout, "Array indexing")
+# --------------------------------------------------------------------------
+def test_linear_index_matches_oracle_all_small_shapes():
+    for rank in range(1, 5):
+        for dims in itertools.product([1, 2, 3], repeat=rank):
+            idx = list(itertools.product(*[range(d) for d in dims]))
+            for m2m in itertools.permutations(range(rank)):
+                got = [H.linear_index(list(dims), list(m2m), list(i)) for i in idx]
+                want = oracle.linear_indices(list(dims), list(m2m), np.array(idx)).tolist()
+                assert got == want
+
+
+def test_linear_index_rejects_bad_input():
+    assert H.linear_index([2, 3], [0, 0], [0, 0]) == -1
+    assert H.linear_index([2, 3], [1, 0], [2, 0]) == -1
+
+
+# --------------------------------------------------------------------------
+# validation: each broken constraint gives HF_ERR_INVALID with the node named
+# --------------------------------------------------------------------------
+def _status(nodes, **kw):
+    try:
+        H.Fusion(nodes, mode="plan", **kw)
+    except H.FusionError as e:
+        return e.status, e.message
+    return "HF_OK", ""
+
+
+def test_validation_errors():
+    s = W.Spec()
+    p = s.parameter(0, "f32", [2, 3])
+    s.transpose(p, [0, 0], "f32", [2, 3])
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "node 1 (transpose)" in msg and "permutation" in msg
+
+    s = W.Spec()
+    p = s.parameter(0, "f32", [2, 3], m2m=[0, 0])
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "minor_to_major" in msg
+
+    s = W.Spec()
+    a = s.parameter(0, "f32", [2, 3])
+    b = s.parameter(1, "f32", [3, 2])
+    s.binary("add", a, b, "f32", [2, 3])
+    assert _status(s.nodes)[0] == "HF_ERR_INVALID"
+
+    s = W.Spec()
+    a = s.parameter(0, "f32", [3])
+    s.broadcast_in_dim(a, [1], "f32", [3, 4])
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "(C5)" in msg
+
+    s = W.Spec()
+    a = s.parameter(0, "f32", [3])
+    s.broadcast_in_dim(a, [0, 1], "f32", [3, 3])
+    assert "(C2)" in _status(s.nodes)[1]
+
+    s = W.Spec()
+    a = s.parameter(0, "f32", [4, 5])
+    s.reduce(a, [1, 1], "add", 0.0, "f32", [4])
+    assert "(C5)" in _status(s.nodes)[1]
+
+    s = W.Spec()
+    a = s.parameter(0, "f32", [4, 5])
+    s.reduce(a, [1], "add", 0.0, "f32", [5])
+    assert "(C7)" in _status(s.nodes)[1]
+
+    # quantization constraints
+    s = W.Spec()
+    s.parameter(0, "s8", [4, 3], quant=W.quant_type("s8", [0.1, -0.2, 0.3], [0, 0, 0], qdim=1))
+    assert "(C6)" in _status(s.nodes)[1]
+    s = W.Spec()
+    s.parameter(0, "s8", [4, 3], quant=W.quant_type("s8", [0.1, 0.2], [0, 0], qdim=1))
+    assert "(C13)" in _status(s.nodes)[1]
+    s = W.Spec()
+    s.parameter(0, "s8", [4, 3], quant=W.quant_type("s8", [0.1], [300]))
+    assert "(C8)" in _status(s.nodes)[1]
+    s = W.Spec()
+    s.parameter(0, "s8", [4, 3], quant=W.quant_type("s8", [float("inf")], [0]))
+    assert "(C7)" in _status(s.nodes)[1]
+
+    # parameter numbering and operand order
+    s = W.Spec()
+    s.parameter(0, "f32", [2])
+    s.parameter(0, "f32", [2])
+    assert _status(s.nodes, n_params=1)[0] == "HF_ERR_INVALID"
+    nodes = [{"op": "log", "operands": [1], "dtype": "f32", "dims": [2]},
+             {"op": "parameter", "param": 0, "dtype": "f32", "dims": [2]}]
+    assert _status(nodes, root=0)[0] == "HF_ERR_INVALID"
+
+
+def test_unsupported_is_distinguished():
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4, 5])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [4])
+    s.unary("log", r, "f32", [4])
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "root" in msg
+
+
+# --------------------------------------------------------------------------
+# planning decisions
+# --------------------------------------------------------------------------
+def test_partitioning_of_log_transpose_add():
+    """param -> log -> {transpose, add}: the pages' partitioner makes three
+    one-instruction functions (XLA:GPU Emitters, "Partitioning")."""
+    spec, _, _ = W.loop_log_transpose_add(64)
+    p = plan_of(spec)
+    assert p["hero"] == "loop" and p["n_partitions"] == 3
+    # the same graph with exp in front of log: exp has one user and joins log
+    s = W.Spec()
+    x = s.parameter(0, "f32", [8, 8], [1, 0])
+    e = s.unary("exponential", x, "f32", [8, 8])
+    l = s.unary("log", e, "f32", [8, 8])
+    t = s.transpose(l, [1, 0], "f32", [8, 8])
+    s.binary("add", l, t, "f32", [8, 8])
+    assert plan_of(s)["n_partitions"] == 3
+    # a node read twice at the same index stays in its user's function
+    s = W.Spec()
+    x = s.parameter(0, "f32", [8, 8])
+    l = s.unary("log", x, "f32", [8, 8])
+    s.binary("multiply", l, l, "f32", [8, 8])
+    assert plan_of(s)["n_partitions"] == 1
+
+
+def test_hero_classification():
+    cases = [
+        (W.transpose_exp_f32(64, 96), "transpose"),
+        (W.transpose_bf16_021(2, 64, 96), "transpose"),
+        (W.row_reduce_exp_add_bf16(2, 4, 512), "row_reduce"),
+        (W.row_reduce_exp_add_bf16(2, 4, 512, m2m=(3, 2, 0, 1)), "row_reduce"),
+        (W.column_reduce_max_f32(256, 64), "column_reduce"),
+        (W.column_reduce_max_f32(256, 64, m2m=(0, 1)), "row_reduce"),
+        (W.quant_dequant_bias_requant(16, 64), "loop"),
+        (W.gelu_bf16(2, 4, 64), "loop"),
+    ]
+    for (spec, _, meta), hero in cases:
+        assert plan_of(spec)["hero"] == hero, meta["name"]
+    # a transpose that is the identity in memory is a plain loop
+    s = W.Spec()
+    x = s.parameter(0, "f32", [64, 32], [0, 1])
+    s.transpose(x, [1, 0], "f32", [32, 64], m2m=[1, 0])
+    assert plan_of(s)["hero"] == "loop"
+    # a layout change without a transpose op is still a transpose in memory
+    s = W.Spec()
+    x = s.parameter(0, "f32", [64, 32], [1, 0])
+    s.unary("exponential", x, "f32", [64, 32], m2m=[0, 1])
+    assert plan_of(s)["hero"] == "transpose"
+
+
+def test_algorithmic_bytes_of_the_workloads():
+    expect = {
+        "loop_log_transpose_add": 32768, "transpose_exp_f32": 134217728,
+        "transpose_bf16_021": 134217728, "row_reduce_exp_add_bf16": 335618048,
+        "column_reduce_max_f32": 268451840, "quant_dequant_bias_requant": 33591296,
+    }
+    for make in (W.loop_log_transpose_add, W.transpose_exp_f32, W.transpose_bf16_021,
+                 W.row_reduce_exp_add_bf16, W.column_reduce_max_f32, W.quant_dequant_bias_requant):
+        spec, _, meta = make()
+        assert plan_of(spec)["algorithmic_bytes"] == expect[meta["name"]], meta["name"]
+
+
+def test_transpose_tile_arithmetic_of_the_pages_example():
+    """The pages' transpose example (20x160x170 -> 170x160x20 with 32-wide tiles
+    over the two swapped dims) has 960 blocks; the same tile count follows
+    from our tiling rule with 32x32 tiles."""
+    ntiles = -(-20 // 32) * 160 * -(-170 // 32)
+    assert ntiles == 960
+    s = W.Spec()
+    x = s.parameter(0, "f32", [20, 160, 170])
+    e = s.unary("exponential", x, "f32", [20, 160, 170])
+    s.transpose(e, [2, 1, 0], "f32", [170, 160, 20])
+    os.environ["HF_TR_TU"], os.environ["HF_TR_TW"] = "32", "32"
+    try:
+        p = plan_of(s)
+    finally:
+        del os.environ["HF_TR_TU"], os.environ["HF_TR_TW"]
+    assert p["hero"] == "transpose" and p["grid_blocks"] == 960
+
+
+# --------------------------------------------------------------------------
+# code generation and compilation for gfx950
+# --------------------------------------------------------------------------
+WORKLOADS = [W.loop_log_transpose_add, W.transpose_exp_f32, W.transpose_bf16_021,
+             W.row_reduce_exp_add_bf16, W.column_reduce_max_f32, W.quant_dequant_bias_requant,
+             W.gelu_bf16]
+
+
+@pytest.mark.parametrize("make", WORKLOADS, ids=lambda m: m.__name__)
+def test_workload_compiles_for_gfx950(make):
+    spec, _, _ = make()
+    f = H.Fusion(spec.nodes, mode="compile")
+    src = f.source()
+    assert "HF_KERNEL_NAME" in src and "__builtin_amdgcn" in src
+
+
+@pytest.mark.skipif(shutil.which("/opt/rocm/bin/hipcc") is None, reason="needs hipcc")
+@pytest.mark.parametrize("make", [W.quant_dequant_bias_requant, W.row_reduce_exp_add_bf16,
+                                  W.transpose_exp_f32], ids=lambda m: m.__name__)
+def test_no_packed_fp32_and_no_scratch(make):
+    """The generated kernels, compiled with the library's flags, contain no
+    packed-FP32 instructions and use no scratch memory."""
+    spec, _, _ = make()
+    src = H.Fusion(spec.nodes, mode="compile").source()
+    with tempfile.TemporaryDirectory() as d:
+        hip = os.path.join(d, "k.hip")
+        co = os.path.join(d, "k.co")
+        open(hip, "w").write(src)
+        subprocess.check_call(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+                               "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
+                               "-packed-fp32-ops", "--cuda-device-only", "--no-gpu-bundle-output",
+                               "-include", "hip/hip_runtime.h", "-c", "-x", "hip", hip, "-o", co],
+                              stderr=subprocess.DEVNULL)
+        dis = subprocess.check_output(["/opt/rocm/llvm/bin/llvm-objdump", "-d", "--mcpu=gfx950", co]).decode()
+        notes = subprocess.check_output(["/opt/rocm/llvm/bin/llvm-readelf", "--notes", co]).decode()
+    assert not re.search(r"v_pk_(fma|mul|add)_f32", dis)
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", notes)
+
+
+def test_generated_code_is_deterministic():
+    spec, _, _ = W.quant_dequant_bias_requant(64, 128)
+    a = H.Fusion(spec.nodes, mode="compile").source()
+    b = H.Fusion(spec.nodes, mode="compile").source()
+    assert a == b
+
+
+# --------------------------------------------------------------------------
+# arithmetic claims the kernels rely on (checked on the host with numpy)
+# --------------------------------------------------------------------------
+def test_reciprocal_double_quotient_equals_ieee_f32_division():
+    """fl32(fl64(y * fl64(1/s))) == fl32(y / s) (IEEE) for f32 y and s: the
+    quantize kernels divide this way.  Random scales and values, and values
+    placed next to every rounding midpoint of the quotient."""
+    g = W.rng(70)
+    for _ in range(40):
+        s = np.float32(np.exp(g.uniform(np.log(1e-4), np.log(10.0))))
+        y = (g.standard_normal(200000) * g.uniform(0.01, 10)).astype(np.float32)
+        got = (y.astype(np.float64) * (1.0 / np.float64(s))).astype(np.float32)
+        want = y / s
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        # quotients next to f32 midpoints: y = fl32(m * s) around midpoints m
+        q = (g.standard_normal(50000) * 100).astype(np.float32)
+        m = (q.astype(np.float64) + np.spacing(q).astype(np.float64) / 2)
+        yy = (m * np.float64(s)).astype(np.float32)
+        for off in (-1, 0, 1):
+            y2 = (yy.view(np.int32) + off).view(np.float32)
+            got = (y2.astype(np.float64) * (1.0 / np.float64(s))).astype(np.float32)
+            assert np.array_equal(got.view(np.uint32), (y2 / s).view(np.uint32))
