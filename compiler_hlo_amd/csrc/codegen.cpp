@@ -146,68 +146,67 @@ class Gen {
   }
 
   // Load of an array (parameter or per-axis quantization array) of element
-  // type dt and shape t, at index E: the raw load goes to the fetch function,
-  // the unpack to the compute function.  Returns the V-lane register array.
+  // type dt and shape t, at index E, into a new V-lane register array.  A
+  // streaming operand's raw load goes to the fetch function (and the hero's
+  // fetch phase); small, reused arrays are loaded where they are used, so a
+  // value that does not change across the hero's steps is loaded once.
   std::string load(Body &b, int tag, const char *reg, hf_dtype dt, const Type &t, const std::string &ptr,
                    const Index &E, bool stream = false) {
     std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
-    std::string m = member(b);
     std::string off = offset(t, E);
     const int V = b.V;
     const int es = dtype_bytes(dt);
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     std::vector<long long> st = phys_strides(t);
     b.os << "  " << reg << " " << v << "[" << V << "];\n";
+    std::string m = stream ? "R." + member(b) : "w" + std::to_string(b.tmp++);
+    std::ostringstream &ld_os = stream ? b.fetch : b.os;
+    auto decl = [&](const std::string &type, int count) {
+      if (stream) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
+      else b.os << "  " << type << " " << m << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
+    };
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
-      b.members << "  " << ctype(dt) << " " << m << ";\n";
-      b.fetch << "  R." << m << " = " << ptr << "[" << off << "];\n";
-      b.os << "  { const " << reg << " s = " << elem_value(dt, "R." + m) << ";\n";
+      decl(ctype(dt), 0);
+      ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
+      b.os << "  { const " << reg << " s = " << elem_value(dt, m) << ";\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
     } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V * es >= 4) {  // contiguous: raw vector load
       const int nb = V * es;
-      b.members << "  hf_u32 " << m << "[" << nb / 4 << "];\n";
-      b.fetch << "  hf_raw_ld<" << nb << (stream ? ", true" : "") << ">(" << ptr << ", (long)(" << off << ") * " << es
-              << ", R." << m << ");\n";
+      decl("hf_u32", nb / 4);
+      ld_os << "  hf_raw_ld<" << nb << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off << ") * "
+            << es << ", " << m << ");\n";
       switch (dt) {
-        case HF_F32: b.os << "  hf_unpack_f32<" << V << ">(R." << m << ", " << v << ");\n"; break;
-        case HF_S32: b.os << "  hf_unpack_i32<" << V << ">(R." << m << ", " << v << ");\n"; break;
-        case HF_BF16: b.os << "  hf_unpack_h<" << V << ", false>(R." << m << ", " << v << ");\n"; break;
-        case HF_F16: b.os << "  hf_unpack_h<" << V << ", true>(R." << m << ", " << v << ");\n"; break;
-        case HF_S8: b.os << "  hf_unpack_b<" << V << ", true>(R." << m << ", " << v << ");\n"; break;
-        case HF_U8: b.os << "  hf_unpack_b<" << V << ", false>(R." << m << ", " << v << ");\n"; break;
+        case HF_F32: b.os << "  hf_unpack_f32<" << V << ">(" << m << ", " << v << ");\n"; break;
+        case HF_S32: b.os << "  hf_unpack_i32<" << V << ">(" << m << ", " << v << ");\n"; break;
+        case HF_BF16: b.os << "  hf_unpack_h<" << V << ", false>(" << m << ", " << v << ");\n"; break;
+        case HF_F16: b.os << "  hf_unpack_h<" << V << ", true>(" << m << ", " << v << ");\n"; break;
+        case HF_S8: b.os << "  hf_unpack_b<" << V << ", true>(" << m << ", " << v << ");\n"; break;
+        case HF_U8: b.os << "  hf_unpack_b<" << V << ", false>(" << m << ", " << v << ");\n"; break;
       }
     } else {  // one load per lane
-      b.members << "  " << ctype(dt) << " " << m << "[" << V << "];\n";
-      b.fetch << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) R." << m
-              << "[l] = " << ptr << "[o + l * " << st[ld] << "]; }\n";
+      decl(ctype(dt), V);
+      ld_os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << m
+            << "[l] = " << ptr << "[o + l * " << st[ld] << "]; }\n";
       b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = "
-           << elem_value(dt, "R." + m + "[l]") << ";\n";
+           << elem_value(dt, m + "[l]") << ";\n";
     }
     return v;
   }
 
-  // Load of a double array (per-axis reciprocal scales) at index E.
+  // Load of a double array (per-axis reciprocal scales) at index E, in the
+  // compute function (a small, reused array).
   std::string load_f64(Body &b, int tag, const Type &t, const std::string &ptr, const Index &E) {
     std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
-    std::string m = member(b);
     std::string off = offset(t, E);
     const int V = b.V;
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     b.os << "  double " << v << "[" << V << "];\n";
     if (ld < 0 || t.dims[ld] <= 1) {
-      b.members << "  double " << m << ";\n";
-      b.fetch << "  R." << m << " = " << ptr << "[" << off << "];\n";
-      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = R." << m << ";\n";
-    } else if (t.dims[ld] % V == 0) {  // 1-D array: contiguous along the lane
-      b.members << "  hf_u32 " << m << "[" << 2 * V << "];\n";
-      b.fetch << "  hf_raw_ld<" << 8 * V << ">(" << ptr << ", (long)(" << off << ") * 8, R." << m << ");\n";
-      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v
-           << "[l] = __builtin_bit_cast(double, (hf_u64)R." << m << "[2 * l] | ((hf_u64)R." << m << "[2 * l + 1] << 32));\n";
+      b.os << "  { const double s = " << ptr << "[" << off << "];\n#pragma unroll\n    for (int l = 0; l < " << V
+           << "; ++l) " << v << "[l] = s; }\n";
     } else {
-      b.members << "  double " << m << "[" << V << "];\n";
-      b.fetch << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) R." << m
-              << "[l] = " << ptr << "[o + l]; }\n";
-      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = R." << m << "[l];\n";
+      b.os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v
+           << "[l] = " << ptr << "[o + l]; }\n";
     }
     return v;
   }
@@ -265,7 +264,7 @@ class Gen {
       b.os << "  { const int o = (" << term_str(tw) << " - hf_w0) * HF_PITCH + (" << term_str(tu) << " - hf_u0);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << b.V << "; ++l) " << v << "[l] = hf_tile[o + l]; }\n";
     } else if (nd.op == HF_PARAMETER) {
-      v = load(b, n, rtype(t), t.dt, t, "A.p" + std::to_string(nd.param), E, is_streaming(g_, n) && nt_loads_);
+      v = load(b, n, rtype(t), t.dt, t, "A.p" + std::to_string(nd.param), E, is_streaming(g_, n));
     } else if (nd.op == HF_CONSTANT) {
       v = fresh(b, n);
       lanes(b, v, "float", flit(round_to_dtype(nd.cst, t.dt)));

@@ -227,9 +227,13 @@ __device__ __forceinline__ void hf_st_b(void *base, int off, const int (&r)[V]) 
   if constexpr (V >= 4) {
     hf_u32 w[V / 4];
 #pragma unroll
-    for (int k = 0; k < V / 4; ++k)
-      w[k] = ((hf_u32)r[4 * k] & 0xFFu) | (((hf_u32)r[4 * k + 1] & 0xFFu) << 8) |
-             (((hf_u32)r[4 * k + 2] & 0xFFu) << 16) | ((hf_u32)r[4 * k + 3] << 24);
+    for (int k = 0; k < V / 4; ++k) {
+      // low bytes of four values with three v_perm_b32: {r0, r1} and {r2, r3}
+      // into the low halves, then both halves into one word
+      const hf_u32 lo = __builtin_amdgcn_perm((hf_u32)r[4 * k + 1], (hf_u32)r[4 * k], 0x0C0C0400u);
+      const hf_u32 hi = __builtin_amdgcn_perm((hf_u32)r[4 * k + 3], (hf_u32)r[4 * k + 2], 0x0C0C0400u);
+      w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
     if constexpr (V % 16 == 0) {
 #pragma unroll
       for (int k = 0; k < V / 16; ++k)
@@ -271,14 +275,23 @@ __device__ __forceinline__ int hf_quantize(float y, float scale, int zp, int smi
 // |y - scale*m| / scale >= 2^(E-24)/2^24 for m in [2^E, 2^(E+1)).  So
 // (float)q is exactly fl32(y/scale), the IEEE quotient, for all finite
 // inputs, with no branch and four full-rate instructions.
+//
+// Rounding and conversion use one add: for |t| < 2^22, a = t + 1.5*2^23 lies
+// in [2^23, 2^24) where floats are the integers, so the add rounds t to the
+// nearest integer with ties to even (1.5*2^23 is even) and a is exactly
+// 1.5*2^23 + rne(t); its low mantissa bits hold rne(t) in two's complement.
+// The clamp is applied to a (bounds shifted by the same constant); |t| >=
+// 2^22 lies far outside any storage range and clamps the same way.  A zero
+// point is added after rounding, as an integer.
 template <int V>
 __device__ __forceinline__ void hf_quantize_v(const float (&y)[V], const double (&rcp)[V], const int (&zp)[V],
                                               int smin, int smax, int (&q)[V]) {
+  constexpr float M = 12582912.0f;  // 1.5 * 2^23
 #pragma unroll
   for (int l = 0; l < V; ++l) {
     const float t = (float)((double)y[l] * rcp[l]);
-    const float r = __builtin_rintf(t);
-    const float c = __builtin_fminf(__builtin_fmaxf(r, (float)(smin - zp[l])), (float)(smax - zp[l]));
-    q[l] = (int)c + zp[l];
+    const float a = t + M;
+    const float c = __builtin_fminf(__builtin_fmaxf(a, M + (float)(smin - zp[l])), M + (float)(smax - zp[l]));
+    q[l] = (int)(__float_as_uint(c) - __float_as_uint(M)) + zp[l];
   }
 }
