@@ -77,6 +77,99 @@ class Case:
         self.fusion.launch_ptrs([t.data_ptr() for t in ins], out.data_ptr(), stream.cuda_stream)
 
 
+def copy_case(dtype, dims):
+    """A fusion whose root is its parameter: a plain copy of known size (the
+    calibration kernel for the HBM counters)."""
+    import workloads as W
+
+    def make():
+        spec = W.Spec()
+        spec.parameter(0, dtype, dims)
+        n = W.numel(dims)
+        g = W.rng(99)
+        x = W.normal_f32(g, n) if dtype == "f32" else W.normal_bf16(g, n)
+        name = "copy_%s_%s" % (dtype, "x".join(map(str, dims)))
+        return spec, [x], {"name": name, "elements": n, "bytes": 2 * n * W.nbytes_of(dtype)}
+    return make
+
+
+def workload_makers():
+    """Every named workload: (maker, kwargs, params transform)."""
+    import workloads as W
+    return {
+        "transpose_exp_f32": (W.transpose_exp_f32, {}, None),
+        "transpose_bf16_021": (W.transpose_bf16_021, {}, None),
+        "row_reduce_exp_add_bf16": (W.row_reduce_exp_add_bf16, {}, None),
+        "column_reduce_max_f32": (W.column_reduce_max_f32, {}, None),
+        "column_reduce_max_f32_colmajor": (W.column_reduce_max_f32, {"m2m": (0, 1)},
+                                           lambda ps: [ps[0].reshape(16384, 4096).T.copy().ravel()]),
+        "quant_dequant_bias_requant": (W.quant_dequant_bias_requant, {}, None),
+        "loop_log_transpose_add": (W.loop_log_transpose_add, {}, None),
+        "gelu_bf16": (W.gelu_bf16, {}, None),
+        "copy_f32_4096x4096": (copy_case("f32", [4096, 4096]), {}, None),
+        "copy_bf16_64x512x1024": (copy_case("bf16", [64, 512, 1024]), {}, None),
+    }
+
+
+def read_pmc_csv(run_dir, counter):
+    """Mean value of `counter` per dispatch for each hf_* kernel in a rocprofv3
+    --pmc run written with --output-format csv."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = r.get("Kernel_Name", "")
+            if r.get("Counter_Name") != counter or not name.startswith("hf_"):
+                continue
+            per.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
+def write_traffic(pmc_root, names):
+    """Turn rocprofv3 --pmc runs into profiles/traffic.json.
+
+    Expects <pmc_root>/<workload>/<COUNTER>/ for COUNTER in FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), including the f32 copy.  Each counter is
+    scaled by the ratio that makes the copy's reading equal its known bytes
+    (read 4n, write 4n); a launch's traffic sums its kernels (a column reduce
+    with segments has a fold kernel too)."""
+    import compiler_hlo_amd as H
+    makers = workload_makers()
+    cal = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        got = read_pmc_csv(os.path.join(pmc_root, "copy_f32_4096x4096", ctr), ctr)
+        kib = sum(got.values())
+        cal[ctr] = (4 * 4096 * 4096) / (kib * 1024.0)
+    out = {"_calibration": {"kernel": "copy f32[4096,4096] (read 64 MiB, write 64 MiB)",
+                            "fetch_factor": round(cal["FETCH_SIZE"], 5),
+                            "write_factor": round(cal["WRITE_SIZE"], 5)}}
+    for name in names:
+        mk, kw, tr = makers[name]
+        spec, _, _ = mk(**kw)
+        f = H.Fusion(spec.nodes, mode="compile")
+        rec = {"source_fnv1a": fnv1a(f.source()), "algorithmic_bytes": f.plan()["algorithmic_bytes"]}
+        total = 0.0
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            got = read_pmc_csv(os.path.join(pmc_root, name, ctr), ctr)
+            kib = sum(got.values())
+            rec[ctr + "_KiB"] = round(kib, 1)
+            b = kib * 1024.0 * cal[ctr]
+            rec[ctr.split("_")[0].lower() + "_bytes"] = round(b)
+            total += b
+        rec["bytes_per_launch"] = round(total)
+        rec["traffic_over_algorithmic"] = round(total / rec["algorithmic_bytes"], 4)
+        out[name] = rec
+        log("%-32s fetch %.1f MB write %.1f MB  x%.3f of algorithmic" % (
+            name, rec["fetch_bytes"] / 1e6, rec["write_bytes"] / 1e6, rec["traffic_over_algorithmic"]))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1, sort_keys=True)
+    log("wrote", path)
+
+
 def time_cases(cases, steps, warmup):
     """Time `steps` steps; a step launches every case once.  Inside the timed
     region the launches are grouped by case (all of case 0, then all of case
@@ -149,33 +242,29 @@ def main():
     ap.add_argument("--no-heroes", action="store_true", help="skip the per-config hero table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", default=None, help="time one named workload alone (profiling)")
+    ap.add_argument("--traffic", default=None, metavar="PMC_DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc runs under PMC_DIR (no GPU)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the fusion is a single-device hot path); "
               "--gpus %d is not supported" % a.gpus, file=sys.stderr)
         sys.exit(2)
+    if a.traffic:
+        write_traffic(a.traffic, [n for n in workload_makers() if not n.startswith("copy_")])
+        return
 
     import torch
-    import workloads as W
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
 
     if a.only:
-        makers = {
-            "transpose_exp_f32": (W.transpose_exp_f32, {}),
-            "transpose_bf16_021": (W.transpose_bf16_021, {}),
-            "row_reduce_exp_add_bf16": (W.row_reduce_exp_add_bf16, {}),
-            "column_reduce_max_f32": (W.column_reduce_max_f32, {}),
-            "quant_dequant_bias_requant": (W.quant_dequant_bias_requant, {}),
-            "loop_log_transpose_add": (W.loop_log_transpose_add, {}),
-            "gelu_bf16": (W.gelu_bf16, {}),
-        }
-        mk, kw = makers[a.only]
-        c = Case(mk, kwargs=kw)
+        mk, kw, tr = workload_makers()[a.only]
+        c = Case(mk, kwargs=kw, transform=tr)
         wall, per = time_cases([c], a.steps, a.warmup)
         log("%s: %.2f us/launch (events), %.1f GB/s" % (a.only, per[0] * 1e6, c.bytes / per[0] / 1e9))
         return
 
+    import workloads as W
     log("building workloads ...")
     c2a = Case(W.transpose_exp_f32)
     c2b = Case(W.transpose_bf16_021)
@@ -202,35 +291,24 @@ def main():
         heroes[c.meta["name"]] = {
             "hero": c.plan["hero"], "us": round(per[i] * 1e6, 3),
             "GBps": round(c.bytes / per[i] / 1e9, 1), "frac": round(c.bytes / per[i] / 1e9 / PEAK_HBM_GBS, 4),
-            "elements_per_s": float("%.4g" % (c.plan["elements"] / per[i]))}
+            "elements_per_s": float("%.4g" % (c.plan["elements"] / per[i])),
+            "traffic": load_traffic(c.meta["name"], fnv1a(c.fusion.source()))}
     del cases, c2a, c2b
     torch.cuda.empty_cache()
     if not a.no_heroes:
-        def copy_case(dtype, dims):
-            def make():
-                spec = W.Spec()
-                spec.parameter(0, dtype, dims)
-                n = W.numel(dims)
-                g = W.rng(99)
-                x = W.normal_f32(g, n) if dtype == "f32" else W.normal_bf16(g, n)
-                return spec, [x], {"name": "copy", "elements": n, "bytes": 2 * n * W.nbytes_of(dtype)}
-            return make
-        others = [("copy_f32_4096x4096 (calibration)", copy_case("f32", [4096, 4096]), {}, None),
-                  ("copy_bf16_64x512x1024 (calibration)", copy_case("bf16", [64, 512, 1024]), {}, None),
-                  ("loop_log_transpose_add", W.loop_log_transpose_add, {}, None),
-                  ("row_reduce_exp_add_bf16", W.row_reduce_exp_add_bf16, {}, None),
-                  ("column_reduce_max_f32", W.column_reduce_max_f32, {}, None),
-                  ("column_reduce_max_f32_colmajor", W.column_reduce_max_f32, {"m2m": (0, 1)},
-                   lambda ps: [ps[0].reshape(16384, 4096).T.copy().ravel()]),
-                  ("quant_dequant_bias_requant", W.quant_dequant_bias_requant, {}, None),
-                  ("gelu_bf16", W.gelu_bf16, {}, None)]
-        for key, mk, kw, tr in others:
+        makers = workload_makers()
+        others = ["copy_f32_4096x4096", "copy_bf16_64x512x1024", "loop_log_transpose_add",
+                  "row_reduce_exp_add_bf16", "column_reduce_max_f32", "column_reduce_max_f32_colmajor",
+                  "quant_dequant_bias_requant", "gelu_bf16"]
+        for key in others:
+            mk, kw, tr = makers[key]
             c = Case(mk, kwargs=kw, transform=tr)
             _, p = time_cases([c], 100, 10)
             heroes[key] = {"hero": c.plan["hero"], "us": round(p[0] * 1e6, 3),
                            "GBps": round(c.bytes / p[0] / 1e9, 1),
                            "frac": round(c.bytes / p[0] / 1e9 / PEAK_HBM_GBS, 4),
-                           "elements_per_s": float("%.4g" % (c.plan["elements"] / p[0]))}
+                           "elements_per_s": float("%.4g" % (c.plan["elements"] / p[0])),
+                           "traffic": load_traffic(key, fnv1a(c.fusion.source()))}
             log("%-32s %-13s %9.2f us %8.1f GB/s  %5.1f%% of peak" % (
                 key, c.plan["hero"], p[0] * 1e6, c.bytes / p[0] / 1e9, 100 * c.bytes / p[0] / 1e9 / PEAK_HBM_GBS))
             del c
