@@ -47,6 +47,11 @@ const char *ctype(hf_dtype dt) {
 bool reg_is_float(const Type &t) { return is_float(t.dt) && t.quant < 0; }
 const char *rtype(const Type &t) { return reg_is_float(t) ? "float" : "int"; }
 
+bool env_flag(const char *name, bool dflt) {  // tuning and A/B switches
+  const char *v = std::getenv(name);
+  return v ? std::atoi(v) != 0 : dflt;
+}
+
 std::string rnd(hf_dtype dt, const std::string &x) {
   if (dt == HF_BF16) return "hf_rnd_bf16(" + x + ")";
   if (dt == HF_F16) return "hf_rnd_f16(" + x + ")";
@@ -74,6 +79,7 @@ struct Body {
   int tmp = 0;
   int nmem = 0;
   bool tile = false;
+  bool raw_root = false;  // the root's value is returned before its rounding
 };
 
 class Gen {
@@ -85,14 +91,18 @@ class Gen {
 
   // Emits (once) the struct, fetch and compute functions of the partition
   // rooted at `node` with lanes along `lane`; returns the function name.
-  std::string fn(int ci, int node, int lane) {
-    std::string name = "hf_c" + std::to_string(ci) + "_n" + std::to_string(node) + "_l" + std::to_string(lane + 1);
+  // With `raw`, the root's own rounding to a 16-bit float type is left to the
+  // caller (which rounds and packs pairs in one step).
+  std::string fn(int ci, int node, int lane, bool raw = false) {
+    std::string name = "hf_c" + std::to_string(ci) + "_n" + std::to_string(node) + "_l" + std::to_string(lane + 1) +
+                       (raw ? "_raw" : "");
     if (done_.count(name)) return name;
     done_[name] = true;
     const Ctx &c = P_.ctx[ci];
     const Type &t = g_.nodes[node].t;
     Body b;
     b.root = node;
+    b.raw_root = raw;
     b.lane = lane;
     b.V = c.V;
     b.tile = c.leaf >= 0;
@@ -287,6 +297,7 @@ class Gen {
         a.push_back(val(ci, b, o, operand_index(g_, n, E, &general)));
       }
       auto A0 = [&](const char *f) { return std::string(f) + "(" + a[0] + "[l])"; };
+      auto rnd = [&](hf_dtype dt, const std::string &e) { return b.raw_root && n == b.root ? e : hf::rnd(dt, e); };
       const std::string x = a.empty() ? "" : a[0] + "[l]";
       const std::string y = a.size() > 1 ? a[1] + "[l]" : "";
       switch (nd.op) {
@@ -501,7 +512,6 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
     case HF_HERO_ROW_REDUCE: case HF_HERO_COLUMN_REDUCE: {
       const Ctx &c = P.ctx[0];
       const Type &it = g.nodes[P.rin].t;
-      std::string f = gen.fn(0, c.root, c.lane);
       std::vector<char> red(it.rank, 0);
       for (int64_t d : R.attr) red[d] = 1;
       std::vector<int> kept, reduced;
@@ -541,9 +551,37 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         else ix << "  (void)r;\n";
       }
       zero_dims(ix, it, set);
-      types << "typedef hf_R_" << f << " hf_regs_t;\n";
-      glue_pair(glue, is_row ? "hf_rr_eval" : "hf_cr_eval", is_row ? "int row, int kv" : "int r, int c", "hf_regs_t",
-                f, ix.str(), call_args(it), "", "", "float (&hf_res)[HF_V]");
+      // A row sum of bf16 values converted to f32 (init not -0) accumulates
+      // packed bf16 pairs: the pair is rounded and packed by one conversion
+      // and added to the f32 accumulator by one two-term dot product with
+      // (1, 1), which keeps denormals and rounds like two f32 additions.  A
+      // zero sum is then always +0, the IEEE result when init is +0.
+      bool packed = false;
+      if (is_row && R.reducer == HF_REDUCER_ADD && !(R.init == 0.0 && std::signbit(R.init)) && c.V % 2 == 0 &&
+          env_flag("HF_RR_PACKED", true)) {
+        const Node &cv = g.nodes[P.rin];
+        if (cv.op == HF_CONVERT && cv.t.dt == HF_F32 && c.root == P.rin) {
+          const Type &yt = g.nodes[cv.opd[0]].t;
+          packed = yt.dt == HF_BF16 && yt.quant < 0;
+        }
+      }
+      if (is_row) glue << "#define HF_RR_PACKED " << (packed ? 1 : 0) << "\n";
+      if (packed) {
+        const int y = g.nodes[P.rin].opd[0];
+        std::string fy = gen.fn(0, y, c.lane, true);
+        types << "typedef hf_R_" << fy << " hf_regs_t;\n";
+        glue << "__device__ __forceinline__ void hf_rr_eval_fetch(const HfArgs &A, int row, int kv, hf_regs_t &R) {\n"
+             << ix.str() << "  " << fy << "_fetch(A" << call_args(it) << ", R);\n}\n";
+        glue << "__device__ __forceinline__ void hf_rr_eval(const HfArgs &A, int row, int kv, const hf_regs_t &R, "
+                "hf_u32 (&hf_res)[HF_V / 2]) {\n"
+             << ix.str() << "  float hf_y[HF_V];\n  " << fy << "(A" << call_args(it) << ", R, hf_y);\n"
+             << "#pragma unroll\n  for (int k = 0; k < HF_V / 2; ++k) hf_res[k] = hf_pack_bf16x2(hf_y[2 * k], hf_y[2 * k + 1]);\n}\n";
+      } else {
+        std::string f = gen.fn(0, c.root, c.lane);
+        types << "typedef hf_R_" << f << " hf_regs_t;\n";
+        glue_pair(glue, is_row ? "hf_rr_eval" : "hf_cr_eval", is_row ? "int row, int kv" : "int r, int c", "hf_regs_t",
+                  f, ix.str(), call_args(it), "", "", "float (&hf_res)[HF_V]");
+      }
       glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store" : "hf_cr_store") << "(const HfArgs &A, int "
            << outer << ", float acc) {\n";
       if (!kept.empty()) delinearize(glue, it, kept, outer, "hf_t");

@@ -13,53 +13,83 @@
 // within lane groups by cross-lane shuffles.
 //
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
-// (vectors per row), HF_TPR, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
-// hf_rr_eval(A, row, kv, R, x), hf_rr_store(A, row, acc).
+// (vectors per row), HF_TPR, HF_RR_PACKED, hf_regs_t,
+// hf_rr_eval_fetch(A, row, kv, R), hf_rr_eval(A, row, kv, R, x) (HF_V floats,
+// or HF_V/2 packed bf16 pairs), hf_rr_store(A, row, acc).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
+#if HF_RR_PACKED
+  // The evaluated row elements arrive as packed bf16 pairs (a sum of bf16
+  // values converted to f32): one dot-product step adds a pair.
+  constexpr int NX = HF_V / 2;
+  typedef hf_u32 xval_t;
+  auto acc_add = [](float a, hf_u32 x) { return hf_acc_bf16x2(a, x); };
+#else
+  constexpr int NX = HF_V;
+  typedef float xval_t;
+  auto acc_add = [](float a, float x) { return hf_red<HF_OP>(a, x); };
+#endif
 #if HF_TPR == HF_BLOCK
-  __shared__ float part[HF_BLOCK / 64];
+  // Two result slots, alternating between a workgroup's consecutive rows, so
+  // that one barrier per row is enough.
+  __shared__ float part[2][HF_BLOCK / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ITERS = (HF_KV + HF_BLOCK - 1) / HF_BLOCK;
-  for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x) {
-    float acc[HF_V];
+  auto finish = [&](int row, const float (&acc)[NX], int slot) {
+    float s = acc[0];
 #pragma unroll
-    for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
-    if constexpr (HF_KV % HF_BLOCK == 0) {
-      hf_regs_t R[ITERS];
+    for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
+    s = hf_wave_reduce<HF_OP>(s);
+    if (lane == 0) part[slot][wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = part[slot][0];
 #pragma unroll
-      for (int it = 0; it < ITERS; ++it) hf_rr_eval_fetch(A, row, it * HF_BLOCK + (int)threadIdx.x, R[it]);
-      HF_LOADS_ISSUED();
+      for (int w = 1; w < HF_BLOCK / 64; ++w) t = hf_red<HF_OP>(t, part[slot][w]);
+      hf_rr_store(A, row, t);
+    }
+  };
+  if constexpr (HF_KV % HF_BLOCK == 0) {
+    hf_regs_t R[ITERS];
+    auto fetch = [&](int row, hf_regs_t (&Rb)[ITERS]) {
+#pragma unroll
+      for (int it = 0; it < ITERS; ++it) hf_rr_eval_fetch(A, row, it * HF_BLOCK + (int)threadIdx.x, Rb[it]);
+    };
+    auto reduce_row = [&](int row, const hf_regs_t (&Rb)[ITERS], int slot) {
+      float acc[NX];
+#pragma unroll
+      for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
 #pragma unroll
       for (int it = 0; it < ITERS; ++it) {
-        float x[HF_V];
-        hf_rr_eval(A, row, it * HF_BLOCK + (int)threadIdx.x, R[it], x);
+        xval_t x[NX];
+        hf_rr_eval(A, row, it * HF_BLOCK + (int)threadIdx.x, Rb[it], x);
 #pragma unroll
-        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
+        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
       }
-    } else {
+      finish(row, acc, slot);
+    };
+    int slot = 0;
+    for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
+      fetch(row, R);
+      HF_LOADS_ISSUED();
+      reduce_row(row, R, slot);
+    }
+  } else {
+    int slot = 0;
+    for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
+      float acc[NX];
+#pragma unroll
+      for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
       for (int kv = threadIdx.x; kv < HF_KV; kv += HF_BLOCK) {
         hf_regs_t R1;
         hf_rr_eval_fetch(A, row, kv, R1);
-        float x[HF_V];
+        xval_t x[NX];
         hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
-        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
+        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
       }
+      finish(row, acc, slot);
     }
-    float s = acc[0];
-#pragma unroll
-    for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[v]);
-    s = hf_wave_reduce<HF_OP>(s);
-    if (lane == 0) part[wave] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = part[0];
-#pragma unroll
-      for (int w = 1; w < HF_BLOCK / 64; ++w) t = hf_red<HF_OP>(t, part[w]);
-      hf_rr_store(A, row, t);
-    }
-    __syncthreads();
   }
 #else
   constexpr int RPB = HF_BLOCK / HF_TPR;
@@ -67,22 +97,22 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
   const int rloc = threadIdx.x / HF_TPR;
   for (int row0 = blockIdx.x * RPB; row0 < HF_ROWS; row0 += gridDim.x * RPB) {
     const int row = row0 + rloc;
-    float acc[HF_V];
+    float acc[NX];
 #pragma unroll
-    for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
+    for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
     if (row < HF_ROWS) {
       for (int kv = sub; kv < HF_KV; kv += HF_TPR) {
         hf_regs_t R1;
         hf_rr_eval_fetch(A, row, kv, R1);
-        float x[HF_V];
+        xval_t x[NX];
         hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
-        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
+        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
       }
     }
     float s = acc[0];
 #pragma unroll
-    for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[v]);
+    for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
     s = hf_group_reduce<HF_OP, HF_TPR>(s);
     if (sub == 0 && row < HF_ROWS) hf_rr_store(A, row, s);
   }

@@ -14,17 +14,22 @@
 // the phase before the first use.
 //
 // Provided by the generated code: HF_BLOCK, HF_TU, HF_TW, HF_PITCH, HF_VIN,
-// HF_VOUT, HF_DU, HF_DW, HF_NTU, HF_NTW, hf_tile_t, hf_val_t, hf_ldregs_t,
-// hf_stregs_t, hf_tr_load_fetch / hf_tr_load (staged node at (b, w.., u)),
+// HF_VOUT, HF_DU, HF_DW, HF_NTU, HF_NTW, HF_ORDER (tile order), hf_tile_t,
+// hf_val_t, hf_ldregs_t, hf_stregs_t, hf_tr_load_fetch / hf_tr_load (staged node at (b, w.., u)),
 // hf_tr_eval_fetch / hf_tr_eval (root at (b, w, u..)), hf_tr_store.
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
   __shared__ hf_tile_t tile[HF_TW * HF_PITCH];
-  int bid = blockIdx.x;
-  const int tu = bid % HF_NTU;
-  bid /= HF_NTU;
-  const int tw = bid % HF_NTW;
-  const int b = bid / HF_NTW;
+  const int bid = blockIdx.x;
+  const int b = bid / (HF_NTU * HF_NTW);
+  const int t = bid % (HF_NTU * HF_NTW);
+#if HF_ORDER == 0  // U-tiles fastest
+  const int tu = t % HF_NTU, tw = t / HF_NTU;
+#elif HF_ORDER == 1  // W-tiles fastest
+  const int tw = t % HF_NTW, tu = t / HF_NTW;
+#else  // diagonal: W-tiles fastest, U-tile shifted by the W-tile
+  const int tw = t % HF_NTW, tu = (t / HF_NTW + tw) % HF_NTU;
+#endif
   const int u0 = tu * HF_TU, w0 = tw * HF_TW;
   constexpr int WV = HF_TW / HF_VIN;          // load-phase vectors per tile row
   constexpr int UV = HF_TU / HF_VOUT;         // store-phase vectors per tile row

@@ -396,6 +396,12 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     long long ntu = ceil_div(DU, tu), ntw = ceil_div(DW, tw);
     long long nb = rt.numel() / (DU * DW);
     int pitch = tu + 1;
+    // Tile order.  U-tiles fastest keeps the writes of concurrent workgroups
+    // spread over the output.  When the input rows of a tile lie 8 KiB or
+    // more apart, the reads of U-consecutive tiles share their low address
+    // bits (and so their HBM channels); a diagonal order then spreads both.
+    const long long in_row_bytes = DW * stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt));
+    const long long order = env_ll("HF_TR_ORDER", in_row_bytes >= 8192 ? 2 : 0);
     P.ctx.push_back(ld);
     P.ctx.push_back(st);
     P.block = 256;
@@ -404,7 +410,7 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     P.empty = rt.numel() == 0;
     P.macros = {{"HF_BLOCK", 256}, {"HF_TU", tu}, {"HF_TW", tw}, {"HF_PITCH", pitch},
                 {"HF_VIN", vin}, {"HF_VOUT", vout}, {"HF_DU", DU}, {"HF_DW", DW},
-                {"HF_NTU", ntu}, {"HF_NTW", ntw}};
+                {"HF_NTU", ntu}, {"HF_NTW", ntw}, {"HF_ORDER", order}};
     P.info.vector_elems = vout;
     P.info.elements = rt.numel();
     P.info.rows = DW;
@@ -494,7 +500,7 @@ Plan plan_reduce(const Graph &g) {
     long long kv = K / V;
     int block, tpr;
     if (kv >= 64) {
-      block = (int)std::min<long long>(256, pow2_floor(kv));
+      block = (int)std::min<long long>(env_ll("HF_ROW_BLOCK", 512), pow2_floor(kv));
       tpr = block;
     } else {
       block = 256;
@@ -504,7 +510,7 @@ Plan plan_reduce(const Graph &g) {
     long long target = env_ll("HF_ROW_WGS", 8192);
     P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb), target));
     P.block = block;
-    P.lds_bytes = (block / 64) * 4;
+    P.lds_bytes = tpr == block ? (block / 64) * 8 : 0;
     P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", J},
                 {"HF_KV", kv}, {"HF_TPR", tpr}};
     P.info.vector_elems = V;
