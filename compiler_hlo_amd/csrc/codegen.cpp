@@ -313,7 +313,10 @@ class Gen {
         case HF_NEGATE: v = fresh(b, n); lanes(b, v, "float", "-" + x); break;
         case HF_ABS: v = fresh(b, n); lanes(b, v, "float", "__builtin_fabsf(" + x + ")"); break;
         case HF_LOG: v = fresh(b, n); lanes(b, v, "float", rnd(t.dt, A0("logf"))); break;
-        case HF_TANH: v = fresh(b, n); lanes(b, v, "float", rnd(t.dt, A0("tanhf"))); break;
+        case HF_TANH:
+          v = fresh(b, n);
+          lanes(b, v, "float", t.dt == HF_BF16 ? rnd(t.dt, A0("hf_tanh_for_bf16")) : rnd(t.dt, A0("tanhf")));
+          break;
         case HF_EXP:
           v = fresh(b, n);
           lanes(b, v, "float", t.dt == HF_BF16 ? rnd(t.dt, A0("hf_exp_for_bf16")) : rnd(t.dt, A0("expf")));

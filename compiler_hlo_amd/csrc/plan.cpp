@@ -295,29 +295,35 @@ Plan plan_loop(const Graph &g, Ctx c) {
   const Type &rt = g.nodes[g.root].t;
   long long DL = c.lane >= 0 ? rt.dims[c.lane] : 1;
   int V = 1;
-  if (c.lane >= 0 && !c.general) V = vec_width(DL, std::max(1, 16 / dtype_bytes(rt.dt)));
+  if (c.lane >= 0 && !c.general)
+    V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", 16), 16 / dtype_bytes(rt.dt))));
   c.V = V;
   long long cols_v = DL / V;
   long long rows = DL > 0 ? rt.numel() / DL : 0;
   int block = 256;
   long long tpr, rpb, nch;
-  if (cols_v >= block) {
-    tpr = block;
-    rpb = 1;
-    nch = ceil_div(cols_v, block);
-  } else {
-    tpr = std::max<long long>(1, cols_v);
-    rpb = block / tpr;
-    nch = 1;
-  }
-  // One row step per thread for pure streaming; four when the fusion also
-  // reads small arrays (per-axis parameters, broadcast biases), whose loads
-  // a thread then reuses across rows.
+  // A fusion that also reads small arrays along the columns (per-axis
+  // quantization parameters, a broadcast bias) gives each wave its own rows of
+  // one 64-vector column strip: the waves of a workgroup then read the same
+  // column data, which they share through L1, and each thread keeps its
+  // column data in registers over four rows, whose loads it issues together.
+  // Pure streaming fusions give the whole workgroup one row segment and each
+  // thread one row.
   bool small = false;
   for (auto &pr : c.param_reads)
     if (!is_streaming(g, pr.first)) small = true;
   for (const Quant &q : g.quants)
     if (q.qdim >= 0) small = true;
+  const long long tpr_cap = env_ll("HF_LOOP_TPR", small ? 64 : block);
+  if (cols_v >= tpr_cap) {
+    tpr = tpr_cap;
+    rpb = block / tpr;
+    nch = ceil_div(cols_v, tpr);
+  } else {
+    tpr = std::max<long long>(1, cols_v);
+    rpb = block / tpr;
+    nch = 1;
+  }
   long long per = small ? 4 : 1;
   long long target = env_ll("HF_LOOP_WGS", nch * ceil_div(ceil_div(rows, rpb), per));
   long long ngroups = std::max<long long>(1, std::min(ceil_div(rows, rpb), std::max<long long>(1, target / nch)));
@@ -327,7 +333,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
   P.empty = rt.numel() == 0;
   P.macros = {{"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", rows}, {"HF_COLS_V", cols_v},
               {"HF_TPR", tpr}, {"HF_RPB", rpb}, {"HF_NCH", nch},
-              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", 2)}};
+              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", small ? 4 : 2)}};
   P.info.vector_elems = V;
   P.info.elements = rt.numel();
   P.info.rows = rows;

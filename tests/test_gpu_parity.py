@@ -282,6 +282,16 @@ def test_exp_bf16_exhaustive():
     say("bf16 exp: %d of 65536 inputs 1 ulp off" % int((d > 0).sum()))
 
 
+def test_tanh_bf16_exhaustive():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = W.Spec()
+    p = s.parameter(0, "bf16", [65536])
+    s.unary("tanh", p, "bf16", [65536])
+    got, _ = run_gpu(s.nodes, [allbits])
+    d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), "bf16", 1)
+    say("bf16 tanh: %d of 65536 inputs 1 ulp off" % int((d > 0).sum()))
+
+
 def test_exp_log_f32_sample():
     g = W.rng(43)
     for op, x in (("exponential", g.uniform(-103, 89, 1 << 20).astype(np.float32)),
