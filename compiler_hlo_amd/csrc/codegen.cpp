@@ -80,6 +80,7 @@ struct Body {
   int nmem = 0;
   bool tile = false;
   bool raw_root = false;  // the root's value is returned before its rounding
+  bool rleaf = false;     // the context's leaf is a reduced value passed in (hf_rv)
 };
 
 class Gen {
@@ -105,11 +106,13 @@ class Gen {
     b.raw_root = raw;
     b.lane = lane;
     b.V = c.V;
-    b.tile = c.leaf >= 0;
+    b.tile = c.leaf >= 0 && P_.hero == HF_HERO_TRANSPOSE;
+    b.rleaf = c.leaf >= 0 && P_.hero != HF_HERO_TRANSPOSE;
     std::string v = val(ci, b, node, identity_index(t.rank));
     std::string idx;
     for (int d = 0; d < t.rank; ++d) idx += ", int i" + std::to_string(d);
     std::string tile = b.tile ? ", const " + tile_type() + " *__restrict__ hf_tile, int hf_w0, int hf_u0" : "";
+    if (b.rleaf) tile += ", float hf_rv";
     std::ostringstream f;
     f << "// partition of node " << node << " (" << op_name(g_.nodes[node].op) << "), lanes along "
       << (lane >= 0 ? "i" + std::to_string(lane) : std::string("nothing")) << "\n";
@@ -266,7 +269,11 @@ class Gen {
     const Type &t = nd.t;
     std::string v;
     bool other_partition = n != b.root && c.part[n] >= 0 && c.part_root[c.part[n]] == n;
-    if (n == c.leaf) {
+    if (n == c.leaf && b.rleaf) {
+      // the reduced value of this output element
+      v = fresh(b, n);
+      lanes(b, v, "float", "hf_rv");
+    } else if (n == c.leaf) {
       // staged value from the LDS tile: [w][u] with u along the lane
       v = fresh(b, n);
       const Term &tw = E[P_.lane_in], &tu = E[P_.lane_out];
@@ -289,6 +296,7 @@ class Gen {
       v = fresh(b, n);
       b.os << "  " << rtype(t) << " " << v << "[" << b.V << "];\n  " << f << "(A";
       if (b.tile) b.os << ", hf_tile, hf_w0, hf_u0";
+      if (b.rleaf) b.os << ", hf_rv";
       b.os << args << ", R." << m << ", " << v << ");\n";
     } else {
       std::vector<std::string> a;
@@ -514,6 +522,7 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
     }
     case HF_HERO_ROW_REDUCE: case HF_HERO_COLUMN_REDUCE: {
       const Ctx &c = P.ctx[0];
+      const Node &R = g.nodes[g.reduce];  // the hero; the root may be an epilogue after it
       const Type &it = g.nodes[P.rin].t;
       std::vector<char> red(it.rank, 0);
       for (int64_t d : R.attr) red[d] = 1;
@@ -536,9 +545,21 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         }
         if (outoff.empty()) outoff = "0";
       }
-      std::string fin = rnd(rt.dt, "hf_red<HF_OP>(" + flit(round_to_dtype(R.init, rt.dt)) + ", acc)");
-      std::string store = rt.dt == HF_F32 ? "  A.out[" + outoff + "] = v;\n"
-                                          : "  { float s1[1] = {v}; " + store_call(rt.dt, 1, outoff, "s1") + " }\n";
+      const hf_dtype odt = R.t.dt;
+      std::string fin = rnd(odt, "hf_red<HF_OP>(" + flit(round_to_dtype(R.init, odt)) + ", acc)");
+      std::string store;
+      if (g.reduce != g.root) {
+        // epilogue at the output index (root dim r is the input's kept dim kept_inc[r])
+        std::string fe = gen.fn(1, g.root, -1);
+        std::string args;
+        for (int r = 0; r < rt.rank; ++r) args += ", i" + std::to_string(kept_inc[r]);
+        store = "  hf_R_" + fe + " Re;\n  " + fe + "_fetch(A" + args + ", Re);\n  hf_val_t s1[1];\n  " + fe + "(A, v" +
+                args + ", Re, s1);\n  " + store_call(rt.dt, 1, outoff, "s1") + "\n";
+      } else if (rt.dt == HF_F32) {
+        store = "  A.out[" + outoff + "] = v;\n";
+      } else {
+        store = "  { float s1[1] = {v}; " + store_call(rt.dt, 1, outoff, "s1") + " }\n";
+      }
       bool is_row = P.hero == HF_HERO_ROW_REDUCE;
       std::ostringstream ix;
       const char *outer = is_row ? "row" : "c";

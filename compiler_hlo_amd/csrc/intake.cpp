@@ -339,8 +339,31 @@ Graph intake(const hf_fusion_desc *desc) {
   for (int i = 0; i < (int)g.nodes.size(); ++i) {
     if (!g.nodes[i].live) continue;
     for (int o : g.nodes[i].opd) g.nodes[o].users.push_back(i);
-    if (g.nodes[i].op == HF_REDUCE && i != g.root)
-      fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (reduce): a reduce must be the fusion root");
+    if (g.nodes[i].op == HF_REDUCE) {
+      if (g.reduce >= 0)
+        fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (reduce): a fusion holds at most one reduce (its hero)");
+      g.reduce = i;
+    }
+  }
+  // Everything that depends on the reduce is its epilogue, evaluated once per
+  // reduce output: elementwise ops on the reduce's output space only.
+  if (g.reduce >= 0 && g.reduce != g.root) {
+    std::vector<char> dep(g.nodes.size(), 0);
+    for (int i = 0; i < (int)g.nodes.size(); ++i) {
+      if (!g.nodes[i].live) continue;
+      dep[i] = i == g.reduce;
+      for (int o : g.nodes[i].opd) dep[i] |= dep[o];
+      if (!dep[i] || i == g.reduce) continue;
+      switch (g.nodes[i].op) {
+        case HF_ADD: case HF_SUBTRACT: case HF_MULTIPLY: case HF_DIVIDE: case HF_MAXIMUM: case HF_MINIMUM:
+        case HF_LOG: case HF_EXP: case HF_TANH: case HF_NEGATE: case HF_ABS: case HF_CONVERT:
+        case HF_UNIFORM_DEQUANTIZE: case HF_UNIFORM_QUANTIZE:
+          break;
+        default:
+          fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (" + op_name(g.nodes[i].op) +
+                                       "): only elementwise ops may follow the reduce");
+      }
+    }
   }
   return g;
 }

@@ -68,6 +68,7 @@ struct Graph {
   std::vector<Node> nodes;
   std::vector<Quant> quants;
   int root = -1;
+  int reduce = -1;              // the reduce node (the hero), if any
   int n_params = 0;
   std::vector<int> param_node;  // parameter number -> node (-1 if unused)
 };

@@ -431,7 +431,7 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
 }
 
 Plan plan_reduce(const Graph &g) {
-  const Node &R = g.nodes[g.root];
+  const Node &R = g.nodes[g.reduce];
   int rin = R.opd[0];
   const Type &it = g.nodes[rin].t;
   Ctx c = make_ctx(g, rin, -1);
@@ -481,7 +481,7 @@ Plan plan_reduce(const Graph &g) {
     else if (minor_kept) row = false;
     else
       fail(HF_ERR_UNSUPPORTED,
-           "node " + std::to_string(g.root) +
+           "node " + std::to_string(g.reduce) +
                " (reduce): reduced dimensions are neither the physically minor nor the physically major ones");
   }
   long long K = 1, J = 1;
@@ -554,6 +554,9 @@ Plan plan_reduce(const Graph &g) {
     P.info.tile_cols = (int)cb;
   }
   P.ctx.push_back(c);
+  // The epilogue: what follows the reduce, evaluated once per output element
+  // with the reduced value as its leaf.
+  if (g.reduce != g.root) P.ctx.push_back(make_ctx(g, g.root, -1, g.reduce));
   P.info.elements = it.numel();
   common_info(g, P);
   return P;
@@ -564,7 +567,7 @@ Plan plan_reduce(const Graph &g) {
 bool is_streaming(const Graph &g, int p) {
   long long n = g.nodes[p].t.numel();
   long long out = g.nodes[g.root].t.numel();
-  if (g.nodes[g.root].op == HF_REDUCE) out = g.nodes[g.nodes[g.root].opd[0]].t.numel();
+  if (g.reduce >= 0) out = g.nodes[g.nodes[g.reduce].opd[0]].t.numel();
   return n >= 1024 && n * 4 >= out;
 }
 
@@ -585,7 +588,7 @@ const char *hero_template_name(hf_hero h) {
 // patterns); everything else is the loop emitter.
 Plan make_plan(const Graph &g) {
   const Node &R = g.nodes[g.root];
-  if (R.op == HF_REDUCE) return plan_reduce(g);
+  if (g.reduce >= 0) return plan_reduce(g);
   Ctx loop = make_ctx(g, g.root, phys_minor(R.t));
   if (!env_ll("HF_NO_TRANSPOSE_HERO", 0)) {
     Plan P;

@@ -111,6 +111,19 @@ def test_transpose_exp_small(n0, n1):
     assert_ulp(got, want, "f32", 2)
 
 
+@pytest.mark.parametrize("dims", [(20, 160, 170), (3, 7, 67)])
+def test_transpose3d_with_epilogue(dims):
+    """The transpose emitter's 3-D example: abs(transpose(exp(x), {2,1,0}));
+    abs runs on the values read back from the tile."""
+    say("transpose3d exp abs", dims)
+    spec, params, _ = W.transpose3d_exp_abs(*dims, seed=30 + dims[0])
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "transpose"
+    want = oracle.evaluate(spec.nodes, params)
+    assert_ulp(got, want, "f32", 2)
+    assert not np.signbit(np.asarray(got, np.float32)).any()
+
+
 def test_transpose_exp_full_and_loop_invariant():
     spec, params, _ = W.transpose_exp_f32()
     say("transpose exp full")
@@ -218,6 +231,63 @@ def test_reductions_exact_on_integers():
         got, f = run_gpu(s.nodes, [x])
         say("exact sum", dims, red, m2m, f.plan()["hero"])
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
+# --------------------------------------------------------------------------
+# elementwise epilogues after a reduce
+# --------------------------------------------------------------------------
+def test_reduce_epilogue_mean():
+    """mean = reduce-sum / N: the division runs once per output, after the
+    reduce (an elementwise epilogue)."""
+    rows, n = 96, 3000
+    g = W.rng(41)
+    x = W.normal_f32(g, rows * n)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [rows, n])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [rows])
+    c = s.constant(float(n), "f32", [rows])
+    s.binary("divide", r, c, "f32", [rows])
+    got, f = run_gpu(s.nodes, [x])
+    assert f.plan()["hero"] == "row_reduce"
+    want = np.asarray(oracle.evaluate(s.nodes, [x]), np.float64)
+    bound = 1e-5 * np.abs(x.reshape(rows, n)).astype(np.float64).sum(1) / n + np.spacing(np.abs(want).astype(np.float32))
+    assert (np.abs(np.asarray(got, np.float64) - want) <= bound).all()
+
+
+def test_reduce_epilogue_exact_cases():
+    """Epilogues whose results are unique: a column max through the segment
+    fold, then negate and convert to bf16; a max plus a per-output bias; an
+    integer-valued sum then per-tensor quantize."""
+    g = W.rng(42)
+    # column max (segments + fold kernel), negate, convert to bf16
+    r_, c_ = 4096, 96
+    x = W.uniform_f32(g, r_ * c_, -100.0, 100.0)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [r_, c_])
+    m = s.reduce(p, [0], "max", float("-inf"), "f32", [c_])
+    ng = s.unary("negate", m, "f32", [c_])
+    s.convert(ng, "bf16", [c_])
+    got, f = run_gpu(s.nodes, [x])
+    assert f.plan()["hero"] == "column_reduce" and f.plan()["workspace_bytes"] > 0
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "bf16")
+    # row max plus a bias parameter of the output's shape
+    x = W.uniform_f32(g, 300 * 700, -100.0, 100.0)
+    bias = W.normal_f32(g, 300)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [300, 700])
+    b = s.parameter(1, "f32", [300])
+    m = s.reduce(p, [1], "max", float("-inf"), "f32", [300])
+    s.binary("add", m, b, "f32", [300])
+    got, _ = run_gpu(s.nodes, [x, bias])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x, bias]), "f32")
+    # integer-valued sum (exact in any order), then quantize to i8
+    x = W.integers(g, 200 * 1000, -4, 4, np.int64).astype(np.float32)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [200, 1000])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [200])
+    s.op("uniform_quantize", [r], "s8", [200], quant=W.quant_type("s8", [0.5], [3]))
+    got, _ = run_gpu(s.nodes, [x])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s8")
 
 
 # --------------------------------------------------------------------------

@@ -139,12 +139,34 @@ def test_validation_errors():
 
 
 def test_unsupported_is_distinguished():
+    # only elementwise ops may follow the reduce hero
     s = W.Spec()
     p = s.parameter(0, "f32", [4, 5])
     r = s.reduce(p, [1], "add", 0.0, "f32", [4])
-    s.unary("log", r, "f32", [4])
+    s.broadcast_in_dim(r, [0], "f32", [4, 3])
     st, msg = _status(s.nodes)
-    assert st == "HF_ERR_UNSUPPORTED" and "root" in msg
+    assert st == "HF_ERR_UNSUPPORTED" and "only elementwise ops may follow the reduce" in msg
+    # one reduce per fusion
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4, 5])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [4])
+    r2 = s.reduce(p, [1], "max", float("-inf"), "f32", [4])
+    s.binary("add", r, r2, "f32", [4])
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "at most one reduce" in msg
+
+
+def test_reduce_epilogue_is_planned_as_a_second_context():
+    s = W.Spec()
+    p = s.parameter(0, "f32", [64, 300])
+    b = s.parameter(1, "f32", [64])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [64])
+    e = s.unary("exponential", r, "f32", [64])
+    s.binary("add", e, b, "f32", [64])
+    pl = plan_of(s)
+    assert pl["hero"] == "row_reduce"
+    assert pl["n_partitions"] == 1  # the epilogue (exp, add); the reduce input is a bare parameter
+    assert pl["algorithmic_bytes"] == 4 * 64 * 300 + 4 * 64 + 4 * 64
 
 
 # --------------------------------------------------------------------------
@@ -182,9 +204,12 @@ def test_hero_classification():
         (W.column_reduce_max_f32(256, 64, m2m=(0, 1)), "row_reduce"),
         (W.quant_dequant_bias_requant(16, 64), "loop"),
         (W.gelu_bf16(2, 4, 64), "loop"),
+        (W.transpose3d_exp_abs(), "transpose"),
     ]
     for (spec, _, meta), hero in cases:
         assert plan_of(spec)["hero"] == hero, meta["name"]
+    # the pages' 3-D example: exp is read into the tile, abs runs after it
+    assert plan_of(W.transpose3d_exp_abs()[0])["n_partitions"] == 2
     # a transpose that is the identity in memory is a plain loop
     s = W.Spec()
     x = s.parameter(0, "f32", [64, 32], [0, 1])

@@ -215,6 +215,20 @@ def quant_dequant_bias_requant(r=4096, c=4096, seed=6, out_scale=0.02, out_zp=0)
                           "bytes": 2 * r * c + 4 * c + 4 * c + 4 * c}
 
 
+def transpose3d_exp_abs(d0=20, d1=160, d2=170, seed=8):
+    """out = abs(transpose(exp(x), {2,1,0})), x f32[d0,d1,d2] ~ N(0,1): the
+    transpose emitter's example on XLA:GPU Emitters ("Transpose emitter"),
+    with an elementwise op after the transpose."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [d0, d1, d2])
+    e = s.unary("exponential", x, "f32", [d0, d1, d2])
+    t = s.transpose(e, [2, 1, 0], "f32", [d2, d1, d0])
+    s.unary("abs", t, "f32", [d2, d1, d0])
+    n = d0 * d1 * d2
+    return s, [normal_f32(g, n)], {"name": "transpose3d_exp_abs", "elements": n, "bytes": 8 * n}
+
+
 def gelu_bf16(d0=6, d1=512, d2=4096, seed=7):
     """The GELU loop fusion in bf16 (tanh form), every op rounding to bf16."""
     g = rng(seed)
