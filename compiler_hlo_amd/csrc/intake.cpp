@@ -168,6 +168,63 @@ void need_operands(const hf_node &n, int k, const Ctx &c) {
 
 }  // namespace
 
+// Rewrites each elementwise op on quantized values into dequantize, the op
+// on f32 values, and quantize to the op's result type
+// (dequantize_op_quantize), so that the rest of the library sees only float
+// arithmetic between uniform_dequantize and uniform_quantize.
+void expand_quantized_ops(Graph &g) {
+  auto elementwise = [](hf_op op) {
+    switch (op) {
+      case HF_ADD: case HF_SUBTRACT: case HF_MULTIPLY: case HF_DIVIDE: case HF_MAXIMUM: case HF_MINIMUM:
+      case HF_LOG: case HF_EXP: case HF_TANH: case HF_NEGATE: case HF_ABS:
+        return true;
+      default:
+        return false;
+    }
+  };
+  bool any = false;
+  for (const Node &nd : g.nodes) any |= elementwise(nd.op) && nd.t.quant >= 0;
+  if (!any) return;
+  auto f32_of = [](const Type &q) {
+    Type t = q;
+    t.dt = HF_F32;
+    t.quant = -1;
+    for (int d = 0; d < t.rank; ++d) t.m2m[d] = t.rank - 1 - d;
+    return t;
+  };
+  std::vector<Node> out;
+  std::vector<int> map(g.nodes.size(), -1);
+  for (size_t i = 0; i < g.nodes.size(); ++i) {
+    Node nd = g.nodes[i];
+    for (int &o : nd.opd) o = map[o];
+    if (elementwise(nd.op) && nd.t.quant >= 0) {
+      for (int &o : nd.opd) {
+        Node d;
+        d.op = HF_UNIFORM_DEQUANTIZE;
+        d.opd = {o};
+        d.t = f32_of(out[o].t);
+        out.push_back(d);
+        o = (int)out.size() - 1;
+      }
+      const Type qt = nd.t;
+      nd.t = f32_of(qt);
+      out.push_back(nd);
+      Node q;
+      q.op = HF_UNIFORM_QUANTIZE;
+      q.opd = {(int)out.size() - 1};
+      q.t = qt;
+      out.push_back(q);
+    } else {
+      out.push_back(nd);
+    }
+    map[i] = (int)out.size() - 1;
+  }
+  for (int &p : g.param_node)
+    if (p >= 0) p = map[p];
+  g.root = map[g.root];
+  g.nodes = std::move(out);
+}
+
 Graph intake(const hf_fusion_desc *desc) {
   if (!desc) fail(HF_ERR_INVALID, "descriptor is NULL");
   if (desc->abi_version != HF_ABI_VERSION) fail(HF_ERR_INVALID, "abi_version mismatch");
@@ -206,6 +263,22 @@ Graph intake(const hf_fusion_desc *desc) {
     const Type &t = n.t;
     auto opt = [&](int k) -> const Type & { return g.nodes[n.opd[k]].t; };
     bool quantized = t.quant >= 0;
+    // An elementwise op on quantized values (StableHLO Specification: each
+    // op's semantics for quantized types, dequantize_op_quantize): operands
+    // and result per-tensor quantized with one baseline type (storage type
+    // and range; the scales and zero points may differ).
+    auto check_quantized = [&]() {
+      for (size_t k = 0; k < n.opd.size(); ++k)
+        if (opt((int)k).quant < 0 || !quantized)
+          c.invalid("baseline types differ (C1): quantized and non-quantized element types mixed");
+      for (size_t k = 0; k <= n.opd.size(); ++k) {
+        const Quant &q = g.quants[k < n.opd.size() ? opt((int)k).quant : t.quant];
+        const Quant &r = g.quants[t.quant];
+        if (q.qdim >= 0) c.invalid("operands and result must be per-tensor quantized tensors (I1)");
+        if (q.smin != r.smin || q.smax != r.smax || q.storage != r.storage)
+          c.invalid("baseline types differ (C1): storage types or ranges differ");
+      }
+    };
 
     switch (src.op) {
       case HF_PARAMETER:
@@ -223,8 +296,8 @@ Graph intake(const hf_fusion_desc *desc) {
         if (!t.same_shape(opt(0)) || t.dt != opt(0).dt)
           c.invalid("baseline_type(operand) = baseline_type(result) violated (C1): " +
                     dims_str(opt(0)) + " vs " + dims_str(t));
-        if (!is_float(t.dt) || quantized || opt(0).quant >= 0)
-          c.unsupported("only non-quantized floating-point element types are supported");
+        if (quantized || opt(0).quant >= 0) check_quantized();
+        else if (!is_float(t.dt)) c.unsupported("only floating-point element types are supported");
         break;
       case HF_ADD: case HF_SUBTRACT: case HF_MULTIPLY: case HF_DIVIDE:
       case HF_MAXIMUM: case HF_MINIMUM:
@@ -232,8 +305,8 @@ Graph intake(const hf_fusion_desc *desc) {
         if (!t.same_shape(opt(0)) || !t.same_shape(opt(1)) || t.dt != opt(0).dt || t.dt != opt(1).dt)
           c.invalid("baseline_type(lhs) = baseline_type(rhs) = baseline_type(result) violated (C1): " +
                     dims_str(opt(0)) + ", " + dims_str(opt(1)) + " -> " + dims_str(t));
-        if (!is_float(t.dt) || quantized || opt(0).quant >= 0 || opt(1).quant >= 0)
-          c.unsupported("only non-quantized floating-point element types are supported");
+        if (quantized || opt(0).quant >= 0 || opt(1).quant >= 0) check_quantized();
+        else if (!is_float(t.dt)) c.unsupported("only floating-point element types are supported");
         break;
       case HF_CONVERT:
         need_operands(src, 1, c);
@@ -323,6 +396,8 @@ Graph intake(const hf_fusion_desc *desc) {
       }
     }
   }
+
+  expand_quantized_ops(g);
 
   // reachability from the root and user lists
   std::vector<int> stack{g.root};

@@ -324,28 +324,42 @@ static int eval(const graph *g, int n, const int64_t *idx, long double *out, aux
       *out = round_to(t->dtype, (long double)nd->constant);
       return 0;
     case OR_LOG: case OR_EXP: case OR_TANH: case OR_NEGATE: case OR_ABS:
-      if ((rc = eval(g, nd->operands[0], idx, &a, NULL))) return rc;
-      switch (nd->op) {
-        case OR_LOG: *out = round_to(t->dtype, logl(a)); break;
-        case OR_EXP: *out = round_to(t->dtype, expl(a)); break;
-        case OR_TANH: *out = round_to(t->dtype, tanhl(a)); break;
-        case OR_NEGATE: *out = -a; break;
-        default: *out = fabsl(a); break;
-      }
-      return 0;
     case OR_ADD: case OR_SUBTRACT: case OR_MULTIPLY: case OR_DIVIDE:
-    case OR_MAXIMUM: case OR_MINIMUM:
+    case OR_MAXIMUM: case OR_MINIMUM: {
+      /* A quantized op (StableHLO Specification, each op's semantics for
+       * quantized types: dequantize_op_quantize): its quantized operands are
+       * dequantized, the op runs on the expressed (f32) values, and the f32
+       * result is quantized to the result type. */
+      const int dt = t->quantized ? OR_F32 : t->dtype;
+      const int binary = nd->op != OR_LOG && nd->op != OR_EXP && nd->op != OR_TANH &&
+                         nd->op != OR_NEGATE && nd->op != OR_ABS;
+      long double r;
       if ((rc = eval(g, nd->operands[0], idx, &a, NULL))) return rc;
-      if ((rc = eval(g, nd->operands[1], idx, &b, NULL))) return rc;
-      switch (nd->op) {
-        case OR_ADD: *out = round_to(t->dtype, a + b); break;
-        case OR_SUBTRACT: *out = round_to(t->dtype, a - b); break;
-        case OR_MULTIPLY: *out = round_to(t->dtype, a * b); break;
-        case OR_DIVIDE: *out = round_to(t->dtype, a / b); break;
-        case OR_MAXIMUM: *out = ieee_maximum(a, b); break;
-        default: *out = ieee_minimum(a, b); break;
+      if (g->nodes[nd->operands[0]].type.quantized) a = dequantize(&g->nodes[nd->operands[0]].type, a, idx, OR_F32);
+      if (binary) {
+        if ((rc = eval(g, nd->operands[1], idx, &b, NULL))) return rc;
+        if (g->nodes[nd->operands[1]].type.quantized) b = dequantize(&g->nodes[nd->operands[1]].type, b, idx, OR_F32);
       }
+      switch (nd->op) {
+        case OR_LOG: r = round_to(dt, logl(a)); break;
+        case OR_EXP: r = round_to(dt, expl(a)); break;
+        case OR_TANH: r = round_to(dt, tanhl(a)); break;
+        case OR_NEGATE: r = -a; break;
+        case OR_ABS: r = fabsl(a); break;
+        case OR_ADD: r = round_to(dt, a + b); break;
+        case OR_SUBTRACT: r = round_to(dt, a - b); break;
+        case OR_MULTIPLY: r = round_to(dt, a * b); break;
+        case OR_DIVIDE: r = round_to(dt, a / b); break;
+        case OR_MAXIMUM: r = ieee_maximum(a, b); break;
+        default: r = ieee_minimum(a, b); break;
+      }
+      if (!t->quantized) {
+        *out = r;
+        return 0;
+      }
+      if (quantize(t, r, idx, out)) { set_err("quantize of a non-finite value", n); return -3; }
       return 0;
+    }
     case OR_CONVERT: {
       if ((rc = eval(g, nd->operands[0], idx, &a, NULL))) return rc;
       if (is_float_type(t->dtype)) *out = round_to(t->dtype, a); /* int->float RNE; float->float RNE */

@@ -233,6 +233,57 @@ def test_reductions_exact_on_integers():
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
 
 
+def test_quantized_elementwise_ops():
+    """Elementwise ops on per-tensor quantized i8 tensors: dequantize, the op
+    on f32 values, quantize to the result type.  The arithmetic ops round
+    once in f32 on both sides: bit-exact."""
+    g = W.rng(61)
+    n0, n1 = 96, 1000
+    a = W.integers(g, n0 * n1, -128, 127, np.int8)
+    b = W.integers(g, n0 * n1, -128, 127, np.int8)
+    qa, qb = W.quant_type("s8", [0.05], [3]), W.quant_type("s8", [0.02], [-7])
+    qo = W.quant_type("s8", [0.04], [1])
+    for op in ("add", "subtract", "multiply", "maximum", "minimum"):
+        s = W.Spec()
+        pa = s.parameter(0, "s8", [n0, n1], quant=qa)
+        pb = s.parameter(1, "s8", [n0, n1], quant=qb)
+        s.op(op, [pa, pb], "s8", [n0, n1], quant=qo)
+        got, _ = run_gpu(s.nodes, [a, b])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [a, b]), "s8")
+    for op in ("negate", "abs"):
+        s = W.Spec()
+        pa = s.parameter(0, "s8", [n0, n1], quant=qa)
+        s.op(op, [pa], "s8", [n0, n1], quant=qo)
+        got, _ = run_gpu(s.nodes, [a])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [a]), "s8")
+    # a chain: quantized add, then a quantized maximum with a third tensor
+    c = W.integers(g, n0 * n1, -128, 127, np.int8)
+    s = W.Spec()
+    pa = s.parameter(0, "s8", [n0, n1], quant=qa)
+    pb = s.parameter(1, "s8", [n0, n1], quant=qb)
+    pc = s.parameter(2, "s8", [n0, n1], quant=qo)
+    ad = s.op("add", [pa, pb], "s8", [n0, n1], quant=qo)
+    s.op("maximum", [ad, pc], "s8", [n0, n1], quant=qa)
+    got, _ = run_gpu(s.nodes, [a, b, c])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [a, b, c]), "s8")
+
+
+def test_quantized_exp_within_one_step():
+    """exp on quantized values: the f32 exp of the device may differ from the
+    correctly rounded one by an ulp, which can move a quotient across a
+    rounding boundary: results within one storage step, and such steps rare."""
+    g = W.rng(62)
+    a = W.integers(g, 200000, -128, 127, np.int8)
+    qa, qo = W.quant_type("s8", [0.02], [0]), W.quant_type("s8", [0.05], [-100])
+    s = W.Spec()
+    pa = s.parameter(0, "s8", [200000], quant=qa)
+    s.op("exponential", [pa], "s8", [200000], quant=qo)
+    got, _ = run_gpu(s.nodes, [a])
+    want = oracle.evaluate(s.nodes, [a])
+    d = np.abs(got.astype(np.int64) - want.astype(np.int64))
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
 # --------------------------------------------------------------------------
 # elementwise epilogues after a reduce
 # --------------------------------------------------------------------------

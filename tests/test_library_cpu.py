@@ -156,6 +156,36 @@ def test_unsupported_is_distinguished():
     assert st == "HF_ERR_UNSUPPORTED" and "at most one reduce" in msg
 
 
+def test_quantized_elementwise_validation_and_expansion():
+    qa, qb = W.quant_type("s8", [0.5], [1]), W.quant_type("s8", [0.25], [0])
+    # per-tensor quantized add: dequantize both, add in f32, quantize
+    s = W.Spec()
+    a = s.parameter(0, "s8", [16, 64], quant=qa)
+    b = s.parameter(1, "s8", [16, 64], quant=qb)
+    s.op("add", [a, b], "s8", [16, 64], quant=W.quant_type("s8", [0.3], [-2]))
+    assert _status(s.nodes) == ("HF_OK", "")
+    assert plan_of(s)["hero"] == "loop"
+    # quantized and non-quantized operands mixed
+    s = W.Spec()
+    a = s.parameter(0, "s8", [16], quant=qa)
+    b = s.parameter(1, "f32", [16])
+    s.op("add", [a, b], "s8", [16], quant=qa)
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "baseline" in msg
+    # per-axis operands are not allowed for the elementwise ops
+    s = W.Spec()
+    a = s.parameter(0, "s8", [2, 3], quant=W.quant_type("s8", [0.1, 0.2, 0.3], [0, 0, 0], qdim=1))
+    s.op("negate", [a], "s8", [2, 3], quant=W.quant_type("s8", [0.1, 0.2, 0.3], [0, 0, 0], qdim=1))
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "per-tensor" in msg
+    # storage ranges differ
+    s = W.Spec()
+    a = s.parameter(0, "s8", [16], quant=qa)
+    s.op("abs", [a], "s8", [16], quant=W.quant_type("s8", [0.5], [1], storage_min=-100, storage_max=100))
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "storage" in msg
+
+
 def test_reduce_epilogue_is_planned_as_a_second_context():
     s = W.Spec()
     p = s.parameter(0, "f32", [64, 300])

@@ -568,6 +568,57 @@ def test_requantize_direct():
 
 
 # --------------------------------------------------------------------------
+# Elementwise ops on quantized tensors (StableHLO Specification, each op's
+# semantics for quantized types: dequantize, op, quantize)
+# --------------------------------------------------------------------------
+def _qop(op, qts, xs, qout):
+    s = Spec()
+    ps = [s.parameter(k, "s8", [len(xs[0])], quant=qt) for k, qt in enumerate(qts)]
+    s.op(op, ps, "s8", [len(xs[0])], quant=qout)
+    return ev(s, xs).astype(np.int64)
+
+
+def test_quantized_add_with_a_shared_power_of_two_scale_is_integer_addition():
+    """scale 2^-2, zero point 0 everywhere: the reals are exact, their sum is
+    exact, and dividing by the scale gives back q1 + q2 (clamped)."""
+    qt = quant_type("s8", [0.25], [0])
+    g = rng(51)
+    a = g.integers(-128, 128, 4000).astype(np.int8)
+    b = g.integers(-128, 128, 4000).astype(np.int8)
+    got = _qop("add", [qt, qt], [a, b], qt)
+    assert np.array_equal(got, np.clip(a.astype(np.int64) + b, -128, 127))
+
+
+def test_quantized_maximum_minimum_with_one_type_are_storage_max_min():
+    """dequantize is increasing and quantize(dequantize(q)) = q for one type
+    (pinned by the per-axis requantize-identity test), so max/min of the
+    reals come back as max/min of the storage values."""
+    qt = quant_type("s8", [0.1], [5])
+    a = np.arange(-128, 128, dtype=np.int8).repeat(256)
+    b = np.tile(np.arange(-128, 128, dtype=np.int8), 256)
+    assert np.array_equal(_qop("maximum", [qt, qt], [a, b], qt), np.maximum(a, b).astype(np.int64))
+    assert np.array_equal(_qop("minimum", [qt, qt], [a, b], qt), np.minimum(a, b).astype(np.int64))
+
+
+def test_quantized_negate_abs_with_zero_point_zero():
+    qt = quant_type("s8", [0.3], [0])
+    x = np.arange(-128, 128, dtype=np.int8)
+    assert np.array_equal(_qop("negate", [qt], [x], qt), np.clip(-x.astype(np.int64), -128, 127))
+    assert np.array_equal(_qop("abs", [qt], [x], qt), np.clip(np.abs(x.astype(np.int64)), -128, 127))
+
+
+def test_quantized_add_worked_values_and_ties():
+    """Different scales: 3*0.5 + 2*0.25 = 2.0 -> 2.0/0.5 + 1 = 5; and a sum
+    that lands on a half-integer multiple of the result scale rounds to even:
+    (1.5 + 1.0)/1.0 = 2.5 -> 2, (0.5 + 1.0)/1.0 = 1.5 -> 2."""
+    a_t, b_t = quant_type("s8", [0.5], [0]), quant_type("s8", [0.25], [0])
+    got = _qop("add", [a_t, b_t], [np.array([3], np.int8), np.array([2], np.int8)], quant_type("s8", [0.5], [1]))
+    assert got.tolist() == [5]
+    got = _qop("add", [a_t, a_t], [np.array([3, 1], np.int8), np.array([2, 2], np.int8)], quant_type("s8", [1.0], [0]))
+    assert got.tolist() == [2, 2]
+
+
+# --------------------------------------------------------------------------
 # The pages' example program (StableHLO Specification, "Programs")
 # --------------------------------------------------------------------------
 def test_program_28x28_selection_weights():
