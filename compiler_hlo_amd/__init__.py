@@ -31,7 +31,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhlofusion.so")
 
+ABI_VERSION = 2
 MAX_RANK = 8
+MAX_OPERANDS = 8
+MAX_ATTR = 3 * MAX_RANK
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "u8": 4, "s32": 5}
 DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "s8": 1, "u8": 1, "s32": 4}
 OPS = {
@@ -39,7 +42,8 @@ OPS = {
     "divide": 5, "maximum": 6, "minimum": 7, "log": 8, "exponential": 9,
     "tanh": 10, "negate": 11, "abs": 12, "convert": 13, "broadcast_in_dim": 14,
     "reshape": 15, "transpose": 16, "uniform_dequantize": 17,
-    "uniform_quantize": 18, "reduce": 19,
+    "uniform_quantize": 18, "reduce": 19, "reverse": 20, "iota": 21, "pad": 22,
+    "concatenate": 23,
 }
 REDUCERS = {"add": 0, "max": 1, "min": 2}
 HEROES = {0: "loop", 1: "transpose", 2: "row_reduce", 3: "column_reduce"}
@@ -66,9 +70,9 @@ class HfType(ctypes.Structure):
 
 class HfNode(ctypes.Structure):
     _fields_ = [("op", ctypes.c_int32), ("n_operands", ctypes.c_int32),
-                ("operands", ctypes.c_int32 * 2), ("type", HfType),
+                ("operands", ctypes.c_int32 * MAX_OPERANDS), ("type", HfType),
                 ("parameter_number", ctypes.c_int32), ("constant", ctypes.c_double),
-                ("n_attr", ctypes.c_int32), ("attr", ctypes.c_int64 * MAX_RANK),
+                ("n_attr", ctypes.c_int32), ("attr", ctypes.c_int64 * MAX_ATTR),
                 ("reducer", ctypes.c_int32), ("init_value", ctypes.c_double)]
 
 
@@ -85,6 +89,17 @@ class HfPlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("algorithmic_bytes", ctypes.c_int64),
                 ("elements", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32)]
+
+
+def node_attr(nd: dict) -> list:
+    """The attribute list of a node dict, in the order hf_node.attr holds it."""
+    if nd["op"] == "pad":
+        return list(nd["edge_padding_low"]) + list(nd["edge_padding_high"]) + list(nd["interior_padding"])
+    if nd["op"] == "iota":
+        return [int(nd["iota_dimension"])]
+    if nd["op"] == "concatenate":
+        return [int(nd["dimension"])]
+    return list(nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", []))))
 
 
 EXPORTS = ["hf_fusion_create", "hf_fusion_plan", "hf_fusion_source", "hf_fusion_launch",
@@ -162,7 +177,7 @@ class Fusion:
         arr = (HfNode * len(nodes))()
         for i, nd in enumerate(nodes):
             self._fill(arr[i], nd)
-        desc = HfFusionDesc(1, len(nodes), arr, self.root, n_params)
+        desc = HfFusionDesc(ABI_VERSION, len(nodes), arr, self.root, n_params)
         self._arr = arr
         flags = {"load": 0, "compile": COMPILE_ONLY, "plan": PLAN_ONLY}[mode]
         h = ctypes.c_void_p()
@@ -209,7 +224,7 @@ class Fusion:
             c.type.quant = ctypes.pointer(hq)
         c.parameter_number = nd.get("param", -1)
         c.constant = float(nd.get("value", 0.0))
-        attr = nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", [])))
+        attr = node_attr(nd)
         c.n_attr = len(attr)
         for k, a in enumerate(attr):
             c.attr[k] = a

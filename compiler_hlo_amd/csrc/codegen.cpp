@@ -300,18 +300,54 @@ class Gen {
       b.os << args << ", R." << m << ", " << v << ");\n";
     } else {
       std::vector<std::string> a;
-      for (int o : nd.opd) {
+      for (size_t k = 0; k < nd.opd.size(); ++k) {
         bool general = false;
-        a.push_back(val(ci, b, o, operand_index(g_, n, E, &general)));
+        a.push_back(val(ci, b, nd.opd[k], operand_index(g_, n, (int)k, E, &general)));
       }
       auto A0 = [&](const char *f) { return std::string(f) + "(" + a[0] + "[l])"; };
       auto rnd = [&](hf_dtype dt, const std::string &e) { return b.raw_root && n == b.root ? e : hf::rnd(dt, e); };
       const std::string x = a.empty() ? "" : a[0] + "[l]";
       const std::string y = a.size() > 1 ? a[1] + "[l]" : "";
       switch (nd.op) {
-        case HF_TRANSPOSE: case HF_BROADCAST_IN_DIM: case HF_RESHAPE:
+        case HF_TRANSPOSE: case HF_BROADCAST_IN_DIM: case HF_RESHAPE: case HF_REVERSE:
           v = a[0];  // pure index transforms
           break;
+        case HF_IOTA: {  // the index along iota_dimension
+          const Term &tm = E[nd.attr[0]];
+          const std::string i = term_str(tm) + (tm.k == Term::VAR && tm.var == b.lane ? " + l" : "");
+          v = fresh(b, n);
+          if (reg_is_float(t)) lanes(b, v, "float", rnd(t.dt, "(float)(" + i + ")"));
+          else lanes(b, v, "int", i);
+          break;
+        }
+        case HF_PAD: {  // an operand element where the index lands on one, else the padding value
+          const Type &ot = g_.nodes[nd.opd[0]].t;
+          const int r = ot.rank;
+          std::string pred;
+          for (int d = 0; d < r; ++d) {
+            const long long lo = nd.attr[d], hi = nd.attr[r + d], step = nd.attr[2 * r + d] + 1;
+            if (lo == 0 && hi == 0 && step == 1) continue;
+            const std::string k = "(" + term_str(E[d]) + " - (" + std::to_string(lo) + "))";
+            pred += std::string(pred.empty() ? "" : " && ") + "(" + k + " >= 0 && " + k + " % " +
+                    std::to_string(step) + " == 0 && " + k + " / " + std::to_string(step) + " < " +
+                    std::to_string(ot.dims[d]) + ")";
+          }
+          v = fresh(b, n);
+          lanes(b, v, rtype(t), pred.empty() ? x : "(" + pred + ") ? " + x + " : " + y);
+          break;
+        }
+        case HF_CONCATENATE: {  // the input whose range along the dim holds the index
+          const int cd = (int)nd.attr[0];
+          std::vector<long long> end;
+          long long off = 0;
+          for (int o : nd.opd) end.push_back(off += g_.nodes[o].t.dims[cd]);
+          std::string e = a.back() + "[l]";
+          for (int k = (int)a.size() - 2; k >= 0; --k)
+            e = "(" + term_str(E[cd]) + " < " + std::to_string(end[k]) + ") ? " + a[k] + "[l] : (" + e + ")";
+          v = fresh(b, n);
+          lanes(b, v, rtype(t), e);
+          break;
+        }
         case HF_ADD: v = fresh(b, n); lanes(b, v, "float", rnd(t.dt, x + " + " + y)); break;
         case HF_SUBTRACT: v = fresh(b, n); lanes(b, v, "float", rnd(t.dt, x + " - " + y)); break;
         case HF_MULTIPLY: v = fresh(b, n); lanes(b, v, "float", rnd(t.dt, x + " * " + y)); break;

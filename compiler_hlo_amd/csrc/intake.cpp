@@ -60,6 +60,10 @@ const char *op_name(hf_op op) {
     case HF_UNIFORM_DEQUANTIZE: return "uniform_dequantize";
     case HF_UNIFORM_QUANTIZE: return "uniform_quantize";
     case HF_REDUCE: return "reduce";
+    case HF_REVERSE: return "reverse";
+    case HF_IOTA: return "iota";
+    case HF_PAD: return "pad";
+    case HF_CONCATENATE: return "concatenate";
   }
   return "?";
 }
@@ -243,17 +247,18 @@ Graph intake(const hf_fusion_desc *desc) {
   for (int i = 0; i < desc->n_nodes; ++i) {
     const hf_node &src = desc->nodes[i];
     Ctx c{i, src.op};
-    if (src.op < HF_PARAMETER || src.op > HF_REDUCE) fail(HF_ERR_INVALID, "node " + std::to_string(i) + ": unknown op");
+    if (src.op < HF_PARAMETER || src.op > HF_CONCATENATE)
+      fail(HF_ERR_INVALID, "node " + std::to_string(i) + ": unknown op");
     Node &n = g.nodes[i];
     n.op = src.op;
-    if (src.n_operands < 0 || src.n_operands > 2) c.invalid("n_operands out of range");
+    if (src.n_operands < 0 || src.n_operands > HF_MAX_OPERANDS) c.invalid("n_operands out of range");
     for (int k = 0; k < src.n_operands; ++k) {
       int o = src.operands[k];
       if (o < 0 || o >= i) c.invalid("operand must be an earlier node");
       n.opd.push_back(o);
     }
     n.t = take_type(src.type, g, c);
-    if (src.n_attr < 0 || src.n_attr > HF_MAX_RANK) c.invalid("n_attr out of range");
+    if (src.n_attr < 0 || src.n_attr > HF_MAX_ATTR) c.invalid("n_attr out of range");
     for (int k = 0; k < src.n_attr; ++k) n.attr.push_back(src.attr[k]);
     n.param = src.parameter_number;
     n.cst = src.constant;
@@ -357,6 +362,69 @@ Graph intake(const hf_fusion_desc *desc) {
           seen[p] = true;
           if (t.dims[d] != o.dims[p]) c.invalid("dim(result, d) = dim(operand, permutation[d]) violated");
         }
+        break;
+      }
+      case HF_REVERSE: {
+        need_operands(src, 1, c);
+        const Type &o = opt(0);
+        if (!t.same_shape(o) || t.dt != o.dt) c.invalid("type(operand) = type(result) violated (C1)");
+        if (quantized || o.quant >= 0) c.unsupported("reverse of quantized values");
+        bool seen[HF_MAX_RANK] = {false};
+        for (int64_t d : n.attr) {
+          if (d < 0 || d >= t.rank) c.invalid("0 <= dimensions < rank(result) violated (C3)");
+          if (seen[d]) c.invalid("is_unique(dimensions) violated (C2)");
+          seen[d] = true;
+        }
+        break;
+      }
+      case HF_IOTA:
+        need_operands(src, 0, c);
+        if (n.attr.size() != 1 || n.attr[0] < 0 || n.attr[0] >= t.rank)
+          c.invalid("0 <= iota_dimension < rank(output) violated (C1)");
+        if (quantized) c.unsupported("quantized iota");
+        if (!is_float(t.dt) && t.dt != HF_S32) c.unsupported("iota of an 8-bit integer type");
+        // the index converts to f32 first: one rounding only while it is exact there
+        if ((t.dt == HF_BF16 || t.dt == HF_F16) && !n.attr.empty() && t.dims[n.attr[0]] > (int64_t(1) << 24))
+          c.unsupported("16-bit float iota longer than 2^24");
+        break;
+      case HF_PAD: {
+        need_operands(src, 2, c);
+        const Type &o = opt(0), &pv = opt(1);
+        if (t.dt != o.dt || pv.dt != o.dt)
+          c.invalid("element_type(operand) = element_type(padding_value) = element_type(result) violated (C1)");
+        if (quantized || o.quant >= 0 || pv.quant >= 0) c.unsupported("pad of quantized values");
+        if (pv.rank != 0) c.invalid("padding_value must be a 0-dimensional tensor (I2)");
+        if ((int)n.attr.size() != 3 * o.rank || o.rank != t.rank)
+          c.invalid("size(edge_padding_low) = size(edge_padding_high) = size(interior_padding) = rank(operand) "
+                    "violated (C2)");
+        for (int d = 0; d < o.rank; ++d) {
+          const int64_t lo = n.attr[d], hi = n.attr[o.rank + d], in = n.attr[2 * o.rank + d];
+          if (in < 0) c.invalid("0 <= interior_padding violated (C3)");
+          if (t.dims[d] != o.dims[d] + lo + std::max<int64_t>(o.dims[d] - 1, 0) * in + hi)
+            c.invalid("shape(result) = shape(operand) + edge_padding_low + max(shape(operand) - 1, 0) * "
+                      "interior_padding + edge_padding_high violated (C4)");
+        }
+        break;
+      }
+      case HF_CONCATENATE: {
+        if (n.opd.empty()) c.invalid("0 < size(inputs) violated (C3)");
+        if (n.attr.size() != 1 || n.attr[0] < 0 || n.attr[0] >= opt(0).rank)
+          c.invalid("0 <= dimension < rank(inputs[0]) violated (C4)");
+        const int cd = n.attr.empty() ? 0 : (int)n.attr[0];
+        int64_t total = 0;
+        for (size_t k = 0; k < n.opd.size(); ++k) {
+          const Type &o = opt((int)k);
+          if (o.dt != opt(0).dt) c.invalid("same(element_type(inputs...)) violated (C1)");
+          if (o.quant >= 0) c.unsupported("concatenate of quantized values");
+          if (o.rank != t.rank) c.invalid("same(shape(inputs...)) except dim(inputs..., dimension) violated (C2)");
+          for (int d = 0; d < t.rank; ++d)
+            if (d != cd && o.dims[d] != t.dims[d])
+              c.invalid("same(shape(inputs...)) except dim(inputs..., dimension) violated (C2)");
+          total += o.dims[cd];
+        }
+        if (t.dt != opt(0).dt) c.invalid("element_type(result) = element_type(inputs[0]) violated (C5)");
+        if (quantized) c.unsupported("concatenate of quantized values");
+        if (t.dims[cd] != total) c.invalid("dim(result, dimension) = sum of dim(inputs..., dimension) violated (C6)");
         break;
       }
       case HF_UNIFORM_DEQUANTIZE:

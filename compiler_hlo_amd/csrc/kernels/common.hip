@@ -74,6 +74,8 @@ __device__ __forceinline__ float hf_tanh_for_bf16(float x) {
   return __builtin_copysignf(a < 0.5f ? small : large, x);
 }
 
+__device__ __forceinline__ int hf_clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // ---------------------------------------------------------- reductions
 // reducer codes: 0 add, 1 maximum, 2 minimum
 template <int OP>

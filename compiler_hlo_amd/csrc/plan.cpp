@@ -53,10 +53,54 @@ int phys_minor(const Type &t) {
   return -1;
 }
 
-Index operand_index(const Graph &g, int n, const Index &E, bool *general) {
+Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general) {
   const Node &nd = g.nodes[n];
-  const Type &ot = g.nodes[nd.opd[0]].t;
+  const Type &ot = g.nodes[nd.opd[k]].t;
+  auto expr = [](const std::string &e) {
+    Term t;
+    t.k = Term::EXPR;
+    t.e = e;
+    return t;
+  };
   switch (nd.op) {
+    case HF_REVERSE: {
+      // operand_index[d] = dim(result, d) - result_index[d] - 1 along the reversed dims
+      Index O = E;
+      for (int64_t d : nd.attr)
+        if (nd.t.dims[d] > 1) {
+          O[d] = expr("(" + std::to_string(nd.t.dims[d] - 1) + " - (" + term_str(E[d]) + "))");
+          *general = true;
+        }
+      return O;
+    }
+    case HF_PAD: {
+      if (k == 1) return Index();  // padding_value: rank 0
+      // result_index = low + operand_index * (interior + 1): read the operand
+      // at the candidate index, clamped into range (the value is used only
+      // where it is an operand element)
+      Index O = E;
+      const int r = ot.rank;
+      for (int d = 0; d < r; ++d) {
+        const long long lo = nd.attr[d], hi = nd.attr[r + d], step = nd.attr[2 * r + d] + 1;
+        if (lo == 0 && hi == 0 && step == 1) continue;
+        O[d] = expr("hf_clampi((" + term_str(E[d]) + " - (" + std::to_string(lo) + ")) / " + std::to_string(step) +
+                    ", 0, " + std::to_string(std::max<long long>(ot.dims[d] - 1, 0)) + ")");
+        *general = true;
+      }
+      return O;
+    }
+    case HF_CONCATENATE: {
+      // input k holds result positions [off_k, off_k + dim_k) along the dim,
+      // read clamped into range
+      const int cd = (int)nd.attr[0];
+      long long off = 0;
+      for (int j = 0; j < k; ++j) off += g.nodes[nd.opd[j]].t.dims[cd];
+      Index O = E;
+      O[cd] = expr("hf_clampi(" + term_str(E[cd]) + " - " + std::to_string(off) + ", 0, " +
+                   std::to_string(std::max<long long>(ot.dims[cd] - 1, 0)) + ")");
+      *general = true;
+      return O;
+    }
     case HF_TRANSPOSE: {
       // result dim d is operand dim perm[d]
       Index O(ot.rank);
@@ -117,7 +161,7 @@ void visit(const Graph &g, Ctx &c, int n, const Index &E) {
     return;
   }
   if (nd.op == HF_CONSTANT) return;
-  for (int o : nd.opd) visit(g, c, o, operand_index(g, n, E, &c.general));
+  for (size_t k = 0; k < nd.opd.size(); ++k) visit(g, c, nd.opd[k], operand_index(g, n, (int)k, E, &c.general));
 }
 
 // Partitioning (XLA:GPU Emitters, "Partitioning").  A node with one user is

@@ -38,8 +38,10 @@
 extern "C" {
 #endif
 
-#define HF_ABI_VERSION 1
+#define HF_ABI_VERSION 2
 #define HF_MAX_RANK 8
+#define HF_MAX_OPERANDS 8               /* concatenate is variadic */
+#define HF_MAX_ATTR (3 * HF_MAX_RANK)   /* pad: low, high and interior per dim */
 #define HF_MAX_PARAMS 16
 #define HF_MAX_NODES 256
 
@@ -82,7 +84,23 @@ typedef enum {
  *   HF_UNIFORM_QUANTIZE   q = clamp(round_half_even(real / scale) +
  *                         zero_point, storage_min, storage_max).
  *   HF_REDUCE             reduce over attr = dimensions with `reducer` and
- *                         `init_value`; must be the root.
+ *                         `init_value`.  At most one per fusion (its hero);
+ *                         only elementwise ops may follow it.
+ *   HF_REVERSE            reverse, attr = dimensions: operand index
+ *                         dim - 1 - i along each of them.
+ *   HF_IOTA               iota, no operands, attr[0] = iota_dimension: the
+ *                         index along that dim, in the element type.
+ *   HF_PAD                pad, operands {operand, padding_value (rank 0)},
+ *                         attr = edge_padding_low[rank], edge_padding_high[rank],
+ *                         interior_padding[rank]: result[i] =
+ *                         operand[(i - low) / (interior + 1)] where that is an
+ *                         operand element, else padding_value.
+ *   HF_CONCATENATE        concatenate, operands = inputs (1..HF_MAX_OPERANDS),
+ *                         attr[0] = dimension.
+ * The elementwise ops (add ... abs) also take per-tensor quantized operands
+ * and results of one baseline type: the operands are dequantized, the op runs
+ * on the f32 values and its result is quantized to the result type (each op's
+ * semantics for quantized types in the StableHLO Specification).
  */
 typedef enum {
   HF_PARAMETER = 0,
@@ -104,7 +122,11 @@ typedef enum {
   HF_TRANSPOSE = 16,
   HF_UNIFORM_DEQUANTIZE = 17,
   HF_UNIFORM_QUANTIZE = 18,
-  HF_REDUCE = 19
+  HF_REDUCE = 19,
+  HF_REVERSE = 20,
+  HF_IOTA = 21,
+  HF_PAD = 22,
+  HF_CONCATENATE = 23
 } hf_op;
 
 typedef enum { HF_REDUCER_ADD = 0, HF_REDUCER_MAX = 1, HF_REDUCER_MIN = 2 } hf_reducer;
@@ -143,12 +165,14 @@ typedef struct {
 typedef struct {
   hf_op op;
   int32_t n_operands;
-  int32_t operands[2];
+  int32_t operands[HF_MAX_OPERANDS];
   hf_type type;                 /* result type, stated explicitly */
   int32_t parameter_number;     /* HF_PARAMETER */
   double constant;              /* HF_CONSTANT */
   int32_t n_attr;
-  int64_t attr[HF_MAX_RANK];    /* permutation | broadcast_dimensions | dimensions */
+  int64_t attr[HF_MAX_ATTR];    /* permutation | broadcast_dimensions | dimensions |
+                                   iota_dimension | pad's low, high, interior |
+                                   concatenate's dimension */
   hf_reducer reducer;           /* HF_REDUCE */
   double init_value;            /* HF_REDUCE */
 } hf_node;

@@ -32,6 +32,8 @@ _SRC = os.path.join(_HERE, "hlo_oracle.c")
 _LIB = os.path.join(_HERE, "libhlo_oracle.so")
 
 MAX_RANK = 8
+MAX_OPERANDS = 8
+MAX_ATTR = 24
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "s32": 4, "u8": 5}
 NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "s8": np.int8,
               "s32": np.int32, "u8": np.uint8}
@@ -41,6 +43,7 @@ OPS = {
     "minimum": 10, "negate": 11, "abs": 12, "convert": 13,
     "broadcast_in_dim": 14, "reshape": 15, "transpose": 16,
     "uniform_dequantize": 17, "uniform_quantize": 18, "reduce": 19, "dot": 20,
+    "reverse": 21, "iota": 22, "pad": 23, "concatenate": 24,
 }
 REDUCERS = {"add": 0, "max": 1, "min": 2}
 
@@ -71,9 +74,9 @@ class OrType(ctypes.Structure):
 class OrNode(ctypes.Structure):
     _fields_ = [
         ("op", ctypes.c_int32), ("n_operands", ctypes.c_int32),
-        ("operands", ctypes.c_int32 * 2), ("type", OrType),
+        ("operands", ctypes.c_int32 * MAX_OPERANDS), ("type", OrType),
         ("param_index", ctypes.c_int32), ("constant", ctypes.c_double),
-        ("n_attr", ctypes.c_int32), ("attr", ctypes.c_int64 * MAX_RANK),
+        ("n_attr", ctypes.c_int32), ("attr", ctypes.c_int64 * MAX_ATTR),
         ("reducer", ctypes.c_int32), ("init", ctypes.c_double),
     ]
 
@@ -147,7 +150,14 @@ class _Graph:
                 c.type.storage_max = q.get("storage_max", hi)
             c.param_index = nd.get("param", -1)
             c.constant = float(nd.get("value", 0.0))
-            attr = nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", [])))
+            if nd["op"] == "pad":
+                attr = list(nd["edge_padding_low"]) + list(nd["edge_padding_high"]) + list(nd["interior_padding"])
+            elif nd["op"] == "iota":
+                attr = [nd["iota_dimension"]]
+            elif nd["op"] == "concatenate":
+                attr = [nd["dimension"]]
+            else:
+                attr = nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", [])))
             c.n_attr = len(attr)
             for k, a in enumerate(attr):
                 c.attr[k] = a

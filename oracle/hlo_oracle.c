@@ -41,6 +41,8 @@
 #include <string.h>
 
 #define OR_MAX_RANK 8
+#define OR_MAX_OPERANDS 8
+#define OR_MAX_ATTR 24
 
 /* element types */
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_S8 = 3, OR_S32 = 4, OR_U8 = 5 };
@@ -52,7 +54,7 @@ enum {
   OR_MAXIMUM = 9, OR_MINIMUM = 10, OR_NEGATE = 11, OR_ABS = 12,
   OR_CONVERT = 13, OR_BROADCAST_IN_DIM = 14, OR_RESHAPE = 15,
   OR_TRANSPOSE = 16, OR_DEQUANTIZE = 17, OR_QUANTIZE = 18, OR_REDUCE = 19,
-  OR_DOT = 20
+  OR_DOT = 20, OR_REVERSE = 21, OR_IOTA = 22, OR_PAD = 23, OR_CONCATENATE = 24
 };
 
 enum { OR_RED_ADD = 0, OR_RED_MAX = 1, OR_RED_MIN = 2 };
@@ -73,12 +75,14 @@ typedef struct {
 typedef struct {
   int32_t op;
   int32_t n_operands;
-  int32_t operands[2];
+  int32_t operands[OR_MAX_OPERANDS];
   or_type type;
   int32_t param_index;         /* OR_PARAM */
   double constant;             /* OR_CONSTANT: scalar, broadcast over type */
-  int32_t n_attr;              /* permutation | broadcast dims | reduce dims */
-  int64_t attr[OR_MAX_RANK];
+  int32_t n_attr;              /* permutation | broadcast dims | reduce dims |
+                                  reverse dims | iota dim | pad low, high,
+                                  interior | concatenate dim */
+  int64_t attr[OR_MAX_ATTR];
   int32_t reducer;             /* OR_REDUCE */
   double init;                 /* OR_REDUCE */
 } or_node;
@@ -388,6 +392,51 @@ static int eval(const graph *g, int n, const int64_t *idx, long double *out, aux
         pos /= ot->dims[d];
       }
       return eval(g, nd->operands[0], oidx, out, NULL);
+    }
+    case OR_REVERSE: {
+      /* operand_index[d] = dim(result, d) - result_index[d] - 1 for d in
+       * dimensions, result_index[d] otherwise */
+      for (int d = 0; d < t->rank; ++d) oidx[d] = idx[d];
+      for (int k = 0; k < nd->n_attr; ++k) {
+        const int d = (int)nd->attr[k];
+        oidx[d] = t->dims[d] - idx[d] - 1;
+      }
+      return eval(g, nd->operands[0], oidx, out, NULL);
+    }
+    case OR_IOTA:
+      /* the index along iota_dimension, in the element type */
+      *out = round_to(t->dtype, (long double)idx[nd->attr[0]]);
+      return 0;
+    case OR_PAD: {
+      /* result[i] = operand[j] where i = edge_padding_low + j * (interior_padding + 1)
+       * for an operand index j; padding_value elsewhere */
+      const or_type *ot = &g->nodes[nd->operands[0]].type;
+      const int r = ot->rank;
+      int inside = 1;
+      for (int d = 0; d < r && inside; ++d) {
+        const int64_t lo = nd->attr[d], step = nd->attr[2 * r + d] + 1;
+        const int64_t k = idx[d] - lo;
+        if (k < 0 || k % step != 0 || k / step >= ot->dims[d]) inside = 0;
+        else oidx[d] = k / step;
+      }
+      if (inside) return eval(g, nd->operands[0], oidx, out, NULL);
+      return eval(g, nd->operands[1], oidx, out, NULL); /* rank 0: no index */
+    }
+    case OR_CONCATENATE: {
+      /* result[.., i_d, ..] = inputs[k][.., i_d - (d_0 + ... + d_{k-1}), ..] */
+      const int cd = (int)nd->attr[0];
+      int64_t off = 0;
+      for (int k = 0; k < nd->n_operands; ++k) {
+        const int64_t dk = g->nodes[nd->operands[k]].type.dims[cd];
+        if (idx[cd] < off + dk) {
+          for (int d = 0; d < t->rank; ++d) oidx[d] = idx[d];
+          oidx[cd] = idx[cd] - off;
+          return eval(g, nd->operands[k], oidx, out, NULL);
+        }
+        off += dk;
+      }
+      set_err("concatenate index out of range", n);
+      return -2;
     }
     case OR_DEQUANTIZE: {
       const or_type *qt = &g->nodes[nd->operands[0]].type;

@@ -285,6 +285,81 @@ def test_quantized_exp_within_one_step():
 
 
 # --------------------------------------------------------------------------
+# index transforms: reverse, iota, pad, concatenate
+# --------------------------------------------------------------------------
+def test_index_transforms_small_bitexact():
+    g = W.rng(81)
+    cases = 0
+    for shape in [(5, 7), (3, 1, 6), (2, 3, 4)]:
+        r = len(shape)
+        x = W.normal_f32(g, int(np.prod(shape)))
+        for dims in [(r - 1,), (0,), tuple(range(r))]:
+            s = W.Spec()
+            p = s.parameter(0, "f32", list(shape))
+            s.reverse(p, dims, "f32", list(shape))
+            got, _ = run_gpu(s.nodes, [x])
+            assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+            cases += 1
+        for d in range(r):
+            for dt in ("f32", "s32", "bf16"):
+                s = W.Spec()
+                s.iota(d, dt, list(shape))
+                got, _ = run_gpu(s.nodes, [])
+                assert_bitexact(got, oracle.evaluate(s.nodes, []), dt)
+                cases += 1
+            other = list(shape)
+            other[d] = 3
+            y = W.normal_f32(g, int(np.prod(other)))
+            out = list(shape)
+            out[d] = 2 * shape[d] + 3
+            s = W.Spec()
+            pa = s.parameter(0, "f32", list(shape))
+            pb = s.parameter(1, "f32", other)
+            s.concatenate([pa, pb, pa], d, "f32", out)
+            got, _ = run_gpu(s.nodes, [x, y])
+            assert_bitexact(got, oracle.evaluate(s.nodes, [x, y]), "f32")
+            cases += 1
+        for lo, hi, it in [([1] * r, [2] * r, [0] * r), ([-1] + [0] * (r - 1), [0] * (r - 1) + [-1], [1] * r),
+                           ([2] * r, [-1] * r, [2] * r)]:
+            out = [n + l + max(n - 1, 0) * i + h for n, l, h, i in zip(shape, lo, hi, it)]
+            if min(out) < 1:
+                continue
+            s = W.Spec()
+            p = s.parameter(0, "f32", list(shape))
+            v = s.parameter(1, "f32", [])
+            s.pad(p, v, lo, hi, it, "f32", out)
+            pv = np.array(-3.25, np.float32)
+            got, _ = run_gpu(s.nodes, [x, pv])
+            assert_bitexact(got, oracle.evaluate(s.nodes, [x, pv]), "f32")
+            cases += 1
+    say("index-transform cases:", cases)
+
+
+def test_index_transforms_composed():
+    """pad (negative edge, interior), reverse along the minor dim, plus iota,
+    then concatenated with a padded second input: every element is a data
+    movement or one f32 add, so the result is bit-exact."""
+    g = W.rng(82)
+    n0, n1, m1 = 1000, 1500, 77
+    x = W.normal_f32(g, n0 * n1)
+    y = W.normal_f32(g, n0 * m1)
+    o0, o1 = 2 + n0 + (n0 - 1) + 1, -1 + n1 + 3
+    s = W.Spec()
+    px = s.parameter(0, "f32", [n0, n1])
+    py = s.parameter(1, "f32", [n0, m1])
+    pv = s.constant(-1.0, "f32", [])
+    p = s.pad(px, pv, [2, -1], [1, 3], [1, 0], "f32", [o0, o1])
+    rv = s.reverse(p, [1], "f32", [o0, o1])
+    io = s.iota(0, "f32", [o0, o1])
+    a = s.binary("add", rv, io, "f32", [o0, o1])
+    yy = s.pad(py, pv, [0, 0], [o0 - n0, 0], [0, 0], "f32", [o0, m1])
+    s.concatenate([a, yy], 1, "f32", [o0, o1 + m1])
+    got, f = run_gpu(s.nodes, [x, y])
+    assert f.plan()["hero"] == "loop"
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x, y]), "f32")
+
+
+# --------------------------------------------------------------------------
 # elementwise epilogues after a reduce
 # --------------------------------------------------------------------------
 def test_reduce_epilogue_mean():

@@ -33,7 +33,7 @@ def test_exports_every_declared_function():
     lib = H.library()
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.hf_abi_version() == 1
+    assert lib.hf_abi_version() == H.ABI_VERSION == 2
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -184,6 +184,48 @@ def test_quantized_elementwise_validation_and_expansion():
     s.op("abs", [a], "s8", [16], quant=W.quant_type("s8", [0.5], [1], storage_min=-100, storage_max=100))
     st, msg = _status(s.nodes)
     assert st == "HF_ERR_INVALID" and "storage" in msg
+
+
+def test_index_transform_validation():
+    def st(build):
+        s = W.Spec()
+        build(s)
+        return _status(s.nodes)
+    def rev(s):
+        p = s.parameter(0, "f32", [3, 4])
+        s.reverse(p, [1, 1], "f32", [3, 4])
+    assert st(rev)[0] == "HF_ERR_INVALID" and "is_unique" in st(rev)[1]
+    def iota(s):
+        s.iota(2, "f32", [3, 4])
+    assert st(iota)[0] == "HF_ERR_INVALID" and "iota_dimension" in st(iota)[1]
+    def pad_shape(s):
+        p = s.parameter(0, "f32", [2, 3])
+        v = s.constant(0.0, "f32", [])
+        s.pad(p, v, [0, 1], [2, 1], [1, 2], "f32", [5, 8])
+    assert st(pad_shape)[0] == "HF_ERR_INVALID" and "(C4)" in st(pad_shape)[1]
+    def pad_interior(s):
+        p = s.parameter(0, "f32", [2, 3])
+        v = s.constant(0.0, "f32", [])
+        s.pad(p, v, [0, 0], [0, 0], [-1, 0], "f32", [1, 3])
+    assert st(pad_interior)[0] == "HF_ERR_INVALID" and "(C3)" in st(pad_interior)[1]
+    def pad_value_rank(s):
+        p = s.parameter(0, "f32", [2, 3])
+        v = s.parameter(1, "f32", [1])
+        s.pad(p, v, [0, 0], [0, 0], [0, 0], "f32", [2, 3])
+    assert st(pad_value_rank)[0] == "HF_ERR_INVALID" and "0-dimensional" in st(pad_value_rank)[1]
+    def cat(s):
+        a = s.parameter(0, "f32", [3, 2])
+        b = s.parameter(1, "f32", [2, 3])
+        s.concatenate([a, b], 0, "f32", [5, 2])
+    assert st(cat)[0] == "HF_ERR_INVALID" and "(C2)" in st(cat)[1]
+    def ok(s):
+        a = s.parameter(0, "f32", [3, 2])
+        b = s.parameter(1, "f32", [1, 2])
+        c = s.concatenate([a, b, a], 0, "f32", [7, 2])
+        r = s.reverse(c, [0], "f32", [7, 2])
+        v = s.constant(0.5, "f32", [])
+        s.pad(r, v, [1, -1], [0, 2], [0, 1], "f32", [8, 4])
+    assert st(ok) == ("HF_OK", "")
 
 
 def test_reduce_epilogue_is_planned_as_a_second_context():

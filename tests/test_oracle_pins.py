@@ -6,6 +6,7 @@ closed forms, library routines with the same definition (numpy transpose,
 reshape, float32 arithmetic), exhaustive enumeration, and exact rational
 arithmetic.  None of them re-types the oracle's own formula.
 """
+import itertools
 import json
 import math
 import os
@@ -565,6 +566,89 @@ def test_requantize_direct():
     deq = (np.float32(0.1) * (x.astype(np.float32) - np.float32(3))).astype(np.float32)
     want = np.clip(np.rint((deq / np.float32(0.05)).astype(np.float32)).astype(np.int64) - 2, -128, 127)
     assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# Index transforms (StableHLO Specification: reverse, iota, pad, concatenate)
+# --------------------------------------------------------------------------
+def test_reverse_iota_pad_concatenate_page_examples():
+    G = GOLD["reverse"]
+    x = np.array(G["operand"], np.int32)
+    s = Spec()
+    p = s.parameter(0, "s32", list(x.shape))
+    s.reverse(p, G["dimensions"], "s32", list(x.shape))
+    assert ev(s, [x]).reshape(x.shape).tolist() == G["result"]
+    G = GOLD["iota"]
+    for d, key in ((0, "dim0"), (1, "dim1")):
+        s = Spec()
+        s.iota(d, "s32", G["dims"])
+        assert ev(s, []).reshape(G["dims"]).tolist() == G[key]
+    G = GOLD["pad"]
+    x = np.array(G["operand"], np.int32)
+    s = Spec()
+    p = s.parameter(0, "s32", list(x.shape))
+    v = s.parameter(1, "s32", [])
+    out = np.array(G["result"])
+    s.pad(p, v, G["edge_padding_low"], G["edge_padding_high"], G["interior_padding"], "s32", list(out.shape))
+    assert ev(s, [x, np.array(G["padding_value"], np.int32)]).reshape(out.shape).tolist() == G["result"]
+    G = GOLD["concatenate"]
+    a, b = np.array(G["input0"], np.int32), np.array(G["input1"], np.int32)
+    s = Spec()
+    pa = s.parameter(0, "s32", list(a.shape))
+    pb = s.parameter(1, "s32", list(b.shape))
+    s.concatenate([pa, pb], G["dimension"], "s32", [4, 2])
+    assert ev(s, [a, b]).reshape(4, 2).tolist() == G["result"]
+
+
+def _np_pad(x, pv, lo, hi, interior):
+    """Interior padding by strided assignment, then edges: np.pad for positive
+    amounts and slicing for negative ones."""
+    inner = [(n - 1) * (i + 1) + 1 if n else 0 for n, i in zip(x.shape, interior)]
+    y = np.full(inner, pv, x.dtype)
+    y[tuple(slice(None, None, i + 1) for i in interior)] = x
+    y = np.pad(y, [(max(l, 0), max(h, 0)) for l, h in zip(lo, hi)], constant_values=pv)
+    return y[tuple(slice(-min(l, 0), y.shape[d] + min(h, 0)) for d, (l, h) in enumerate(zip(lo, hi)))]
+
+
+def test_index_transforms_against_numpy():
+    g = rng(71)
+    for shape in [(2, 3), (3, 1, 4), (5,), (2, 2, 2, 3)]:
+        x = g.standard_normal(shape).astype(np.float32)
+        r = len(shape)
+        for dims in itertools.chain.from_iterable(itertools.combinations(range(r), k) for k in range(r + 1)):
+            s = Spec()
+            p = s.parameter(0, "f32", list(shape))
+            s.reverse(p, dims, "f32", list(shape))
+            assert np.array_equal(ev(s, [x]).reshape(shape), np.flip(x, dims) if dims else x)
+        for d in range(r):
+            s = Spec()
+            s.iota(d, "f32", list(shape))
+            want = np.broadcast_to(np.arange(shape[d]).reshape([-1 if k == d else 1 for k in range(r)]), shape)
+            assert np.array_equal(ev(s, []).reshape(shape), want.astype(np.float32))
+            other = list(shape)
+            other[d] = 2
+            y = g.standard_normal(other).astype(np.float32)
+            out = list(shape)
+            out[d] += 2
+            s = Spec()
+            pa = s.parameter(0, "f32", list(shape))
+            pb = s.parameter(1, "f32", other)
+            s.concatenate([pa, pb, pa], d, "f32", [out[k] + (shape[d] if k == d else 0) for k in range(r)])
+            assert np.array_equal(ev(s, [x, y]).reshape(np.concatenate([x, y, x], d).shape),
+                                  np.concatenate([x, y, x], d))
+        for _ in range(6):
+            lo = g.integers(-1, 3, r).tolist()
+            hi = g.integers(-1, 3, r).tolist()
+            it = g.integers(0, 3, r).tolist()
+            out = [n + l + max(n - 1, 0) * i + h for n, l, h, i in zip(shape, lo, hi, it)]
+            if min(out) < 1:
+                continue
+            s = Spec()
+            p = s.parameter(0, "f32", list(shape))
+            v = s.parameter(1, "f32", [])
+            s.pad(p, v, lo, hi, it, "f32", out)
+            want = _np_pad(x, np.float32(-7.5), lo, hi, it)
+            assert np.array_equal(ev(s, [x, np.array(-7.5, np.float32)]).reshape(out), want)
 
 
 # --------------------------------------------------------------------------

@@ -88,6 +88,19 @@ class Spec:
         return self.op("reduce", [x], dtype, dims, m2m, dimensions=list(dims_to_reduce),
                        reducer=reducer, init=float(init))
 
+    def reverse(self, x, dims_to_reverse, dtype, dims, m2m=None) -> int:
+        return self.op("reverse", [x], dtype, dims, m2m, dimensions=list(dims_to_reverse))
+
+    def iota(self, iota_dimension, dtype, dims, m2m=None) -> int:
+        return self.op("iota", [], dtype, dims, m2m, iota_dimension=int(iota_dimension))
+
+    def pad(self, x, padding_value, low, high, interior, dtype, dims, m2m=None) -> int:
+        return self.op("pad", [x, padding_value], dtype, dims, m2m, edge_padding_low=list(low),
+                       edge_padding_high=list(high), interior_padding=list(interior))
+
+    def concatenate(self, inputs, dimension, dtype, dims, m2m=None) -> int:
+        return self.op("concatenate", list(inputs), dtype, dims, m2m, dimension=int(dimension))
+
     def convert(self, x, dtype, dims, m2m=None) -> int:
         return self.op("convert", [x], dtype, dims, m2m)
 
