@@ -452,13 +452,17 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // bits (and so their HBM channels); a diagonal order then spreads both.
     const long long in_row_bytes = DW * stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt));
     const long long order = env_ll("HF_TR_ORDER", in_row_bytes >= 8192 ? 2 : 0);
+    // 512 threads per tile (each moves one or two 128-bit vectors per phase)
+    // when both phases of a full tile divide evenly among them, else 256
+    const long long lv = (long long)tu * (tw / vin), sv = (long long)tw * (tu / vout);
+    const int tblock = (int)env_ll("HF_TR_BLOCK", lv % 512 == 0 && sv % 512 == 0 ? 512 : 256);
     P.ctx.push_back(ld);
     P.ctx.push_back(st);
-    P.block = 256;
+    P.block = tblock;
     P.grid = nb * ntu * ntw;
     P.lds_bytes = tw * pitch * 4;
     P.empty = rt.numel() == 0;
-    P.macros = {{"HF_BLOCK", 256}, {"HF_TU", tu}, {"HF_TW", tw}, {"HF_PITCH", pitch},
+    P.macros = {{"HF_BLOCK", tblock}, {"HF_TU", tu}, {"HF_TW", tw}, {"HF_PITCH", pitch},
                 {"HF_VIN", vin}, {"HF_VOUT", vout}, {"HF_DU", DU}, {"HF_DW", DW},
                 {"HF_NTU", ntu}, {"HF_NTW", ntw}, {"HF_ORDER", order}};
     P.info.vector_elems = vout;
