@@ -532,11 +532,10 @@ Plan plan_reduce(const Graph &g) {
            "node " + std::to_string(g.reduce) +
                " (reduce): reduced dimensions are neither the physically minor nor the physically major ones");
   }
+  // K: elements per output (0 when a reduced dim is empty: every output is
+  // init); J: outputs
   long long K = 1, J = 1;
   for (int d = 0; d < it.rank; ++d) (red[d] ? K : J) *= it.dims[d];
-  if (it.numel() == 0) K = J = 0;
-  for (int d = 0; d < it.rank; ++d)
-    if (it.dims[d] == 0) (red[d] ? K : J) = 0;
 
   Plan P;
   P.rin = rin;

@@ -285,6 +285,69 @@ def test_quantized_exp_within_one_step():
 
 
 # --------------------------------------------------------------------------
+# degenerate and maximum sizes
+# --------------------------------------------------------------------------
+def test_empty_and_degenerate_shapes():
+    """Zero-size arrays launch nothing; a reduce over a zero-length dim gives
+    init for every output (row and column layouts); a reduce to a scalar."""
+    import torch
+    for dims in ([0, 64], [64, 0], [3, 0, 5]):
+        s = W.Spec()
+        p = s.parameter(0, "f32", dims)
+        s.unary("exponential", p, "f32", dims)
+        got, _ = run_gpu(s.nodes, [np.zeros(0, np.float32)])
+        assert got.size == 0
+    s = W.Spec()
+    p = s.parameter(0, "f32", [0, 64])
+    s.transpose(p, [1, 0], "f32", [64, 0])
+    got, _ = run_gpu(s.nodes, [np.zeros(0, np.float32)])
+    assert got.size == 0
+    for dims, rdim, m2m in (([37, 0], 1, [1, 0]), ([37, 0], 1, [0, 1]), ([0, 37], 0, [1, 0])):
+        for red, init in (("add", 1.5), ("max", -2.0)):
+            s = W.Spec()
+            p = s.parameter(0, "f32", dims, m2m)
+            s.reduce(p, [rdim], red, init, "f32", [37])
+            got, f = run_gpu(s.nodes, [np.zeros(0, np.float32)])
+            say("empty reduce", m2m, red, f.plan()["hero"])
+            assert np.array_equal(got, np.full(37, init, np.float32))
+            assert_bitexact(got, oracle.evaluate(s.nodes, [np.zeros(0, np.float32)]), "f32")
+    g = W.rng(91)
+    x = W.integers(g, 3000, -8, 8, np.int64).astype(np.float32)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [3000])
+    s.reduce(p, [0], "add", 0.0, "f32", [])
+    got, _ = run_gpu(s.nodes, [x])
+    assert got.reshape(-1)[0] == np.float32(x.astype(np.float64).sum())
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind", ["loop", "transpose"])
+def test_largest_arrays_below_the_size_limit(kind):
+    """f32[8191, 65536] is the largest 2-D f32 array below the 2 GiB limit:
+    32-bit offsets reach their maximum.  Sampled outputs against the oracle."""
+    n0, n1 = 8191, 65536
+    say("largest arrays", kind, n0, n1)
+    g = W.rng(92)
+    x = W.uniform_f32(g, n0 * n1, -4.0, 4.0)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [n0, n1])
+    e = s.unary("exponential", p, "f32", [n0, n1])
+    if kind == "transpose":
+        s.transpose(e, [1, 0], "f32", [n1, n0])
+        odims = [n1, n0]
+    else:
+        odims = [n0, n1]
+    got, f = run_gpu(s.nodes, [x])
+    assert f.plan()["hero"] == kind
+    pts = np.stack([g.integers(0, odims[0], 20000), g.integers(0, odims[1], 20000)], 1)
+    pts = np.concatenate([pts, [[0, 0], [odims[0] - 1, odims[1] - 1], [odims[0] - 1, 0], [0, odims[1] - 1]]])
+    want, _ = oracle.evaluate_points(s.nodes, [x], pts)
+    lin = pts[:, 0] * odims[1] + pts[:, 1]
+    assert_ulp(got[lin], want.astype(np.float32), "f32", 2)
+    del x, got
+
+
+# --------------------------------------------------------------------------
 # index transforms: reverse, iota, pad, concatenate
 # --------------------------------------------------------------------------
 def test_index_transforms_small_bitexact():

@@ -186,6 +186,18 @@ def test_quantized_elementwise_validation_and_expansion():
     assert st == "HF_ERR_INVALID" and "storage" in msg
 
 
+def test_size_limit():
+    ok = W.Spec()
+    p = ok.parameter(0, "f32", [8191, 65536])
+    ok.unary("exponential", p, "f32", [8191, 65536])
+    assert _status(ok.nodes) == ("HF_OK", "")
+    big = W.Spec()
+    p = big.parameter(0, "f32", [8192, 65536])
+    big.unary("exponential", p, "f32", [8192, 65536])
+    st, msg = _status(big.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "2 GiB" in msg
+
+
 def test_index_transform_validation():
     def st(build):
         s = W.Spec()
