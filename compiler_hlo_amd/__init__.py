@@ -45,7 +45,7 @@ OPS = {
     "uniform_quantize": 18, "reduce": 19, "reverse": 20, "iota": 21, "pad": 22,
     "concatenate": 23,
 }
-REDUCERS = {"add": 0, "max": 1, "min": 2}
+REDUCERS = {"add": 0, "max": 1, "min": 2, "argmax": 3}
 HEROES = {0: "loop", 1: "transpose", 2: "row_reduce", 3: "column_reduce"}
 STATUS = {0: "HF_OK", 1: "HF_ERR_INVALID", 2: "HF_ERR_UNSUPPORTED", 3: "HF_ERR_COMPILE",
           4: "HF_ERR_HIP", 5: "HF_ERR_NOMEM"}
@@ -223,7 +223,7 @@ class Fusion:
             self._keep += [sc, zp, hq]
             c.type.quant = ctypes.pointer(hq)
         c.parameter_number = nd.get("param", -1)
-        c.constant = float(nd.get("value", 0.0))
+        c.constant = float(nd.get("value", nd.get("index_init", 0.0)))
         attr = node_attr(nd)
         c.n_attr = len(attr)
         for k, a in enumerate(attr):

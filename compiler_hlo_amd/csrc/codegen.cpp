@@ -642,6 +642,22 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         glue_pair(glue, is_row ? "hf_rr_eval" : "hf_cr_eval", is_row ? "int row, int kv" : "int r, int c", "hf_regs_t",
                   f, ix.str(), call_args(it), "", "", "float (&hf_res)[HF_V]");
       }
+      if (R.reducer == HF_REDUCER_ARGMAX) {
+        // max/argmax: the folds start from (init_value, index init); the
+        // result is the index
+        glue << "#define HF_ARG_V0 " << flit(round_to_dtype(R.init, g.nodes[P.rin].t.dt)) << "\n#define HF_ARG_K0 ("
+             << (long long)R.cst << ")\n";
+        glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store_arg" : "hf_cr_store_arg")
+             << "(const HfArgs &A, int " << outer << ", int k) {\n";
+        if (!kept.empty()) delinearize(glue, it, kept, outer, "hf_t");
+        else glue << "  (void)" << outer << ";\n";
+        std::vector<char> kset(it.rank, 0);
+        for (int d : kept) kset[d] = 1;
+        for (int d : kept_inc)
+          if (!kset[d]) glue << "  const int i" << d << " = 0;\n";
+        glue << "  A.out[" << outoff << "] = k;\n}\n";
+        break;
+      }
       glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store" : "hf_cr_store") << "(const HfArgs &A, int "
            << outer << ", float acc) {\n";
       if (!kept.empty()) delinearize(glue, it, kept, outer, "hf_t");

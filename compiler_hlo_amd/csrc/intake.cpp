@@ -440,11 +440,26 @@ Graph intake(const hf_fusion_desc *desc) {
         if (opt(0).quant < 0 && opt(0).dt != HF_F32) c.unsupported("operand must be f32 or quantized");
         break;
       case HF_REDUCE: {
-        need_operands(src, 1, c);
+        if (src.reducer < HF_REDUCER_ADD || src.reducer > HF_REDUCER_ARGMAX) c.invalid("unknown reducer");
         const Type &o = opt(0);
-        if (t.dt != o.dt) c.invalid("element_type(inputs) = element_type(init_values) = result type violated (C2, C8)");
-        if (!is_float(t.dt) || o.quant >= 0) c.unsupported("only floating-point reductions are supported");
-        if (src.reducer < HF_REDUCER_ADD || src.reducer > HF_REDUCER_MIN) c.invalid("unknown reducer");
+        if (src.reducer == HF_REDUCER_ARGMAX) {
+          // variadic max/argmax: {values, indices} -> the index of the maximum
+          need_operands(src, 2, c);
+          const Node &ix = g.nodes[n.opd[1]];
+          if (!is_float(o.dt) || o.quant >= 0) c.unsupported("argmax values must be floating point");
+          if (!ix.t.same_shape(o)) c.invalid("all inputs must have the same dimensions");
+          if (t.dt != HF_S32 || ix.t.dt != HF_S32) c.invalid("the argmax result and the indices must be s32");
+          if (n.attr.size() != 1) c.unsupported("argmax over more than one dimension");
+          if (ix.op != HF_IOTA || n.attr.empty() || ix.attr[0] != n.attr[0])
+            c.unsupported("argmax indices must be an iota along the reduced dimension");
+          if (n.cst != std::floor(n.cst) || n.cst < INT32_MIN || n.cst > INT32_MAX)
+            c.invalid("the index init value must be an s32 value");
+        } else {
+          need_operands(src, 1, c);
+          if (t.dt != o.dt)
+            c.invalid("element_type(inputs) = element_type(init_values) = result type violated (C2, C8)");
+          if (!is_float(t.dt) || o.quant >= 0) c.unsupported("only floating-point reductions are supported");
+        }
         bool red[HF_MAX_RANK] = {false};
         for (int64_t d : n.attr) {
           if (d < 0 || d >= o.rank) c.invalid("0 <= dimensions < rank(inputs[0]) violated (C4)");

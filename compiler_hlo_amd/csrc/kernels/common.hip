@@ -119,6 +119,34 @@ __device__ __forceinline__ float hf_group_reduce(float v) {
   return v;
 }
 
+// Max/argmax pairs (the variadic reduce of Operation semantics).  A thread
+// folds its elements in increasing index order with the reducer body: the
+// value replaces the running maximum when value >= max (so NaN never does,
+// and later equal values win).  Partial results then combine by larger
+// value, then larger index -- a commutative, associative choice that gives
+// the sequential fold's answer.
+__device__ __forceinline__ void hf_arg_step(float &m, int &k, float v, int j) {
+  if (v >= m) {
+    m = v;
+    k = j;
+  }
+}
+__device__ __forceinline__ void hf_arg_combine(float &m, int &k, float m2, int k2) {
+  if (m2 > m || (m2 == m && k2 > k)) {
+    m = m2;
+    k = k2;
+  }
+}
+template <int W>  // across groups of W lanes (W a power of two <= 64)
+__device__ __forceinline__ void hf_arg_group_reduce(float &m, int &k) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, W);
+    const int k2 = __shfl_xor(k, o, W);
+    hf_arg_combine(m, k, m2, k2);
+  }
+}
+
 // ------------------------------------------------------------ loads
 // Global loads are split from their use: a fetch function issues the raw
 // loads of a whole hero step into registers (so every load of the step is in

@@ -17,9 +17,60 @@
 //
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_C, HF_R, HF_CL,
 // HF_RL, HF_CB, HF_NCB, HF_S, HF_RS, hf_regs_t, hf_cr_eval_fetch(A, r, c, R),
-// hf_cr_eval(A, r, c, R, x), hf_cr_store(A, c, acc).
+// hf_cr_eval(A, r, c, R, x), hf_cr_store(A, c, acc); for max/argmax (HF_OP 3)
+// HF_ARG_V0, HF_ARG_K0 and hf_cr_store_arg(A, c, index).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
+#if HF_OP == 3
+  // max/argmax: the index of an element is its row r; each thread visits its
+  // rows in increasing order.  The workspace holds the segments' maxima
+  // ([HF_S][HF_C] floats) followed by their indices ([HF_S][HF_C] ints).
+  __shared__ float pm[HF_RL * HF_CB];
+  __shared__ int pk[HF_RL * HF_CB];
+  {
+    const int cb = blockIdx.x % HF_NCB, seg = blockIdx.x / HF_NCB;
+    const int cl = threadIdx.x % HF_CL, rl = threadIdx.x / HF_CL;
+    const int c = cb * HF_CB + cl * HF_V;
+    float m[HF_V];
+    int k[HF_V];
+#pragma unroll
+    for (int v = 0; v < HF_V; ++v) {
+      m[v] = HF_ARG_V0;
+      k[v] = HF_ARG_K0;
+    }
+    const int r_begin = seg * HF_RS;
+    const int r_end = r_begin + HF_RS < HF_R ? r_begin + HF_RS : HF_R;
+    if (c < HF_C) {
+      for (int r = r_begin + rl; r < r_end; r += HF_RL) {
+        hf_regs_t R1;
+        hf_cr_eval_fetch(A, r, c, R1);
+        float x[HF_V];
+        hf_cr_eval(A, r, c, R1, x);
+#pragma unroll
+        for (int v = 0; v < HF_V; ++v) hf_arg_step(m[v], k[v], x[v], r);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < HF_V; ++v) {
+      pm[rl * HF_CB + cl * HF_V + v] = m[v];
+      pk[rl * HF_CB + cl * HF_V + v] = k[v];
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < HF_CB; j += HF_BLOCK) {
+      float mm = pm[j];
+      int kk = pk[j];
+      for (int q = 1; q < HF_RL; ++q) hf_arg_combine(mm, kk, pm[q * HF_CB + j], pk[q * HF_CB + j]);
+      if (cb * HF_CB + j < HF_C) {
+#if HF_S == 1
+        hf_cr_store_arg(A, cb * HF_CB + j, kk);
+#else
+        ((float *)A.ws)[(long)seg * HF_C + cb * HF_CB + j] = mm;
+        ((int *)A.ws)[(long)HF_S * HF_C + (long)seg * HF_C + cb * HF_CB + j] = kk;
+#endif
+      }
+    }
+  }
+#else
   __shared__ float part[HF_RL * HF_CB];
   const int cb = blockIdx.x % HF_NCB, seg = blockIdx.x / HF_NCB;
   const int cl = threadIdx.x % HF_CL, rl = threadIdx.x / HF_CL;
@@ -68,6 +119,7 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
 #endif
     }
   }
+#endif  // HF_OP == 3
 }
 
 #if HF_S > 1
@@ -77,6 +129,27 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
 // combined in wave order -- a fixed order, so the result is deterministic.
 extern "C" __global__ __launch_bounds__(256) void HF_FOLD_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
+#if HF_OP == 3
+  __shared__ float pm[4][64];
+  __shared__ int pk[4][64];
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + lane;
+    float m = HF_ARG_V0;
+    int k = HF_ARG_K0;
+    if (col < HF_C)
+      for (int q = wave; q < HF_S; q += 4)
+        hf_arg_combine(m, k, ((const float *)A.ws)[(long)q * HF_C + col],
+                       ((const int *)A.ws)[(long)HF_S * HF_C + (long)q * HF_C + col]);
+    pm[wave][lane] = m;
+    pk[wave][lane] = k;
+    __syncthreads();
+    if (wave == 0 && col < HF_C) {
+      for (int w = 1; w < 4; ++w) hf_arg_combine(m, k, pm[w][lane], pk[w][lane]);
+      hf_cr_store_arg(A, col, k);
+    }
+  }
+#else
   __shared__ float part[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = blockIdx.x * 64 + lane;
@@ -91,5 +164,6 @@ extern "C" __global__ __launch_bounds__(256) void HF_FOLD_NAME(HF_KERNEL_PARAMS)
   if (wave == 0 && col < HF_C)
     hf_cr_store(A, col, hf_red<HF_OP>(hf_red<HF_OP>(part[0][lane], part[1][lane]),
                                       hf_red<HF_OP>(part[2][lane], part[3][lane])));
+#endif  // HF_OP == 3
 }
 #endif

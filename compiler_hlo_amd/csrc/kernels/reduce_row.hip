@@ -15,9 +15,50 @@
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
 // (vectors per row), HF_TPR, HF_RR_PACKED, hf_regs_t,
 // hf_rr_eval_fetch(A, row, kv, R), hf_rr_eval(A, row, kv, R, x) (HF_V floats,
-// or HF_V/2 packed bf16 pairs), hf_rr_store(A, row, acc).
+// or HF_V/2 packed bf16 pairs), hf_rr_store(A, row, acc); for max/argmax
+// (HF_OP 3) HF_ARG_V0, HF_ARG_K0 and hf_rr_store_arg(A, row, index).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
+#if HF_OP == 3
+  // max/argmax: the index of element (row, kv, v) along the reduced dim is
+  // kv * HF_V + v; each lane visits its elements in increasing index order.
+  constexpr int RPB = HF_BLOCK / HF_TPR;
+  constexpr int GW = HF_TPR < 64 ? HF_TPR : 64;  // lanes reduced by shuffles
+  __shared__ float pm[HF_BLOCK / 64];
+  __shared__ int pk[HF_BLOCK / 64];
+  const int sub = threadIdx.x % HF_TPR, rloc = threadIdx.x / HF_TPR;
+  for (int row0 = blockIdx.x * RPB; row0 < HF_ROWS; row0 += gridDim.x * RPB) {
+    const int row = row0 + rloc;
+    float m = HF_ARG_V0;
+    int k = HF_ARG_K0;
+    if (row < HF_ROWS) {
+      for (int kv = sub; kv < HF_KV; kv += HF_TPR) {
+        hf_regs_t R1;
+        hf_rr_eval_fetch(A, row, kv, R1);
+        float x[HF_V];
+        hf_rr_eval(A, row, kv, R1, x);
+#pragma unroll
+        for (int v = 0; v < HF_V; ++v) hf_arg_step(m, k, x[v], kv * HF_V + v);
+      }
+    }
+    hf_arg_group_reduce<GW>(m, k);
+    if (HF_TPR > 64) {  // one row per workgroup: combine the waves through LDS
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      if (lane == 0) {
+        pm[wave] = m;
+        pk[wave] = k;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int w = 1; w < HF_BLOCK / 64; ++w) hf_arg_combine(m, k, pm[w], pk[w]);
+        hf_rr_store_arg(A, row, k);
+      }
+      __syncthreads();
+    } else if (sub == 0 && row < HF_ROWS) {
+      hf_rr_store_arg(A, row, k);
+    }
+  }
+#else
 #if HF_RR_PACKED
   // The evaluated row elements arrive as packed bf16 pairs (a sum of bf16
   // values converted to f32): one dot-product step adds a pair.
@@ -117,4 +158,5 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     if (sub == 0 && row < HF_ROWS) hf_rr_store(A, row, s);
   }
 #endif
+#endif  // HF_OP == 3
 }

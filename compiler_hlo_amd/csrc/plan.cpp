@@ -588,7 +588,7 @@ Plan plan_reduce(const Graph &g) {
     P.block = block;
     P.lds_bytes = (int)(rl * cb * 4 + 4);
     if (segs > 1) {
-      P.ws_bytes = segs * Cc * 4;
+      P.ws_bytes = segs * Cc * (op == HF_REDUCER_ARGMAX ? 8 : 4);  // max/argmax: value and index
       P.fold_grid = ceil_div(Cc, 64);
     }
     P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_C", Cc}, {"HF_R", Rr},

@@ -129,7 +129,20 @@ typedef enum {
   HF_CONCATENATE = 23
 } hf_op;
 
-typedef enum { HF_REDUCER_ADD = 0, HF_REDUCER_MAX = 1, HF_REDUCER_MIN = 2 } hf_reducer;
+/* HF_REDUCER_ARGMAX is the variadic max/argmax reduce of Operation semantics
+ * ("Variadic Reduce"): operands {values, indices}, where indices must be an
+ * s32 iota along the single reduced dimension; the result (s32) is the index
+ * part of the tuple fold f(max, argmax, value, index) = value >= max ?
+ * (value, index) : (max, argmax), started from (init_value, constant).  The
+ * library folds in parallel and combines partial results by larger value,
+ * then larger index: ties go to the last index, as in the sequential fold, and
+ * NaN values are never selected. */
+typedef enum {
+  HF_REDUCER_ADD = 0,
+  HF_REDUCER_MAX = 1,
+  HF_REDUCER_MIN = 2,
+  HF_REDUCER_ARGMAX = 3
+} hf_reducer;
 
 /* Uniform quantization parameters of a quantized element type (StableHLO
  * Specification, "Types": QuantizedTensorElementType, constraints C1-C13;
@@ -174,7 +187,8 @@ typedef struct {
                                    iota_dimension | pad's low, high, interior |
                                    concatenate's dimension */
   hf_reducer reducer;           /* HF_REDUCE */
-  double init_value;            /* HF_REDUCE */
+  double init_value;            /* HF_REDUCE (for HF_REDUCER_ARGMAX: the value
+                                   init; `constant` holds the index init) */
 } hf_node;
 
 typedef struct {

@@ -45,7 +45,7 @@ OPS = {
     "uniform_dequantize": 17, "uniform_quantize": 18, "reduce": 19, "dot": 20,
     "reverse": 21, "iota": 22, "pad": 23, "concatenate": 24,
 }
-REDUCERS = {"add": 0, "max": 1, "min": 2}
+REDUCERS = {"add": 0, "max": 1, "min": 2, "argmax": 3}
 
 
 def build(force: bool = False) -> str:
@@ -149,7 +149,7 @@ class _Graph:
                 c.type.storage_min = q.get("storage_min", lo)
                 c.type.storage_max = q.get("storage_max", hi)
             c.param_index = nd.get("param", -1)
-            c.constant = float(nd.get("value", 0.0))
+            c.constant = float(nd.get("value", nd.get("index_init", 0.0)))
             if nd["op"] == "pad":
                 attr = list(nd["edge_padding_low"]) + list(nd["edge_padding_high"]) + list(nd["interior_padding"])
             elif nd["op"] == "iota":

@@ -57,7 +57,7 @@ enum {
   OR_DOT = 20, OR_REVERSE = 21, OR_IOTA = 22, OR_PAD = 23, OR_CONCATENATE = 24
 };
 
-enum { OR_RED_ADD = 0, OR_RED_MAX = 1, OR_RED_MIN = 2 };
+enum { OR_RED_ADD = 0, OR_RED_MAX = 1, OR_RED_MIN = 2, OR_RED_ARGMAX = 3 };
 
 typedef struct {
   int32_t dtype;               /* element (storage) type */
@@ -290,6 +290,7 @@ static int eval_reduce(const graph *g, int n, const int64_t *ridx, long double *
     else oidx[d] = ridx[r++];
   }
   long double acc = (long double)nd->init;
+  long double arg = (long double)nd->constant; /* argmax: the index part of the tuple */
   long double abs_sum = 0;
   int64_t count = 1;
   for (int k = 0; k < nrd; ++k) count *= in->type.dims[rd[k]];
@@ -300,14 +301,22 @@ static int eval_reduce(const graph *g, int n, const int64_t *ridx, long double *
     if (rc) return rc;
     if (nd->reducer == OR_RED_ADD) { acc += x; abs_sum += fabsl(x); }
     else if (nd->reducer == OR_RED_MAX) acc = ieee_maximum(acc, x);
-    else acc = ieee_minimum(acc, x);
+    else if (nd->reducer == OR_RED_MIN) acc = ieee_minimum(acc, x);
+    else {
+      /* Operation semantics, "Variadic Reduce": f(max, argmax, value, index)
+       * = value >= max ? (value, index) : (max, argmax), applied in order */
+      long double k;
+      rc = eval(g, nd->operands[1], oidx, &k, NULL);
+      if (rc) return rc;
+      if (x >= acc) { acc = x; arg = k; }
+    }
     for (int k = nrd - 1; k >= 0; --k) {
       if (++oidx[rd[k]] < in->type.dims[rd[k]]) break;
       oidx[rd[k]] = 0;
     }
   }
   if (aux) { aux->abs_sum = abs_sum; aux->raw = acc; }
-  *out = round_to(nd->type.dtype, acc);
+  *out = nd->reducer == OR_RED_ARGMAX ? arg : round_to(nd->type.dtype, acc);
   return 0;
 }
 

@@ -285,6 +285,40 @@ def test_quantized_exp_within_one_step():
 
 
 # --------------------------------------------------------------------------
+# variadic max/argmax
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dims,rdim,dtype", [([64, 3000], 1, "f32"), ([3000, 64], 0, "f32"),
+                                             ([16384, 512], 0, "f32"), ([100, 40], 1, "bf16"),
+                                             ([7, 5], 1, "f32"), ([10240, 2048], 1, "bf16")])
+def test_argmax(dims, rdim, dtype):
+    """Integer-valued data: many ties, which must go to the last index."""
+    say("argmax", dims, rdim, dtype)
+    g = W.rng(111 + dims[0])
+    n = int(np.prod(dims))
+    x = W.integers(g, n, -20, 20, np.int64).astype(np.float32)
+    if dtype == "bf16":
+        x = (x.view(np.uint32) >> 16).astype(np.uint16)
+    s = W.Spec()
+    p = s.parameter(0, dtype, dims)
+    s.argmax(p, rdim, dims)
+    got, f = run_gpu(s.nodes, [x])
+    say("  hero", f.plan()["hero"], "workspace", f.plan()["workspace_bytes"])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32")
+
+
+def test_argmax_nan_and_init_ties():
+    nan, ninf = np.float32("nan"), np.float32("-inf")
+    rows = np.array([[1, nan, 3, nan, 3], [nan] * 5, [ninf, ninf, 2, ninf, ninf], [ninf] * 5], np.float32)
+    x = np.tile(rows, (1, 200))           # rows of 1000
+    for rdim, arr in ((1, x), (0, np.ascontiguousarray(x.T))):
+        s = W.Spec()
+        p = s.parameter(0, "f32", list(arr.shape))
+        s.argmax(p, rdim, list(arr.shape))
+        got, _ = run_gpu(s.nodes, [arr.ravel()])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [arr.ravel()]), "s32")
+
+
+# --------------------------------------------------------------------------
 # degenerate and maximum sizes
 # --------------------------------------------------------------------------
 def test_empty_and_degenerate_shapes():

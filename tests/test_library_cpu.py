@@ -186,6 +186,32 @@ def test_quantized_elementwise_validation_and_expansion():
     assert st == "HF_ERR_INVALID" and "storage" in msg
 
 
+def test_argmax_validation():
+    s = W.Spec()
+    p = s.parameter(0, "f32", [8, 9])
+    s.argmax(p, 1, [8, 9])
+    assert _status(s.nodes) == ("HF_OK", "")
+    # indices that are not an iota along the reduced dim
+    s = W.Spec()
+    p = s.parameter(0, "f32", [8, 9])
+    k = s.parameter(1, "s32", [8, 9])
+    s.op("reduce", [p, k], "s32", [8], dimensions=[1], reducer="argmax", init=float("-inf"), index_init=-1)
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "iota" in msg
+    s = W.Spec()
+    p = s.parameter(0, "f32", [8, 9])
+    k = s.iota(0, "s32", [8, 9])
+    s.op("reduce", [p, k], "s32", [8], dimensions=[1], reducer="argmax", init=float("-inf"), index_init=-1)
+    assert _status(s.nodes)[0] == "HF_ERR_UNSUPPORTED"
+    # the result must be s32
+    s = W.Spec()
+    p = s.parameter(0, "f32", [8, 9])
+    k = s.iota(1, "s32", [8, 9])
+    s.op("reduce", [p, k], "f32", [8], dimensions=[1], reducer="argmax", init=float("-inf"), index_init=-1)
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_INVALID" and "s32" in msg
+
+
 def test_size_limit():
     ok = W.Spec()
     p = ok.parameter(0, "f32", [8191, 65536])

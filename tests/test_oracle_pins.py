@@ -652,6 +652,38 @@ def test_index_transforms_against_numpy():
 
 
 # --------------------------------------------------------------------------
+# Variadic max/argmax reduce (Operation semantics, "Variadic Reduce")
+# --------------------------------------------------------------------------
+def _argmax_spec(dims, rdim, dtype="f32", init=float("-inf"), index_init=-1):
+    s = Spec()
+    p = s.parameter(0, dtype, list(dims))
+    k = s.iota(rdim, "s32", list(dims))
+    out = [d for i, d in enumerate(dims) if i != rdim]
+    s.op("reduce", [p, k], "s32", out, dimensions=[rdim], reducer="argmax", init=init, index_init=index_init)
+    return s
+
+
+def test_argmax_is_the_last_index_of_the_maximum():
+    """The fold f(max, argmax, v, i) = v >= max ? (v, i) : (max, argmax) in
+    index order keeps the LAST index of the maximum: n - 1 - argmax of the
+    reversed row (numpy's argmax keeps the first)."""
+    g = rng(101)
+    x = g.integers(-5, 5, (40, 33)).astype(np.float32)   # many ties
+    for rdim in (0, 1):
+        got = ev(_argmax_spec(x.shape, rdim), [x]).astype(np.int64)
+        n = x.shape[rdim]
+        want = n - 1 - np.argmax(np.flip(x, rdim), axis=rdim)
+        assert np.array_equal(got, want)
+
+
+def test_argmax_skips_nan_and_takes_values_equal_to_init():
+    nan, ninf = float("nan"), float("-inf")
+    rows = np.array([[1, nan, 3, nan, 3], [nan] * 5, [ninf, ninf, 2, ninf, ninf], [ninf] * 5], np.float32)
+    got = ev(_argmax_spec(rows.shape, 1, index_init=-1), [rows]).astype(np.int64).tolist()
+    assert got == [4, -1, 2, 4]
+
+
+# --------------------------------------------------------------------------
 # Elementwise ops on quantized tensors (StableHLO Specification, each op's
 # semantics for quantized types: dequantize, op, quantize)
 # --------------------------------------------------------------------------

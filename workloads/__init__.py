@@ -101,6 +101,14 @@ class Spec:
     def concatenate(self, inputs, dimension, dtype, dims, m2m=None) -> int:
         return self.op("concatenate", list(inputs), dtype, dims, m2m, dimension=int(dimension))
 
+    def argmax(self, x, rdim, dims, index_init=-1, init=float("-inf"), m2m=None) -> int:
+        """Variadic max/argmax reduce over `rdim` of x with an iota index
+        operand; the result is the s32 index."""
+        k = self.iota(rdim, "s32", dims)
+        out = [d for i, d in enumerate(dims) if i != rdim]
+        return self.op("reduce", [x, k], "s32", out, m2m, dimensions=[rdim], reducer="argmax",
+                       init=float(init), index_init=int(index_init))
+
     def convert(self, x, dtype, dims, m2m=None) -> int:
         return self.op("convert", [x], dtype, dims, m2m)
 
