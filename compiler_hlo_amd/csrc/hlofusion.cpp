@@ -76,18 +76,21 @@ const std::vector<const char *> &rtc_options() {
   return o;
 }
 
+// Compiled code objects of this process, keyed by the full compile input
+// (options, compiler version, source): no two sources can share an entry.
 std::mutex g_cache_mu;
-std::map<uint64_t, std::vector<char>> g_cache;
+std::map<std::string, std::vector<char>> g_cache;
 
 hf_status compile(const std::string &src, std::vector<char> *code) {
   std::string opts;
   for (const char *o : rtc_options()) opts += std::string(o) + " ";
   int ver_major = 0, ver_minor = 0;
   hiprtcVersion(&ver_major, &ver_minor);
-  uint64_t key = fnv1a(opts + std::to_string(ver_major) + "." + std::to_string(ver_minor) + "\n" + src);
+  const std::string full = opts + std::to_string(ver_major) + "." + std::to_string(ver_minor) + "\n" + src;
+  const uint64_t key = fnv1a(full);
   {
     std::lock_guard<std::mutex> lk(g_cache_mu);
-    auto it = g_cache.find(key);
+    auto it = g_cache.find(full);
     if (it != g_cache.end()) {
       *code = it->second;
       return HF_OK;
@@ -103,7 +106,7 @@ hf_status compile(const std::string &src, std::vector<char> *code) {
       code->assign(std::istreambuf_iterator<char>(f), std::istreambuf_iterator<char>());
       if (!code->empty()) {
         std::lock_guard<std::mutex> lk(g_cache_mu);
-        g_cache[key] = *code;
+        g_cache[full] = *code;
         return HF_OK;
       }
     }
@@ -125,10 +128,18 @@ hf_status compile(const std::string &src, std::vector<char> *code) {
     return HF_ERR_COMPILE;
   }
   size_t sz = 0;
-  hiprtcGetCodeSize(prog, &sz);
+  if (hiprtcGetCodeSize(prog, &sz) != HIPRTC_SUCCESS || sz == 0) {
+    hiprtcDestroyProgram(&prog);
+    set_err("hiprtcGetCodeSize failed");
+    return HF_ERR_COMPILE;
+  }
   code->resize(sz);
-  hiprtcGetCode(prog, code->data());
+  r = hiprtcGetCode(prog, code->data());
   hiprtcDestroyProgram(&prog);
+  if (r != HIPRTC_SUCCESS) {
+    set_err(std::string("hiprtcGetCode failed: ") + hiprtcGetErrorString(r));
+    return HF_ERR_COMPILE;
+  }
   if (!cpath.empty()) {
     std::string tmp = cpath + ".tmp" + std::to_string((long)getpid());
     std::ofstream f(tmp, std::ios::binary);
@@ -137,7 +148,7 @@ hf_status compile(const std::string &src, std::vector<char> *code) {
     std::rename(tmp.c_str(), cpath.c_str());
   }
   std::lock_guard<std::mutex> lk(g_cache_mu);
-  g_cache[key] = *code;
+  g_cache[full] = *code;
   return HF_OK;
 }
 
@@ -243,8 +254,10 @@ int64_t hf_linear_index(int32_t rank, const int64_t *dims, const int32_t *m2m, c
     int d = m2m[k];
     if (d < 0 || d >= rank || seen[d] || index[d] < 0 || index[d] >= dims[d]) return -1;
     seen[d] = true;
-    lin += index[d] * stride;
-    stride *= dims[d];
+    int64_t term;
+    if (__builtin_mul_overflow(index[d], stride, &term) || __builtin_add_overflow(lin, term, &lin) ||
+        __builtin_mul_overflow(stride, dims[d], &stride))
+      return -1;
   }
   return lin;
 }
@@ -256,8 +269,9 @@ hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion
     return HF_ERR_INVALID;
   }
   *out = nullptr;
-  std::unique_ptr<hf_fusion> f(new hf_fusion);
+  // No exception crosses the C boundary.
   try {
+    std::unique_ptr<hf_fusion> f(new hf_fusion);
     f->g = hf::intake(desc);
     f->P = hf::make_plan(f->g);
     f->plan_only = flags & HF_CREATE_PLAN_ONLY;
@@ -265,28 +279,32 @@ hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion
     if (!f->plan_only) {
       std::string prelude = k_src_common;
       f->source = hf::generate_source(f->g, f->P, prelude, hero_text(f->P.hero));
+      dump(f.get());
+      hf_status st = compile(f->source, &f->code);
+      if (st != HF_OK) return st;
+      if (!f->compile_only) {
+        st = load_on_device(f.get());
+        if (st != HF_OK) {
+          release(f.release());
+          return st;
+        }
+      }
     }
+    *out = f.release();
+    return HF_OK;
   } catch (const hf::Error &e) {
     set_err(e.msg);
     return e.status;
+  } catch (const std::bad_alloc &) {
+    set_err("out of host memory");
+    return HF_ERR_NOMEM;
   } catch (const std::exception &e) {
     set_err(std::string("internal error: ") + e.what());
     return HF_ERR_INVALID;
+  } catch (...) {
+    set_err("internal error");
+    return HF_ERR_INVALID;
   }
-  if (!f->plan_only) {
-    dump(f.get());
-    hf_status st = compile(f->source, &f->code);
-    if (st != HF_OK) return st;
-    if (!f->compile_only) {
-      st = load_on_device(f.get());
-      if (st != HF_OK) {
-        release(f.release());
-        return st;
-      }
-    }
-  }
-  *out = f.release();
-  return HF_OK;
 }
 
 hf_status hf_fusion_plan(const hf_fusion *f, hf_plan_info *info) {
@@ -355,19 +373,24 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
     }
   }
   if (f->P.empty) return HF_OK;
-  std::vector<void *> vals;
-  for (int k = 0; k < n_params; ++k) vals.push_back(const_cast<void *>(params[k]));
-  vals.push_back(result);
-  for (void *q : f->qdev) vals.push_back(q);
-  vals.push_back(f->ws);
-  std::vector<void *> ptrs;
-  for (void *&v : vals) ptrs.push_back(&v);
+  // Kernel arguments, in the generated kernel's order: parameters, result,
+  // the per-axis quantization arrays, the workspace.  On the stack: a launch
+  // allocates nothing.
+  constexpr int kMaxArgs = HF_MAX_NODES + 1 + 3 * HF_MAX_NODES + 1;
+  void *vals[kMaxArgs];
+  void *ptrs[kMaxArgs];
+  int na = 0;
+  for (int k = 0; k < n_params; ++k) vals[na++] = const_cast<void *>(params[k]);
+  vals[na++] = result;
+  for (void *q : f->qdev) vals[na++] = q;
+  vals[na++] = f->ws;
+  for (int k = 0; k < na; ++k) ptrs[k] = &vals[k];
   e = hipModuleLaunchKernel(f->fn, (unsigned)f->P.grid, 1, 1, (unsigned)f->P.block, 1, 1, 0, (hipStream_t)stream,
-                            ptrs.data(), nullptr);
+                            ptrs, nullptr);
   if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
   if (f->fold) {
-    e = hipModuleLaunchKernel(f->fold, (unsigned)f->P.fold_grid, 1, 1, 256, 1, 1, 0, (hipStream_t)stream,
-                              ptrs.data(), nullptr);
+    e = hipModuleLaunchKernel(f->fold, (unsigned)f->P.fold_grid, 1, 1, 256, 1, 1, 0, (hipStream_t)stream, ptrs,
+                              nullptr);
     if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(fold)");
   }
   return HF_OK;
