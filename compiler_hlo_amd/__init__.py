@@ -264,11 +264,16 @@ class Fusion:
             want = int(np.prod(nd["dims"], dtype=np.int64)) * DTYPE_BYTES[nd["dtype"]]
             if not p.is_contiguous() or p.numel() * p.element_size() != want:
                 raise ValueError("parameter %d must be a dense buffer of %d bytes" % (k, want))
+            if not p.is_cuda:
+                raise ValueError("parameter %d must be a GPU tensor" % k)
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
+               "s8": torch.int8, "u8": torch.uint8, "s32": torch.int32}[self.out_dtype]
         if out is None:
-            tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-                   "s8": torch.int8, "u8": torch.uint8, "s32": torch.int32}[self.out_dtype]
             dev = params[0].device if params else torch.device("cuda")
             out = torch.empty(self.out_numel, dtype=tdt, device=dev)
+        elif (not out.is_cuda or not out.is_contiguous() or out.dtype != tdt
+              or out.numel() != self.out_numel):
+            raise ValueError("out must be a dense GPU tensor of %d %s elements" % (self.out_numel, self.out_dtype))
         if stream is None:
             stream = torch.cuda.current_stream()
         self.launch_ptrs([p.data_ptr() for p in params], out.data_ptr(), stream.cuda_stream)

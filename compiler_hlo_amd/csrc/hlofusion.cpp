@@ -350,13 +350,45 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
     set_err("the current device differs from the device the fusion was created on");
     return HF_ERR_INVALID;
   }
+  // A buffer must be device memory of this device (or managed memory), with
+  // its whole extent inside one allocation: anything else is rejected here,
+  // before a kernel could fault on it.
+  auto check_buffer = [&](const void *p, size_t bytes, const std::string &what) -> bool {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the failed query to the next call
+      set_err(what + " is not device memory");
+      return false;
+    }
+    const bool managed = a.isManaged || a.type == hipMemoryTypeManaged;
+    if (!managed && (a.type != hipMemoryTypeDevice || a.device != f->device)) {
+      set_err(what + " is not device memory of the fusion's device");
+      return false;
+    }
+    if (!managed) {
+      hipDeviceptr_t base = nullptr;
+      size_t size = 0;
+      if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err(what + ": hipMemGetAddressRange failed");
+        return false;
+      }
+      if ((uintptr_t)p + bytes > (uintptr_t)base + size) {
+        set_err(what + " extends past the end of its allocation");
+        return false;
+      }
+    }
+    return true;
+  };
   const hf::Type &rt = f->g.nodes[f->g.root].t;
+  const size_t rbytes = (size_t)(rt.numel() * hf::dtype_bytes(rt.dt));
   const uintptr_t r0 = (uintptr_t)result;
-  const uintptr_t r1 = r0 + (uintptr_t)(rt.numel() * hf::dtype_bytes(rt.dt));
+  const uintptr_t r1 = r0 + (uintptr_t)rbytes;
   if (rt.numel() > 0 && (!result || (r0 & 15))) {
     set_err("result must be a non-NULL, 16-byte aligned device pointer");
     return HF_ERR_INVALID;
   }
+  if (rt.numel() > 0 && !check_buffer(result, rbytes, "the result")) return HF_ERR_INVALID;
   for (int k = 0; k < n_params; ++k) {
     int pn = f->g.param_node[k];
     if (pn < 0) continue;
@@ -367,6 +399,7 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
       set_err("parameter " + std::to_string(k) + " must be a non-NULL, 16-byte aligned device pointer");
       return HF_ERR_INVALID;
     }
+    if (!check_buffer(params[k], (size_t)(p1 - p0), "parameter " + std::to_string(k))) return HF_ERR_INVALID;
     if (rt.numel() > 0 && p0 < r1 && r0 < p1) {
       set_err("the result buffer overlaps parameter " + std::to_string(k));
       return HF_ERR_INVALID;

@@ -719,6 +719,19 @@ def test_launch_argument_errors():
     with pytest.raises(H.FusionError) as e:
         f.launch_ptrs([x.data_ptr()], x.data_ptr())
     assert e.value.status == "HF_ERR_INVALID" and "overlaps" in e.value.message
+    # pinned host memory is not device memory (the GPU could read it, so the
+    # launch would not fault even if it were let through)
+    h = torch.empty(64 * 64, dtype=torch.float32).pin_memory()
+    with pytest.raises(H.FusionError) as e:
+        f.launch_ptrs([h.data_ptr()], out.data_ptr())
+    assert e.value.status == "HF_ERR_INVALID" and "device memory" in e.value.message
+    # the binding checks tensors before anything reaches the library
+    with pytest.raises(ValueError):
+        f(x.cpu())
+    with pytest.raises(ValueError):
+        f(x, out=torch.empty(100, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        f(x, out=torch.empty(64 * 64, dtype=torch.int32, device="cuda"))
     f(x, out=out)
     torch.cuda.synchronize()
     assert from_device(out, "f32").size == 4096
