@@ -249,8 +249,13 @@ hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *le
  * parameter).  The same parameter pointer may be passed twice.  stream is a
  * hipStream_t (NULL = the null stream).  The launch is asynchronous and
  * allocates nothing; a fault inside the kernel surfaces at the caller's next
- * synchronisation.  Errors: HF_ERR_INVALID (count, NULL, alignment, overlap,
- * plan-only handle, wrong device), HF_ERR_HIP. */
+ * synchronisation.  Each buffer must be device memory of the fusion's
+ * device (or managed memory) whose whole extent lies in one allocation; host
+ * memory, pinned or not, is rejected.  Errors: HF_ERR_INVALID (count, NULL,
+ * alignment, overlap, not device memory, extent past its allocation,
+ * plan-only handle, wrong current device), HF_ERR_HIP.  Launches of one
+ * handle must not overlap in time (a column reduce's workspace belongs to the
+ * handle). */
 hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params,
                            void *result, void *stream);
 
