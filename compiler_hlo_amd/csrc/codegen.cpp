@@ -394,8 +394,10 @@ class Gen {
           std::string sc, zp, rc;
           quant_params(b, t.quant, E, &sc, &zp, &rc);
           v = fresh(b, n);
-          b.os << "  int " << v << "[" << b.V << "];\n  hf_quantize_v<" << b.V << ">(" << y0 << ", " << rc << ", " << zp
-               << ", " << Q.smin << ", " << Q.smax << ", " << v << ");\n";
+          // the fusion's 8-bit result: only the low byte of each value is stored
+          const bool low_byte = n == g_.root && dtype_bytes(t.dt) == 1;
+          b.os << "  int " << v << "[" << b.V << "];\n  hf_quantize_v<" << b.V << (low_byte ? ", true" : "") << ">("
+               << y0 << ", " << rc << ", " << zp << ", " << Q.smin << ", " << Q.smax << ", " << v << ");\n";
           (void)sc;
           break;
         }

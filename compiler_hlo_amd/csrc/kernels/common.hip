@@ -345,8 +345,10 @@ __device__ __forceinline__ int hf_quantize(float y, float scale, int zp, int smi
 // 1.5*2^23 + rne(t); its low mantissa bits hold rne(t) in two's complement.
 // The clamp is applied to a (bounds shifted by the same constant); |t| >=
 // 2^22 lies far outside any storage range and clamps the same way.  A zero
-// point is added after rounding, as an integer.
-template <int V>
+// point is added after rounding, as an integer.  With LOW_BYTE, q keeps only
+// a correct low byte (all an 8-bit store needs): for a zero point of 0 that
+// is the low byte of a's bits, since 1.5*2^23's low byte is 0.
+template <int V, bool LOW_BYTE = false>
 __device__ __forceinline__ void hf_quantize_v(const float (&y)[V], const double (&rcp)[V], const int (&zp)[V],
                                               int smin, int smax, int (&q)[V]) {
   constexpr float M = 12582912.0f;  // 1.5 * 2^23
@@ -355,6 +357,7 @@ __device__ __forceinline__ void hf_quantize_v(const float (&y)[V], const double 
     const float t = (float)((double)y[l] * rcp[l]);
     const float a = t + M;
     const float c = __builtin_fminf(__builtin_fmaxf(a, M + (float)(smin - zp[l])), M + (float)(smax - zp[l]));
-    q[l] = (int)(__float_as_uint(c) - __float_as_uint(M)) + zp[l];
+    if constexpr (LOW_BYTE) q[l] = (int)__float_as_uint(c) + zp[l];
+    else q[l] = (int)(__float_as_uint(c) - __float_as_uint(M)) + zp[l];
   }
 }
