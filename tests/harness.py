@@ -63,13 +63,22 @@ def nan_mask_bf16(bits):
     return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
 
 
+def nan_mask_f16(bits):
+    b = np.asarray(bits, np.uint16)
+    return ((b & 0x7C00) == 0x7C00) & ((b & 0x03FF) != 0)
+
+
+def nan_mask_16(bits, dtype: str):
+    return nan_mask_f16(bits) if dtype == "f16" else nan_mask_bf16(bits)
+
+
 def assert_bitexact(got: np.ndarray, want: np.ndarray, dtype: str):
     if dtype == "f32":
         gn, wn = nan_mask_f32(got), nan_mask_f32(want)
         assert np.array_equal(gn, wn), "NaN positions differ"
         g, w = got.view(np.uint32)[~gn], want.view(np.uint32)[~wn]
     elif dtype in ("bf16", "f16"):
-        gn, wn = nan_mask_bf16(got), nan_mask_bf16(want)
+        gn, wn = nan_mask_16(got, dtype), nan_mask_16(want, dtype)
         assert np.array_equal(gn, wn), "NaN positions differ"
         g, w = got[~gn], want[~wn]
     else:
@@ -84,8 +93,8 @@ def assert_ulp(got, want, dtype: str, max_ulp: int):
         gn, wn = nan_mask_f32(got), nan_mask_f32(want)
         assert np.array_equal(gn, wn), "NaN positions differ"
         d = ulp_dist_f32(got[~gn], want[~wn])
-    else:
-        gn, wn = nan_mask_bf16(got), nan_mask_bf16(want)
+    else:  # bf16 or f16: ordinal distance of the 16-bit sign-magnitude patterns
+        gn, wn = nan_mask_16(got, dtype), nan_mask_16(want, dtype)
         assert np.array_equal(gn, wn), "NaN positions differ"
         d = ulp_dist_bf16(got[~gn], want[~wn])
     worst = int(d.max()) if d.size else 0

@@ -285,6 +285,64 @@ def test_quantized_exp_within_one_step():
 
 
 # --------------------------------------------------------------------------
+# f16 and u8 element types
+# --------------------------------------------------------------------------
+def test_f16_paths():
+    """f16 through each hero: an elementwise loop (add, convert), a transpose
+    (bit-exact), a row sum of f16 values in f32, and f16 exp within an ulp."""
+    g = W.rng(131)
+    n0, n1 = 300, 520
+    a = (g.standard_normal(n0 * n1) * 20).astype(np.float16).view(np.uint16)
+    b = (g.standard_normal(n0 * n1) * 20).astype(np.float16).view(np.uint16)
+    s = W.Spec()
+    pa = s.parameter(0, "f16", [n0, n1])
+    pb = s.parameter(1, "f16", [n0, n1])
+    ad = s.binary("add", pa, pb, "f16", [n0, n1])
+    s.binary("multiply", ad, pa, "f16", [n0, n1])
+    got, f = run_gpu(s.nodes, [a, b])
+    assert f.plan()["hero"] == "loop"
+    assert_bitexact(got, oracle.evaluate(s.nodes, [a, b]), "f16")
+    s = W.Spec()
+    pa = s.parameter(0, "f16", [n0, n1])
+    s.transpose(pa, [1, 0], "f16", [n1, n0])
+    got, f = run_gpu(s.nodes, [a])
+    assert f.plan()["hero"] == "transpose"
+    assert_bitexact(got, oracle.evaluate(s.nodes, [a]), "f16")
+    x = W.integers(g, n0 * n1, -6, 6, np.int64).astype(np.float16).view(np.uint16)
+    s = W.Spec()
+    pa = s.parameter(0, "f16", [n0, n1])
+    cv = s.convert(pa, "f32", [n0, n1])
+    s.reduce(cv, [1], "add", 0.0, "f32", [n0])
+    got, f = run_gpu(s.nodes, [x])
+    assert f.plan()["hero"] == "row_reduce"
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+    e = (g.standard_normal(n0 * n1) * 3).astype(np.float16).view(np.uint16)
+    s = W.Spec()
+    pa = s.parameter(0, "f16", [n0 * n1])
+    s.unary("exponential", pa, "f16", [n0 * n1])
+    got, _ = run_gpu(s.nodes, [e])
+    assert_ulp(got, oracle.evaluate(s.nodes, [e]), "f16", 1)
+
+
+def test_u8_quantize_dequantize():
+    g = W.rng(132)
+    y = W.uniform_f32(g, 200000, -80.0, 80.0)
+    qt = W.quant_type("u8", [0.5], [128])
+    s = W.Spec()
+    p = s.parameter(0, "f32", [200000])
+    s.op("uniform_quantize", [p], "u8", [200000], quant=qt)
+    got, _ = run_gpu(s.nodes, [y])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [y]), "u8")
+    q = W.integers(g, 300 * 256, 0, 255, np.uint8)
+    s = W.Spec()
+    p = s.parameter(0, "u8", [300, 256], quant=W.quant_type("u8", list(np.linspace(0.01, 0.2, 256)),
+                                                               list(range(0, 256)), qdim=1))
+    s.op("uniform_dequantize", [p], "f32", [300, 256])
+    got, _ = run_gpu(s.nodes, [q])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [q]), "f32")
+
+
+# --------------------------------------------------------------------------
 # variadic max/argmax
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("dims,rdim,dtype", [([64, 3000], 1, "f32"), ([3000, 64], 0, "f32"),

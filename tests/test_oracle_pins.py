@@ -569,6 +569,42 @@ def test_requantize_direct():
 
 
 # --------------------------------------------------------------------------
+# f16 and u8 (element types beyond the configs)
+# --------------------------------------------------------------------------
+def test_f16_convert_and_add_match_numpy_float16():
+    """f32 -> f16 rounds to nearest even (numpy's float16 conversion); f16 add
+    is the f32 sum of the operands rounded to f16 (exact in f32 before the
+    rounding, so it is the correctly rounded f16 sum)."""
+    g = rng(121)
+    x = np.concatenate([g.standard_normal(4000).astype(np.float32) * 300,
+                        np.array([65504, 65519.99, 65520, 6.1e-5, 5.96e-8, 2.98e-8, -0.0], np.float32)])
+    s = Spec()
+    p = s.parameter(0, "f32", [x.size])
+    s.convert(p, "f16", [x.size])
+    got = ev(s, [x])
+    assert np.array_equal(got.view(np.uint16), x.astype(np.float16).view(np.uint16))
+    a = (g.standard_normal(4000) * 30).astype(np.float16)
+    b = (g.standard_normal(4000) * 30).astype(np.float16)
+    s = Spec()
+    pa = s.parameter(0, "f16", [4000])
+    pb = s.parameter(1, "f16", [4000])
+    s.binary("add", pa, pb, "f16", [4000])
+    got = ev(s, [a.view(np.uint16), b.view(np.uint16)])
+    assert np.array_equal(got.view(np.uint16), (a + b).view(np.uint16))
+
+
+def test_u8_quantize_range_and_zero_point():
+    """u8 storage: [0, 255]; zero point 128 puts real 0 mid-range."""
+    q = quant_type("u8", [0.5], [128])
+    y = np.array([0.0, 0.25, 0.75, -64.0, -64.25, -64.5, 63.5, 63.75, 1e6, -1e6], np.float32)
+    s = Spec()
+    p = s.parameter(0, "f32", [y.size])
+    s.op("uniform_quantize", [p], "u8", [y.size], quant=q)
+    got = ev(s, [y]).astype(np.int64).tolist()
+    assert got == [128, 128, 130, 0, 0, 0, 255, 255, 255, 0]
+
+
+# --------------------------------------------------------------------------
 # Index transforms (StableHLO Specification: reverse, iota, pad, concatenate)
 # --------------------------------------------------------------------------
 def test_reverse_iota_pad_concatenate_page_examples():
