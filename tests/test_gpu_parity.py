@@ -284,6 +284,36 @@ def test_quantized_exp_within_one_step():
     assert d.max() <= 1 and (d > 0).mean() < 1e-3
 
 
+def test_every_f32_elementwise_op():
+    """Each f32 elementwise op on wide-range operands (subnormal results
+    included): the IEEE arithmetic and sign ops bit-exact, the
+    transcendentals within 2 ulp."""
+    g = W.rng(133)
+    n = 1 << 18
+    a = (g.standard_normal(n) * np.exp2(g.integers(-130, 60, n))).astype(np.float32)
+    b = (g.standard_normal(n) * np.exp2(g.integers(-130, 60, n))).astype(np.float32)
+    pos = np.abs(a) + np.float32(1e-30)
+    small = (g.standard_normal(n) * 4).astype(np.float32)
+    for op in ("add", "subtract", "multiply", "divide", "maximum", "minimum"):
+        s = W.Spec()
+        x = s.parameter(0, "f32", [n])
+        y = s.parameter(1, "f32", [n])
+        s.binary(op, x, y, "f32", [n])
+        got, _ = run_gpu(s.nodes, [a, b])
+        assert_bitexact(got, oracle.evaluate(s.nodes, [a, b]), "f32")
+    for op, arr, bar in (("negate", a, 0), ("abs", a, 0), ("log", pos, 2), ("exponential", small, 2),
+                         ("tanh", small, 2)):
+        s = W.Spec()
+        x = s.parameter(0, "f32", [n])
+        s.unary(op, x, "f32", [n])
+        got, _ = run_gpu(s.nodes, [arr])
+        want = oracle.evaluate(s.nodes, [arr])
+        if bar == 0:
+            assert_bitexact(got, want, "f32")
+        else:
+            assert_ulp(got, want, "f32", bar)
+
+
 # --------------------------------------------------------------------------
 # f16 and u8 element types
 # --------------------------------------------------------------------------

@@ -209,6 +209,26 @@ def test_f32_add_mul_match_ieee_float32():
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), op
 
 
+def test_negate_abs_minimum_maximum_match_numpy():
+    """negate and abs are exact sign operations; minimum and maximum of
+    nonzero, non-NaN operands pick an operand (signed zeros and NaN are in the
+    special-value test)."""
+    g = rng(12)
+    a = (g.standard_normal(20000) * np.exp2(g.integers(-140, 100, 20000))).astype(np.float32)
+    b = (g.standard_normal(20000) * np.exp2(g.integers(-140, 100, 20000))).astype(np.float32)
+    for op, ref in (("negate", -a), ("abs", np.abs(a))):
+        s = Spec()
+        x = s.parameter(0, "f32", [a.size])
+        s.unary(op, x, "f32", [a.size])
+        assert np.array_equal(ev(s, [a]).view(np.uint32), ref.view(np.uint32)), op
+    for op, ref in (("minimum", np.minimum(a, b)), ("maximum", np.maximum(a, b))):
+        s = Spec()
+        x = s.parameter(0, "f32", [a.size])
+        y = s.parameter(1, "f32", [a.size])
+        s.binary(op, x, y, "f32", [a.size])
+        assert np.array_equal(ev(s, [a, b]).view(np.uint32), ref.view(np.uint32)), op
+
+
 def test_convert_s32_to_f32_and_rounding():
     g = GOLD["convert_s32_f32"]
     s = Spec()
@@ -808,13 +828,14 @@ def test_evaluate_points_matches_whole():
 
 
 def test_exp_log_f32_correctly_rounded_sample():
-    """f32 exp and log are correctly rounded: equal to numpy's float64 result
+    """f32 exp, log and tanh are correctly rounded: equal to numpy's float64 result
     rounded to f32 wherever that f64 value is not within 1e-12 (relative) of
     an f32 rounding boundary."""
     g = rng(19)
     for op, x, ref in (
         ("exponential", g.uniform(-87, 88, 100000).astype(np.float32), np.exp),
         ("log", np.exp2(g.uniform(-140, 127, 100000)).astype(np.float32), np.log),
+        ("tanh", (g.standard_normal(100000) * np.exp2(g.integers(-12, 3, 100000))).astype(np.float32), np.tanh),
     ):
         s = Spec()
         p = s.parameter(0, "f32", [x.size])
