@@ -1,6 +1,8 @@
 // plan.cpp -- hero selection, index-map propagation, partitioning, geometry.
 #include "plan.h"
 
+#include <cctype>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
@@ -53,7 +55,23 @@ int phys_minor(const Type &t) {
   return -1;
 }
 
-Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general) {
+namespace {
+// Whether index term t moves with the lane variable (lane < 0: assume it does).
+bool moves_with_lane(const Term &t, int lane) {
+  if (lane < 0) return true;
+  if (t.k == Term::VAR) return t.var == lane;
+  if (t.k != Term::EXPR) return false;
+  const std::string v = "i" + std::to_string(lane);
+  for (size_t p = t.e.find(v); p != std::string::npos; p = t.e.find(v, p + 1)) {
+    const size_t e = p + v.size();
+    if ((p == 0 || !std::isalnum((unsigned char)t.e[p - 1])) && (e >= t.e.size() || !std::isdigit((unsigned char)t.e[e])))
+      return true;
+  }
+  return false;
+}
+}  // namespace
+
+Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general, int lane) {
   const Node &nd = g.nodes[n];
   const Type &ot = g.nodes[nd.opd[k]].t;
   auto expr = [](const std::string &e) {
@@ -69,7 +87,7 @@ Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general)
       for (int64_t d : nd.attr)
         if (nd.t.dims[d] > 1) {
           O[d] = expr("(" + std::to_string(nd.t.dims[d] - 1) + " - (" + term_str(E[d]) + "))");
-          *general = true;
+          if (moves_with_lane(E[d], lane)) *general = true;
         }
       return O;
     }
@@ -85,7 +103,7 @@ Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general)
         if (lo == 0 && hi == 0 && step == 1) continue;
         O[d] = expr("hf_clampi((" + term_str(E[d]) + " - (" + std::to_string(lo) + ")) / " + std::to_string(step) +
                     ", 0, " + std::to_string(std::max<long long>(ot.dims[d] - 1, 0)) + ")");
-        *general = true;
+        if (moves_with_lane(E[d], lane)) *general = true;
       }
       return O;
     }
@@ -98,7 +116,7 @@ Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general)
       Index O = E;
       O[cd] = expr("hf_clampi(" + term_str(E[cd]) + " - " + std::to_string(off) + ", 0, " +
                    std::to_string(std::max<long long>(ot.dims[cd] - 1, 0)) + ")");
-      *general = true;
+      if (moves_with_lane(E[cd], lane)) *general = true;
       return O;
     }
     case HF_TRANSPOSE: {
@@ -161,7 +179,8 @@ void visit(const Graph &g, Ctx &c, int n, const Index &E) {
     return;
   }
   if (nd.op == HF_CONSTANT) return;
-  for (size_t k = 0; k < nd.opd.size(); ++k) visit(g, c, nd.opd[k], operand_index(g, n, (int)k, E, &c.general));
+  for (size_t k = 0; k < nd.opd.size(); ++k)
+    visit(g, c, nd.opd[k], operand_index(g, n, (int)k, E, &c.general, c.lane));
 }
 
 // Partitioning (XLA:GPU Emitters, "Partitioning").  A node with one user is
@@ -252,7 +271,10 @@ Access classify(const Graph &g, int p, const Index &E, int lane) {
   int at = -1;
   for (int d = 0; d < t.rank; ++d) {
     if (E[d].k == Term::VAR && E[d].var == lane) at = d;
-    if (E[d].k == Term::EXPR) return GATHER;
+    // an expression index that moves with the lane (a div/mod reshape, a
+    // reversed or padded lane dim) reads a gather; one that does not (a
+    // reversed row dim) leaves the lane's accesses as they are
+    if (E[d].k == Term::EXPR && moves_with_lane(E[d], lane)) return GATHER;
   }
   if (at < 0) return UNIFORM;
   return at == phys_minor(t) ? CONTIG : STRIDED;
@@ -389,15 +411,19 @@ Plan plan_loop(const Graph &g, Ctx c) {
 bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
   const Type &rt = g.nodes[g.root].t;
   int lout = loop.lane;
-  if (lout < 0 || loop.general) return false;
+  if (lout < 0) return false;
   int lin = -1;
   bool any = false;
+  // A large parameter whose contiguous dim is read with a plain variable other
+  // than the output's minor one is read transposed.  (Whether the load and
+  // store phases can then run 128-bit lanes is checked on their own contexts
+  // below.)
   for (auto &pr : loop.param_reads) {
     if (!large(g, pr.first)) continue;
-    if (classify(g, pr.first, pr.second, lout) == GATHER) return false;
     int pm = phys_minor(g.nodes[pr.first].t);
     if (pm < 0) continue;
     const Term &t = pr.second[pm];
+    if (t.k == Term::EXPR) return false;
     if (t.k != Term::VAR || t.var == lout) continue;
     if (lin >= 0 && lin != t.var) return false;  // two different transposed directions
     lin = t.var;

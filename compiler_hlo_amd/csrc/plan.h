@@ -26,10 +26,11 @@ std::string index_key(const Index &E);
 Index identity_index(int rank);
 
 // Output-to-input index map of operand `k` of node `n` read at E
-// (XLA:GPU Emitters, "Indexing transforms").  Sets *general when the map is
-// not a plain renaming of variables (a div/mod reshape, reverse, pad,
-// concatenate): such a context runs one element per lane.
-Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general);
+// (XLA:GPU Emitters, "Indexing transforms").  Sets *general when the map
+// changes how the lane variable `lane` moves through memory (a div/mod
+// reshape; reverse, pad or concatenate of the lane's dim; lane < 0: of any
+// dim): such a context runs one element per lane.
+Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general, int lane = -1);
 
 // Physical stride (in elements) of every logical dim of t.
 std::vector<long long> phys_strides(const Type &t);

@@ -544,6 +544,31 @@ def test_index_transforms_composed():
     assert_bitexact(got, oracle.evaluate(s.nodes, [x, y]), "f32")
 
 
+def test_index_transforms_on_major_dims_vectorize():
+    """pad, reverse and concatenate along the major dim leave the lane dim
+    alone: the loop keeps 128-bit lanes, and a reverse inside a transpose's
+    prologue keeps the transpose hero.  Bit-exact."""
+    spec, params, _ = W.pad_reverse_concat_f32(300, 520, 77)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "loop" and f.plan()["vector_elems"] == 4
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "f32")
+    spec, params, _ = W.pad_reverse_concat_f32()
+    got, f = run_gpu(spec.nodes, params)
+    g = W.rng(83)
+    pts = np.stack([g.integers(0, 6146, 20000), g.integers(0, 4096, 20000)], 1)
+    pts = np.concatenate([pts, [[0, 0], [1, 5], [4096, 7], [4097, 4095], [4098, 0], [6145, 4095]]])
+    want, _ = oracle.evaluate_points(spec.nodes, params, pts)
+    assert_bitexact(got[pts[:, 0] * 4096 + pts[:, 1]], want.astype(np.float32), "f32")
+    s = W.Spec()
+    x = s.parameter(0, "f32", [1000, 1536])
+    r = s.reverse(x, [0], "f32", [1000, 1536])
+    s.transpose(r, [1, 0], "f32", [1536, 1000])
+    xs = W.normal_f32(g, 1000 * 1536)
+    got, f = run_gpu(s.nodes, [xs])
+    assert f.plan()["hero"] == "transpose"
+    assert_bitexact(got, oracle.evaluate(s.nodes, [xs]), "f32")
+
+
 # --------------------------------------------------------------------------
 # elementwise epilogues after a reduce
 # --------------------------------------------------------------------------

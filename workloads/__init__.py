@@ -250,6 +250,57 @@ def transpose3d_exp_abs(d0=20, d1=160, d2=170, seed=8):
     return s, [normal_f32(g, n)], {"name": "transpose3d_exp_abs", "elements": n, "bytes": 8 * n}
 
 
+def pad_reverse_concat_f32(n0=4096, n1=4096, m0=2048, seed=9):
+    """out = concatenate([pad(x, low [1,0], high [1,0]), reverse(y, {0})], 0)
+    with x f32[n0,n1], y f32[m0,n1] ~ N(0,1): index transforms along the major
+    dim (StableHLO Specification: pad, reverse, concatenate)."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [n0, n1])
+    y = s.parameter(1, "f32", [m0, n1])
+    z = s.constant(0.0, "f32", [])
+    p = s.pad(x, z, [1, 0], [1, 0], [0, 0], "f32", [n0 + 2, n1])
+    r = s.reverse(y, [0], "f32", [m0, n1])
+    s.concatenate([p, r], 0, "f32", [n0 + 2 + m0, n1])
+    return s, [normal_f32(g, n0 * n1), normal_f32(g, m0 * n1)], {
+        "name": "pad_reverse_concat_f32", "elements": (n0 + 2 + m0) * n1,
+        "bytes": 4 * (n0 * n1 + m0 * n1 + (n0 + 2 + m0) * n1)}
+
+
+def quantized_add_i8(r=4096, c=4096, seed=10):
+    """out = add(a, b) on per-tensor quantized i8[r,c] tensors (scales 0.05 and
+    0.02, zero points 3 and -7), quantized to scale 0.04, zero point 1."""
+    g = rng(seed)
+    s = Spec()
+    a = s.parameter(0, "s8", [r, c], quant=quant_type("s8", [0.05], [3]))
+    b = s.parameter(1, "s8", [r, c], quant=quant_type("s8", [0.02], [-7]))
+    s.op("add", [a, b], "s8", [r, c], quant=quant_type("s8", [0.04], [1]))
+    return s, [integers(g, r * c, -128, 127, np.int8), integers(g, r * c, -128, 127, np.int8)], {
+        "name": "quantized_add_i8", "elements": r * c, "bytes": 3 * r * c}
+
+
+def row_mean_f32(r=16384, c=4096, seed=11):
+    """out f32[r] = reduce-sum over dim 1 of x f32[r,c] ~ N(0,1), divided by c:
+    a reduce with an elementwise epilogue."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [r, c])
+    m = s.reduce(x, [1], "add", 0.0, "f32", [r])
+    n = s.constant(float(c), "f32", [r])
+    s.binary("divide", m, n, "f32", [r])
+    return s, [normal_f32(g, r * c)], {"name": "row_mean_f32", "elements": r * c, "bytes": 4 * r * c + 4 * r}
+
+
+def argmax_rows_bf16(r=8192, c=8192, seed=12):
+    """out s32[r] = argmax over dim 1 of x bf16[r,c] ~ N(0,1) (the variadic
+    max/argmax reduce with an iota index operand)."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "bf16", [r, c])
+    s.argmax(x, 1, [r, c])
+    return s, [normal_bf16(g, r * c)], {"name": "argmax_rows_bf16", "elements": r * c, "bytes": 2 * r * c + 4 * r}
+
+
 def gelu_bf16(d0=6, d1=512, d2=4096, seed=7):
     """The GELU loop fusion in bf16 (tanh form), every op rounding to bf16."""
     g = rng(seed)
