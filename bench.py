@@ -106,6 +106,11 @@ def workload_makers():
         "quant_dequant_bias_requant": (W.quant_dequant_bias_requant, {}, None),
         "loop_log_transpose_add": (W.loop_log_transpose_add, {}, None),
         "gelu_bf16": (W.gelu_bf16, {}, None),
+        "transpose3d_exp_abs": (W.transpose3d_exp_abs, {}, None),
+        "pad_reverse_concat_f32": (W.pad_reverse_concat_f32, {}, None),
+        "quantized_add_i8": (W.quantized_add_i8, {}, None),
+        "row_mean_f32": (W.row_mean_f32, {}, None),
+        "argmax_rows_bf16": (W.argmax_rows_bf16, {}, None),
         "copy_f32_4096x4096": (copy_case("f32", [4096, 4096]), {}, None),
         "copy_bf16_64x512x1024": (copy_case("bf16", [64, 512, 1024]), {}, None),
     }
@@ -299,7 +304,8 @@ def main():
         makers = workload_makers()
         others = ["copy_f32_4096x4096", "copy_bf16_64x512x1024", "loop_log_transpose_add",
                   "row_reduce_exp_add_bf16", "column_reduce_max_f32", "column_reduce_max_f32_colmajor",
-                  "quant_dequant_bias_requant", "gelu_bf16"]
+                  "quant_dequant_bias_requant", "gelu_bf16", "transpose3d_exp_abs", "pad_reverse_concat_f32",
+                  "quantized_add_i8", "row_mean_f32", "argmax_rows_bf16"]
         for key in others:
             mk, kw, tr = makers[key]
             c = Case(mk, kwargs=kw, transform=tr)

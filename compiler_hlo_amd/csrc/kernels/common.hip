@@ -137,6 +137,29 @@ __device__ __forceinline__ void hf_arg_combine(float &m, int &k, float m2, int k
     k = k2;
   }
 }
+// A whole wave's pairs by the DPP pattern of hf_wave_reduce; the result is
+// returned in every lane.  Every lane must be active.
+__device__ __forceinline__ void hf_arg_wave_reduce(float &m, int &k) {
+#define HF_ARG_DPP(ctrl)                                                        \
+  {                                                                            \
+    const float m2 = HF_DPP(m, ctrl);                                          \
+    const int k2 = __builtin_amdgcn_update_dpp(0, k, (ctrl), 0xF, 0xF, false); \
+    hf_arg_combine(m, k, m2, k2);                                              \
+  }
+  HF_ARG_DPP(0xB1)   // quad_perm [1,0,3,2]
+  HF_ARG_DPP(0x4E)   // quad_perm [2,3,0,1]
+  HF_ARG_DPP(0x124)  // row_ror:4
+  HF_ARG_DPP(0x128)  // row_ror:8
+#undef HF_ARG_DPP
+  float mr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+  int kr = __builtin_amdgcn_readlane(k, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16)
+    hf_arg_combine(mr, kr, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), r)),
+                   __builtin_amdgcn_readlane(k, r));
+  m = mr;
+  k = kr;
+}
 template <int W>  // across groups of W lanes (W a power of two <= 64)
 __device__ __forceinline__ void hf_arg_group_reduce(float &m, int &k) {
 #pragma unroll

@@ -32,16 +32,31 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     float m = HF_ARG_V0;
     int k = HF_ARG_K0;
     if (row < HF_ROWS) {
-      for (int kv = sub; kv < HF_KV; kv += HF_TPR) {
-        hf_regs_t R1;
-        hf_rr_eval_fetch(A, row, kv, R1);
-        float x[HF_V];
-        hf_rr_eval(A, row, kv, R1, x);
+      // the row's chunks in batches of up to 8 per thread, loads first
+      constexpr int IT = (HF_KV + HF_TPR - 1) / HF_TPR;
+      constexpr int NB = IT < 8 ? (IT > 0 ? IT : 1) : 8;
+      for (int it0 = 0; it0 < IT; it0 += NB) {
+        hf_regs_t R[NB];
 #pragma unroll
-        for (int v = 0; v < HF_V; ++v) hf_arg_step(m, k, x[v], kv * HF_V + v);
+        for (int b = 0; b < NB; ++b) {
+          const int kv = (it0 + b) * HF_TPR + sub;
+          if (kv < HF_KV) hf_rr_eval_fetch(A, row, kv, R[b]);
+        }
+        HF_LOADS_ISSUED();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int kv = (it0 + b) * HF_TPR + sub;
+          if (kv < HF_KV) {
+            float x[HF_V];
+            hf_rr_eval(A, row, kv, R[b], x);
+#pragma unroll
+            for (int v = 0; v < HF_V; ++v) hf_arg_step(m, k, x[v], kv * HF_V + v);
+          }
+        }
       }
     }
-    hf_arg_group_reduce<GW>(m, k);
+    if constexpr (GW == 64) hf_arg_wave_reduce(m, k);
+    else hf_arg_group_reduce<GW>(m, k);
     if (HF_TPR > 64) {  // one row per workgroup: combine the waves through LDS
       const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
       if (lane == 0) {
@@ -91,29 +106,32 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     }
   };
   if constexpr (HF_KV % HF_BLOCK == 0) {
-    hf_regs_t R[ITERS];
-    auto fetch = [&](int row, hf_regs_t (&Rb)[ITERS]) {
-#pragma unroll
-      for (int it = 0; it < ITERS; ++it) hf_rr_eval_fetch(A, row, it * HF_BLOCK + (int)threadIdx.x, Rb[it]);
-    };
-    auto reduce_row = [&](int row, const hf_regs_t (&Rb)[ITERS], int slot) {
+    // a row's chunks in batches of up to 8 per thread, each batch's loads
+    // issued before its accumulation
+    constexpr int NB = ITERS < 8 ? ITERS : 8;
+    int slot = 0;
+    for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
       float acc[NX];
 #pragma unroll
       for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
+      for (int it0 = 0; it0 < ITERS; it0 += NB) {
+        hf_regs_t R[NB];
 #pragma unroll
-      for (int it = 0; it < ITERS; ++it) {
-        xval_t x[NX];
-        hf_rr_eval(A, row, it * HF_BLOCK + (int)threadIdx.x, Rb[it], x);
+        for (int b = 0; b < NB; ++b)
+          if (ITERS % NB == 0 || it0 + b < ITERS)
+            hf_rr_eval_fetch(A, row, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[b]);
+        HF_LOADS_ISSUED();
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+        for (int b = 0; b < NB; ++b) {
+          if (ITERS % NB == 0 || it0 + b < ITERS) {
+            xval_t x[NX];
+            hf_rr_eval(A, row, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[b], x);
+#pragma unroll
+            for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+          }
+        }
       }
       finish(row, acc, slot);
-    };
-    int slot = 0;
-    for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
-      fetch(row, R);
-      HF_LOADS_ISSUED();
-      reduce_row(row, R, slot);
     }
   } else {
     int slot = 0;

@@ -375,6 +375,23 @@ def test_u8_quantize_dequantize():
 # --------------------------------------------------------------------------
 # variadic max/argmax
 # --------------------------------------------------------------------------
+def test_long_rows():
+    """Rows of 2^20 elements (512 chunks per thread, fetched in batches):
+    an integer-valued sum (exact in any order) and an argmax."""
+    g = W.rng(112)
+    x = W.integers(g, 4 << 20, -3, 3, np.int64).astype(np.float32)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4, 1 << 20])
+    s.reduce(p, [1], "add", 0.0, "f32", [4])
+    got, _ = run_gpu(s.nodes, [x])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4, 1 << 20])
+    s.argmax(p, 1, [4, 1 << 20])
+    got, _ = run_gpu(s.nodes, [x])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32")
+
+
 @pytest.mark.parametrize("dims,rdim,dtype", [([64, 3000], 1, "f32"), ([3000, 64], 0, "f32"),
                                              ([16384, 512], 0, "f32"), ([100, 40], 1, "bf16"),
                                              ([7, 5], 1, "f32"), ([10240, 2048], 1, "bf16")])
