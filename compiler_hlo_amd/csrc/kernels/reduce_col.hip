@@ -156,8 +156,20 @@ extern "C" __global__ __launch_bounds__(256) void HF_FOLD_NAME(HF_KERNEL_PARAMS)
   const float *ws = (const float *)A.ws;
   float s = hf_red_identity<HF_OP>();
   if (col < HF_C) {
-#pragma unroll 8
-    for (int k = wave; k < HF_S; k += 4) s = hf_red<HF_OP>(s, ws[(long)k * HF_C + col]);
+    // the wave's segments k = wave, wave + 4, ...: up to 32 loads in flight,
+    // then combined in segment order
+    constexpr int NK = (HF_S + 3) / 4;
+    constexpr int NB = NK < 32 ? NK : 32;
+    for (int i0 = 0; i0 < NK; i0 += NB) {
+      float t[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int k = wave + 4 * (i0 + i);
+        t[i] = k < HF_S ? ws[(long)k * HF_C + col] : hf_red_identity<HF_OP>();
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) s = hf_red<HF_OP>(s, t[i]);
+    }
   }
   part[wave][lane] = s;
   __syncthreads();
