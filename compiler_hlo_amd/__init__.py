@@ -111,6 +111,11 @@ def _load():
         raise ImportError(
             "compiler_hlo_amd: %s is missing; build it with `python compiler_hlo_amd/build.py` "
             "(there is no fallback implementation)" % _LIB_PATH)
+    # PyTorch ships its own HIP runtime under the same soname as the system's.
+    # Loaded first, it serves this library too; loaded after the system one,
+    # the process would hold two HIP runtimes, and whichever initialises
+    # second finds no device.  So torch is imported before the library.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     lib.hf_fusion_create.restype = ctypes.c_int
     lib.hf_fusion_create.argtypes = [ctypes.POINTER(HfFusionDesc), ctypes.c_uint32,

@@ -88,6 +88,10 @@ class Gen {
   Gen(const Graph &g, Plan &P) : g_(g), P_(P) {
     const char *nt = std::getenv("HF_NT");  // tuning knob: bit 0 loads, bit 1 stores
     nt_loads_ = nt ? (std::atoi(nt) & 1) : true;
+    // A hero that keeps the next step's loads in flight while it computes
+    // needs every load of a step in its fetch phase, small arrays included.
+    for (auto &m : P.macros)
+      if (m.first == "HF_RR_PIPE" && m.second) fetch_all_ = true;
   }
 
   // Emits (once) the struct, fetch and compute functions of the partition
@@ -172,10 +176,11 @@ class Gen {
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     std::vector<long long> st = phys_strides(t);
     b.os << "  " << reg << " " << v << "[" << V << "];\n";
-    std::string m = stream ? "R." + member(b) : "w" + std::to_string(b.tmp++);
-    std::ostringstream &ld_os = stream ? b.fetch : b.os;
+    const bool in_fetch = stream || fetch_all_;
+    std::string m = in_fetch ? "R." + member(b) : "w" + std::to_string(b.tmp++);
+    std::ostringstream &ld_os = in_fetch ? b.fetch : b.os;
     auto decl = [&](const std::string &type, int count) {
-      if (stream) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
+      if (in_fetch) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
       else b.os << "  " << type << " " << m << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
     };
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
@@ -412,6 +417,7 @@ class Gen {
   const Graph &g_;
   Plan &P_;
   bool nt_loads_ = true;
+  bool fetch_all_ = false;
   std::ostringstream defs_;
   std::map<std::string, bool> done_;
 };

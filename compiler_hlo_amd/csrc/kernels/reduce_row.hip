@@ -86,70 +86,161 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
   auto acc_add = [](float a, float x) { return hf_red<HF_OP>(a, x); };
 #endif
 #if HF_TPR == HF_BLOCK
-  // Two result slots, alternating between a workgroup's consecutive rows, so
-  // that one barrier per row is enough.
-  __shared__ float part[2][HF_BLOCK / 64];
+  // Two result slots, alternating between a workgroup's consecutive steps, so
+  // that one barrier per step is enough.
+  constexpr int RR = HF_RR_ROWS;
+  __shared__ float part[2][RR][HF_BLOCK / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ITERS = (HF_KV + HF_BLOCK - 1) / HF_BLOCK;
-  auto finish = [&](int row, const float (&acc)[NX], int slot) {
-    float s = acc[0];
+  // acc[r] holds row row0 + r; rows past the end are neither read nor stored
+  auto finish = [&](int row0, const float (&acc)[RR][NX], int slot) {
 #pragma unroll
-    for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
-    s = hf_wave_reduce<HF_OP>(s);
-    if (lane == 0) part[slot][wave] = s;
+    for (int r = 0; r < RR; ++r) {
+      float s = acc[r][0];
+#pragma unroll
+      for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[r][v]);
+      s = hf_wave_reduce<HF_OP>(s);
+      if (lane == 0) part[slot][r][wave] = s;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = part[slot][0];
+    if (threadIdx.x < RR && row0 + (int)threadIdx.x < HF_ROWS) {
+      const int r = threadIdx.x;
+      float t = part[slot][r][0];
 #pragma unroll
-      for (int w = 1; w < HF_BLOCK / 64; ++w) t = hf_red<HF_OP>(t, part[slot][w]);
-      hf_rr_store(A, row, t);
+      for (int w = 1; w < HF_BLOCK / 64; ++w) t = hf_red<HF_OP>(t, part[slot][r][w]);
+      hf_rr_store(A, row0 + r, t);
     }
   };
-  if constexpr (HF_KV % HF_BLOCK == 0) {
-    // a row's chunks in batches of up to 8 per thread, each batch's loads
-    // issued before its accumulation
-    constexpr int NB = ITERS < 8 ? ITERS : 8;
+#if HF_RR_PIPE
+  {
+    // Two rows in flight per workgroup: the loads of row + gridDim.x are
+    // issued before row is accumulated.  Unrolled by two, so that the two
+    // register sets swap roles without copies.  The loop holds no global
+    // store (on this target stores and loads share one counter, and a
+    // pending store would make every wait a full drain): the workgroup's
+    // row results (at most HF_RR_PIPE_K) collect in LDS and are stored after
+    // the last row.
+    static_assert(RR == 1 && HF_KV % HF_BLOCK == 0 && ITERS <= 8, "pipelined rows take one batch each");
+    __shared__ float res[HF_RR_PIPE_K];
+    hf_regs_t R0[ITERS], R1[ITERS];
+    auto fetch = [&](int row, hf_regs_t(&R)[ITERS]) {
+#pragma unroll
+      for (int b = 0; b < ITERS; ++b) hf_rr_eval_fetch(A, row, b * HF_BLOCK + (int)threadIdx.x, R[b]);
+    };
+    auto consume = [&](int row, int k, const hf_regs_t(&R)[ITERS], int slot) {
+      float s = hf_red_identity<HF_OP>();
+      {
+        xval_t x[NX];
+        hf_rr_eval(A, row, (int)threadIdx.x, R[0], x);
+        float acc[NX];
+#pragma unroll
+        for (int v = 0; v < NX; ++v) acc[v] = acc_add(hf_red_identity<HF_OP>(), x[v]);
+#pragma unroll
+        for (int b = 1; b < ITERS; ++b) {
+          hf_rr_eval(A, row, b * HF_BLOCK + (int)threadIdx.x, R[b], x);
+#pragma unroll
+          for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+        }
+        s = acc[0];
+#pragma unroll
+        for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
+      }
+      s = hf_wave_reduce<HF_OP>(s);
+      if (lane == 0) part[slot][0][wave] = s;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float t = part[slot][0][0];
+#pragma unroll
+        for (int w = 1; w < HF_BLOCK / 64; ++w) t = hf_red<HF_OP>(t, part[slot][0][w]);
+        res[k] = t;
+      }
+    };
+    // Every fetch inside the loop is unconditional (the next row is known to
+    // exist), so that each wait counts only the other register set's loads;
+    // the last row is accumulated on the way out.
+    int row = blockIdx.x, k = 0;
+    if (row < HF_ROWS) {
+      fetch(row, R0);
+      for (;;) {
+        if (row + (int)gridDim.x >= HF_ROWS) {
+          consume(row, k++, R0, 0);
+          break;
+        }
+        fetch(row + gridDim.x, R1);
+        HF_LOADS_ISSUED();
+        consume(row, k++, R0, 0);
+        row += gridDim.x;
+        if (row + (int)gridDim.x >= HF_ROWS) {
+          consume(row, k++, R1, 1);
+          break;
+        }
+        fetch(row + gridDim.x, R0);
+        HF_LOADS_ISSUED();
+        consume(row, k++, R1, 1);
+        row += gridDim.x;
+      }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < k; j += HF_BLOCK) hf_rr_store(A, blockIdx.x + j * gridDim.x, res[j]);
+  }
+#elif HF_KV % HF_BLOCK == 0
+  {
+    // RR rows per step; their chunks in batches of up to 8 loads per thread,
+    // each batch's loads issued before its accumulation
+    constexpr int NB0 = 8 / RR > 0 ? 8 / RR : 1;
+    constexpr int NB = ITERS < NB0 ? ITERS : NB0;
     int slot = 0;
-    for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
-      float acc[NX];
+    for (int row0 = blockIdx.x * RR; row0 < HF_ROWS; row0 += gridDim.x * RR, slot ^= 1) {
+      float acc[RR][NX];
 #pragma unroll
-      for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
+      for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int v = 0; v < NX; ++v) acc[r][v] = hf_red_identity<HF_OP>();
       for (int it0 = 0; it0 < ITERS; it0 += NB) {
-        hf_regs_t R[NB];
+        hf_regs_t R[RR][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (ITERS % NB == 0 || it0 + b < ITERS)
-            hf_rr_eval_fetch(A, row, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[b]);
+        for (int r = 0; r < RR; ++r)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            if ((RR == 1 || row0 + r < HF_ROWS) && (ITERS % NB == 0 || it0 + b < ITERS))
+              hf_rr_eval_fetch(A, row0 + r, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[r][b]);
         HF_LOADS_ISSUED();
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          if (ITERS % NB == 0 || it0 + b < ITERS) {
-            xval_t x[NX];
-            hf_rr_eval(A, row, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[b], x);
 #pragma unroll
-            for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+          for (int r = 0; r < RR; ++r) {
+            if ((RR == 1 || row0 + r < HF_ROWS) && (ITERS % NB == 0 || it0 + b < ITERS)) {
+              xval_t x[NX];
+              hf_rr_eval(A, row0 + r, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[r][b], x);
+#pragma unroll
+              for (int v = 0; v < NX; ++v) acc[r][v] = acc_add(acc[r][v], x[v]);
+            }
           }
         }
       }
-      finish(row, acc, slot);
+      finish(row0, acc, slot);
     }
-  } else {
+  }
+#else
+  {
+    static_assert(RR == 1, "rows of unequal chunks take one row per step");
     int slot = 0;
     for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
-      float acc[NX];
+      float acc[1][NX];
 #pragma unroll
-      for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
+      for (int v = 0; v < NX; ++v) acc[0][v] = hf_red_identity<HF_OP>();
       for (int kv = threadIdx.x; kv < HF_KV; kv += HF_BLOCK) {
         hf_regs_t R1;
         hf_rr_eval_fetch(A, row, kv, R1);
         xval_t x[NX];
         hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+        for (int v = 0; v < NX; ++v) acc[0][v] = acc_add(acc[0][v], x[v]);
       }
       finish(row, acc, slot);
     }
   }
+#endif
 #else
   constexpr int RPB = HF_BLOCK / HF_TPR;
   const int sub = threadIdx.x % HF_TPR;

@@ -586,12 +586,26 @@ Plan plan_reduce(const Graph &g) {
       tpr = pow2_ceil(std::max<long long>(1, kv));
     }
     long long rpb = tpr == block ? 1 : block / tpr;
+    // Whole-row workgroups whose rows split into equal chunks take several
+    // rows per step: their loads go out together, and what the prologue reads
+    // along the row (a broadcast bias) is loaded once for all of them.
+    // Two rows per step for rows of eight or more chunks per thread (measured
+    // faster there; shorter rows gained nothing or lost).
+    long long rr = 1;
+    if (tpr == block && kv % block == 0 && op != HF_REDUCER_ARGMAX)
+      rr = std::max<long long>(1, std::min<long long>(env_ll("HF_ROW_RPS", kv / block >= 8 ? 2 : 1), 4));
+    long long pipe = 0;
+    if (rr == 1 && tpr == block && kv % block == 0 && kv / block <= 8 && op != HF_REDUCER_ARGMAX)
+      pipe = env_ll("HF_ROW_PIPE", 0) ? 1 : 0;
     long long target = env_ll("HF_ROW_WGS", 8192);
-    P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb), target));
+    P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb * rr), target));
+    const long long pipe_k = ceil_div(J, P.grid);  // rows per workgroup
+    if (pipe_k > 1024) pipe = 0;
     P.block = block;
-    P.lds_bytes = tpr == block ? (block / 64) * 8 : 0;
+    P.lds_bytes = tpr == block ? (block / 64) * 8 * (int)rr : 0;
     P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", J},
-                {"HF_KV", kv}, {"HF_TPR", tpr}};
+                {"HF_KV", kv}, {"HF_TPR", tpr}, {"HF_RR_ROWS", rr}, {"HF_RR_PIPE", pipe},
+                {"HF_RR_PIPE_K", std::max<long long>(1, pipe_k)}};
     P.info.vector_elems = V;
     P.info.rows = J;
     P.info.cols = K;
