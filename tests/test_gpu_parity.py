@@ -200,6 +200,48 @@ def test_row_reduce_full_sampled_and_layout_invariant():
     assert np.array_equal(got.view(np.uint32), got2.view(np.uint32))
 
 
+@pytest.mark.parametrize("d0,d2,d3", [(1, 5, 32768), (3, 3, 36864)])
+def test_row_reduce_two_rows_per_step(d0, d2, d3):
+    """Rows of eight or more chunks per thread are reduced two per workgroup
+    step: odd row counts leave one row in the last step, and 36864 (nine
+    chunks) leaves a partial batch of loads."""
+    say("row reduce two rows per step", d0, d2, d3)
+    spec, params, _ = W.row_reduce_exp_add_bf16(d0, d2, d3, seed=50 + d2)
+    got, f = run_gpu(spec.nodes, params)
+    assert "#define HF_RR_ROWS 2" in f.source()
+    _check_sum(got, spec, params, [[a, 0, c] for a in range(d0) for c in range(d2)])
+    g = W.rng(51)
+    for rows, cols, red in ((37, 16384, "max"), (7, 20480, "add")):
+        x = W.integers(g, rows * cols, -1000, 1000, np.int64).astype(np.float32)  # exact sums
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, cols])
+        s.reduce(p, [1], red, float("-inf") if red == "max" else 0.0, "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        assert "#define HF_RR_ROWS 2" in f.source()
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
+def test_row_reduce_pipelined_option(monkeypatch):
+    """The optional pipelined row path (next row's loads in flight while the
+    current one is accumulated; results stored after the loop), on a grid of
+    5 workgroups so that they take different, odd and even, row counts."""
+    monkeypatch.setenv("HF_ROW_PIPE", "1")
+    monkeypatch.setenv("HF_ROW_WGS", "5")
+    spec, params, _ = W.row_reduce_exp_add_bf16(3, 7, 16384, seed=52)
+    got, f = run_gpu(spec.nodes, params)
+    assert "#define HF_RR_PIPE 1" in f.source() and f.plan()["grid_blocks"] == 5
+    _check_sum(got, spec, params, [[a, 0, c] for a in range(3) for c in range(7)])
+    g = W.rng(53)
+    for rows in (23, 4, 1):
+        x = W.normal_f32(g, rows * 4096)
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, 4096])
+        s.reduce(p, [1], "max", float("-inf"), "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        assert "#define HF_RR_PIPE 1" in f.source()
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
 def test_row_reduce_bf16_intermediates_loop():
     """The reduce operand y = add(exp x, b) itself (a bf16 loop fusion) is
     within 1 bf16 ulp of the oracle elementwise."""
