@@ -175,14 +175,36 @@ def write_traffic(pmc_root, names):
     log("wrote", path)
 
 
-def time_cases(cases, steps, warmup):
-    """Time `steps` steps; a step launches every case once.  Inside the timed
-    region the launches are grouped by case (all of case 0, then all of case
-    1, ...) with one HIP event pair around each group on the launch stream, so
-    the per-case average launch time carries no per-launch event overhead.
-    Returns (wall seconds per step, [mean seconds per launch of each case])."""
+SETTLE_SECONDS = 0.25
+
+
+def settle(cases, seconds=SETTLE_SECONDS):
+    """Run the cases, untimed, for `seconds` of wall time.  After an idle gap
+    (a kernel compile, a host-side step) the GPU's clocks take a few tens of
+    milliseconds of load to return to their sustained level: measured on C3,
+    the first ~25 ms of launches ran 10-30% slower.  A timing that starts cold
+    measures that ramp instead of the kernel."""
     import torch
     stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            for c in cases:
+                c.launch(stream)
+        torch.cuda.synchronize()
+
+
+def time_cases(cases, steps, warmup):
+    """Time `steps` steps; a step launches every case once.  Before the
+    `warmup` steps the cases run for SETTLE_SECONDS (see settle).  Inside the
+    timed region the launches are grouped by case (all of case 0, then all of
+    case 1, ...) with one HIP event pair around each group on the launch
+    stream, so the per-case average launch time carries no per-launch event
+    overhead.  Returns (wall seconds per step, [mean seconds per launch of
+    each case])."""
+    import torch
+    stream = torch.cuda.current_stream()
+    settle(cases)
     for _ in range(warmup):
         for c in cases:
             c.launch(stream)
