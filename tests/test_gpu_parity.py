@@ -111,6 +111,37 @@ def test_transpose_exp_small(n0, n1):
     assert_ulp(got, want, "f32", 2)
 
 
+@pytest.mark.parametrize("dims,perm,tile,block", [([100, 2048], [1, 0], (128, 32), 1024),
+                                                  ([3, 36, 4096], [0, 2, 1], (128, 32), 1024),
+                                                  ([8, 2048], [1, 0], (128, 8), 256)])
+def test_transpose_narrow_tiles(dims, perm, tile, block):
+    """f32 transposes whose input rows lie a power of two (>= 8 KiB) apart take
+    tiles 128 wide in the load and up to 32 in the store, with 1024 threads
+    when each thread then moves one vector per phase.  Ragged U extents (100,
+    36) take the bounds-checked path.  The exp before the tile is checked
+    against the oracle and bitwise against the same exp through the loop hero,
+    transposed on the host."""
+    say("transpose narrow tiles", dims, perm)
+    n = int(np.prod(dims))
+    out_dims = [dims[p] for p in perm]
+    s = W.Spec()
+    x = s.parameter(0, "f32", dims)
+    e = s.unary("exponential", x, "f32", dims)
+    s.transpose(e, perm, "f32", out_dims)
+    params = [W.normal_f32(W.rng(60 + dims[0]), n)]
+    got, f = run_gpu(s.nodes, params)
+    p = f.plan()
+    assert p["hero"] == "transpose" and (p["tile_rows"], p["tile_cols"]) == tile and p["block_threads"] == block
+    assert_ulp(got, oracle.evaluate(s.nodes, params), "f32", 2)
+    s2 = W.Spec()
+    x2 = s2.parameter(0, "f32", dims)
+    s2.unary("exponential", x2, "f32", dims)
+    e2, f2 = run_gpu(s2.nodes, params)
+    assert f2.plan()["hero"] == "loop"
+    want = np.transpose(e2.reshape(dims), perm).ravel()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("dims", [(20, 160, 170), (3, 7, 67)])
 def test_transpose3d_with_epilogue(dims):
     """The transpose emitter's 3-D example: abs(transpose(exp(x), {2,1,0}));
