@@ -34,9 +34,17 @@ _LIB = os.path.join(_HERE, "libhlo_oracle.so")
 MAX_RANK = 8
 MAX_OPERANDS = 8
 MAX_ATTR = 24
-DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "s32": 4, "u8": 5}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "s32": 4, "u8": 5, "s4": 6, "u4": 7}
+# Host buffers: one element per item, except s4/u4, which are packed two per
+# byte (see storage_size).
 NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "s8": np.int8,
-              "s32": np.int32, "u8": np.uint8}
+              "s32": np.int32, "u8": np.uint8, "s4": np.uint8, "u4": np.uint8}
+
+
+def storage_size(dtype: str, n: int) -> int:
+    """Items of NP_STORAGE[dtype] that hold n elements: s4/u4 take one byte
+    per two elements (the last byte half used when n is odd)."""
+    return (n + 1) // 2 if dtype in ("s4", "u4") else n
 OPS = {
     "parameter": 0, "constant": 1, "log": 2, "exponential": 3, "tanh": 4,
     "add": 5, "subtract": 6, "multiply": 7, "divide": 8, "maximum": 9,
@@ -106,7 +114,8 @@ def default_m2m(rank: int) -> list[int]:
 
 
 def _storage_bounds(dtype: str) -> tuple[int, int]:
-    return {"s8": (-128, 127), "u8": (0, 255), "s32": (-(2 ** 31), 2 ** 31 - 1)}[dtype]
+    return {"s8": (-128, 127), "u8": (0, 255), "s4": (-8, 7), "u4": (0, 15),
+            "s32": (-(2 ** 31), 2 ** 31 - 1)}[dtype]
 
 
 class _Graph:
@@ -183,7 +192,8 @@ def evaluate(nodes: list[dict], params: list[np.ndarray], root: int | None = Non
     """Whole root, encoded in the root's layout: flat array of its storage type."""
     g = _Graph(nodes, root)
     rn = g.root_node
-    out = np.zeros(int(np.prod(rn["dims"], dtype=np.int64)), dtype=NP_STORAGE[rn["dtype"]])
+    n = int(np.prod(rn["dims"], dtype=np.int64))
+    out = np.zeros(storage_size(rn["dtype"], n), dtype=NP_STORAGE[rn["dtype"]])
     pp, npar = g.param_ptrs(params)
     _check(lib().or_eval(g.arr, g.n, g.root, pp, npar, ctypes.c_void_p(out.ctypes.data)))
     return out

@@ -45,7 +45,10 @@
 #define OR_MAX_ATTR 24
 
 /* element types */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_S8 = 3, OR_S32 = 4, OR_U8 = 5 };
+/* si4/ui4 (Specification, "Types": 4-bit integers): the pages give no memory
+   packing.  Reading taken here: two elements per byte in physical (linear)
+   order, the element with the even linear index in the low four bits. */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2, OR_S8 = 3, OR_S32 = 4, OR_U8 = 5, OR_S4 = 6, OR_U4 = 7 };
 
 /* ops */
 enum {
@@ -192,6 +195,11 @@ static long double load_elem(int dtype, const void *buf, int64_t lin) {
     case OR_S8: return (long double)((const int8_t *)buf)[lin];
     case OR_U8: return (long double)((const uint8_t *)buf)[lin];
     case OR_S32: return (long double)((const int32_t *)buf)[lin];
+    case OR_S4: case OR_U4: {
+      const unsigned byte = ((const uint8_t *)buf)[lin / 2];
+      const int nib = (int)((lin % 2) ? (byte >> 4) : (byte & 0xFu));
+      return (long double)(dtype == OR_S4 && nib >= 8 ? nib - 16 : nib);
+    }
   }
   return NAN;
 }
@@ -215,6 +223,14 @@ static void store_elem(int dtype, void *buf, int64_t lin, long double v) {
     case OR_S8: ((int8_t *)buf)[lin] = (int8_t)v; break;
     case OR_U8: ((uint8_t *)buf)[lin] = (uint8_t)v; break;
     case OR_S32: ((int32_t *)buf)[lin] = (int32_t)v; break;
+    case OR_S4: case OR_U4: {
+      /* v is in [-8, 7] (si4) or [0, 15] (ui4); its low four bits are the
+         two's-complement nibble.  The other nibble of the byte is kept. */
+      uint8_t *b = (uint8_t *)buf + lin / 2;
+      const unsigned nib = (unsigned)((int)v & 0xF);
+      *b = (lin % 2) ? (uint8_t)((*b & 0x0Fu) | (nib << 4)) : (uint8_t)((*b & 0xF0u) | nib);
+      break;
+    }
   }
 }
 

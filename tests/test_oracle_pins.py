@@ -625,6 +625,68 @@ def test_u8_quantize_range_and_zero_point():
 
 
 # --------------------------------------------------------------------------
+# si4 / ui4 (Specification, "Types": 4-bit integers).  Packing reading: two
+# elements per byte in physical order, the even linear index in the low four
+# bits.  The expected values are worked by hand from that reading.
+# --------------------------------------------------------------------------
+def test_s4_u4_decode_worked_bytes():
+    raw = np.array([0x21, 0xF8, 0x7E], np.uint8)
+    for dt, want in (("s4", [1, 2, -8, -1, -2, 7]), ("u4", [1, 2, 8, 15, 14, 7])):
+        s = Spec()
+        p = s.parameter(0, dt, [6])
+        s.convert(p, "f32", [6])
+        assert ev(s, [raw]).tolist() == want
+    # the same bytes as a [2,3] array stored column-major: linear order is
+    # (0,0) (1,0) (0,1) (1,1) (0,2) (1,2)
+    s = Spec()
+    p = s.parameter(0, "s4", [2, 3], [0, 1])
+    s.convert(p, "f32", [2, 3], [1, 0])
+    assert ev(s, [raw]).reshape(2, 3).tolist() == [[1, -8, -2], [2, -1, 7]]
+
+
+def test_s4_u4_round_trip_every_byte():
+    """Decoding then encoding every byte value gives it back; an odd count
+    leaves the last byte's high nibble zero."""
+    raw = np.arange(256, dtype=np.uint8)
+    for dt in ("s4", "u4"):
+        s = Spec()
+        s.parameter(0, dt, [512])
+        assert np.array_equal(ev(s, [raw]), raw)
+        s = Spec()
+        p = s.parameter(0, dt, [512])
+        s.convert(p, "f32", [512])
+        vals = ev(s, [raw])
+        lo, hi = raw & 0xF, raw >> 4
+        if dt == "s4":
+            lo = np.where(lo >= 8, lo.astype(np.int64) - 16, lo)
+            hi = np.where(hi >= 8, hi.astype(np.int64) - 16, hi)
+        assert np.array_equal(vals, np.stack([lo, hi], 1).ravel().astype(np.float32))
+    q = quant_type("s4", [1.0], [0])
+    s = Spec()
+    p = s.parameter(0, "f32", [3])
+    s.op("uniform_quantize", [p], "s4", [3], quant=q)
+    assert ev(s, [np.array([-1.0, 3.0, -8.0], np.float32)]).tolist() == [0x3F, 0x08]
+
+
+def test_s4_u4_quantize_rounds_clamps_and_packs():
+    y = np.array([-100.0, -8.4, -7.6, -0.5, 0.5, 1.5, 6.6, 100.0], np.float32)
+    for dt, zp, want in (("s4", 0, [0x88, 0x08, 0x20, 0x77]), ("u4", 8, [0x00, 0x80, 0xA8, 0xFF])):
+        q = quant_type(dt, [1.0], [zp])
+        s = Spec()
+        p = s.parameter(0, "f32", [y.size])
+        s.op("uniform_quantize", [p], dt, [y.size], quant=q)
+        assert ev(s, [y]).tolist() == want
+    # per-axis dequantize of si4 along dim 1 with scales (0.5, 0.25) and zero
+    # points (1, -2): real = scale * (q - zp)
+    q = quant_type("s4", [0.5, 0.25], [1, -2], qdim=1)
+    s = Spec()
+    p = s.parameter(0, "s4", [2, 2], quant=q)
+    s.op("uniform_dequantize", [p], "f32", [2, 2])
+    # bytes: row 0 = (7, -8) -> 0x87; row 1 = (-1, 2) -> 0x2F
+    assert ev(s, [np.array([0x87, 0x2F], np.uint8)]).reshape(2, 2).tolist() == [[3.0, -1.5], [-1.0, 1.0]]
+
+
+# --------------------------------------------------------------------------
 # Index transforms (StableHLO Specification: reverse, iota, pad, concatenate)
 # --------------------------------------------------------------------------
 def test_reverse_iota_pad_concatenate_page_examples():
