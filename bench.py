@@ -104,6 +104,7 @@ def workload_makers():
         "column_reduce_max_f32_colmajor": (W.column_reduce_max_f32, {"m2m": (0, 1)},
                                            lambda ps: [ps[0].reshape(16384, 4096).T.copy().ravel()]),
         "quant_dequant_bias_requant": (W.quant_dequant_bias_requant, {}, None),
+        "quant_dequant_bias_requant_s4": (W.quant_dequant_bias_requant_s4, {}, None),
         "loop_log_transpose_add": (W.loop_log_transpose_add, {}, None),
         "gelu_bf16": (W.gelu_bf16, {}, None),
         "transpose3d_exp_abs": (W.transpose3d_exp_abs, {}, None),

@@ -31,12 +31,18 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhlofusion.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_RANK = 8
 MAX_OPERANDS = 8
 MAX_ATTR = 3 * MAX_RANK
-DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "u8": 4, "s32": 5}
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "s8": 1, "u8": 1, "s32": 4}
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "u8": 4, "s32": 5, "s4": 6, "u4": 7}
+DTYPE_BITS = {"f32": 32, "bf16": 16, "f16": 16, "s8": 8, "u8": 8, "s32": 32, "s4": 4, "u4": 4}
+
+
+def storage_bytes(dtype: str, n: int) -> int:
+    """Bytes of an array of n elements; s4/u4 pack two elements per byte (the
+    even linear index in the low half), so n elements take ceil(n / 2)."""
+    return (n * DTYPE_BITS[dtype] + 7) // 8
 OPS = {
     "parameter": 0, "constant": 1, "add": 2, "subtract": 3, "multiply": 4,
     "divide": 5, "maximum": 6, "minimum": 7, "log": 8, "exponential": 9,
@@ -266,19 +272,22 @@ class Fusion:
             nd = self._param_nodes.get(k)
             if nd is None:
                 continue
-            want = int(np.prod(nd["dims"], dtype=np.int64)) * DTYPE_BYTES[nd["dtype"]]
+            want = storage_bytes(nd["dtype"], int(np.prod(nd["dims"], dtype=np.int64)))
             if not p.is_contiguous() or p.numel() * p.element_size() != want:
                 raise ValueError("parameter %d must be a dense buffer of %d bytes" % (k, want))
             if not p.is_cuda:
                 raise ValueError("parameter %d must be a GPU tensor" % k)
+        # s4/u4 results are bytes, two elements each
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16,
-               "s8": torch.int8, "u8": torch.uint8, "s32": torch.int32}[self.out_dtype]
+               "s8": torch.int8, "u8": torch.uint8, "s32": torch.int32,
+               "s4": torch.uint8, "u4": torch.uint8}[self.out_dtype]
+        n_out = storage_bytes(self.out_dtype, self.out_numel) if self.out_dtype in ("s4", "u4") else self.out_numel
         if out is None:
             dev = params[0].device if params else torch.device("cuda")
-            out = torch.empty(self.out_numel, dtype=tdt, device=dev)
+            out = torch.empty(n_out, dtype=tdt, device=dev)
         elif (not out.is_cuda or not out.is_contiguous() or out.dtype != tdt
-              or out.numel() != self.out_numel):
-            raise ValueError("out must be a dense GPU tensor of %d %s elements" % (self.out_numel, self.out_dtype))
+              or out.numel() != n_out):
+            raise ValueError("out must be a dense GPU tensor of %d %s items" % (n_out, tdt))
         if stream is None:
             stream = torch.cuda.current_stream()
         self.launch_ptrs([p.data_ptr() for p in params], out.data_ptr(), stream.cuda_stream)

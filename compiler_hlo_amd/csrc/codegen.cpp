@@ -39,12 +39,19 @@ const char *ctype(hf_dtype dt) {
     case HF_BF16: case HF_F16: return "hf_u16";
     case HF_S8: return "signed char";
     case HF_U8: return "unsigned char";
+    case HF_S4: case HF_U4: return "unsigned char";  // two elements per byte
     case HF_S32: return "int";
   }
   return "void";
 }
 
 bool reg_is_float(const Type &t) { return is_float(t.dt) && t.quant < 0; }
+
+// Per-axis zero points live on the device one byte per entry, also for 4-bit
+// storage types (as the 8-bit type of the same signedness).
+hf_dtype zp_dtype(hf_dtype storage) {
+  return storage == HF_S4 ? HF_S8 : storage == HF_U4 ? HF_U8 : storage;
+}
 const char *rtype(const Type &t) { return reg_is_float(t) ? "float" : "int"; }
 
 bool env_flag(const char *name, bool dflt) {  // tuning and A/B switches
@@ -169,6 +176,7 @@ class Gen {
   // value that does not change across the hero's steps is loaded once.
   std::string load(Body &b, int tag, const char *reg, hf_dtype dt, const Type &t, const std::string &ptr,
                    const Index &E, bool stream = false) {
+    if (is_nibble(dt)) return load_nibbles(b, tag, reg, dt, t, ptr, E, stream);
     std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
     std::string off = offset(t, E);
     const int V = b.V;
@@ -207,6 +215,56 @@ class Gen {
             << "[l] = " << ptr << "[o + l * " << st[ld] << "]; }\n";
       b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = "
            << elem_value(dt, m + "[l]") << ";\n";
+    }
+    return v;
+  }
+
+  // Load of a 4-bit array (two elements per byte, the even linear index in
+  // the low half).  A lane run of V >= 8 elements along the contiguous dim
+  // starts at an even element offset (the run start is a multiple of V and
+  // every other stride a multiple of that dim's size, itself a multiple of
+  // V), so it is one raw load of V/2 bytes.  Otherwise each element is read
+  // from its byte and its half picked by the offset's parity.
+  std::string load_nibbles(Body &b, int tag, const char *reg, hf_dtype dt, const Type &t, const std::string &ptr,
+                           const Index &E, bool stream) {
+    std::string v = "v" + std::to_string(tag) + "_" + std::to_string(b.tmp++);
+    std::string off = offset(t, E);
+    const int V = b.V;
+    const char *sgn = dt == HF_S4 ? "true" : "false";
+    int ld = V > 1 ? lane_dim(E, b.lane) : -1;
+    std::vector<long long> st = phys_strides(t);
+    b.os << "  " << reg << " " << v << "[" << V << "];\n";
+    const bool in_fetch = stream || fetch_all_;
+    std::string m = in_fetch ? "R." + member(b) : "w" + std::to_string(b.tmp++);
+    std::ostringstream &ld_os = in_fetch ? b.fetch : b.os;
+    auto decl = [&](const std::string &type, int count) {
+      if (in_fetch) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
+      else b.os << "  " << type << " " << m << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
+    };
+    const std::string bytes = "((const unsigned char *)" + ptr + ")";
+    if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
+      decl("unsigned char", 0);
+      ld_os << "  " << m << " = " << bytes << "[(" << off << ") >> 1];\n";
+      b.os << "  { const int s = hf_nibble<" << sgn << ">(" << m << ", (" << off << ") & 1);\n";
+      b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
+    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V % 2 == 0) {
+      decl("hf_u32", (V + 7) / 8);
+      if (V >= 8) {
+        ld_os << "  hf_raw_ld<" << V / 2 << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off
+              << ") / 2, " << m << ");\n";
+      } else {  // 2 or 4 elements: one byte or one aligned 16-bit word
+        const char *w = V == 4 ? "unsigned short" : "unsigned char";
+        ld_os << "  " << m << "[0] = (hf_u32)*(const " << w << " *)((const unsigned char *)" << ptr << " + (long)(" << off
+              << ") / 2);\n";
+      }
+      b.os << "  { int s[" << V << "];\n    hf_unpack_n<" << V << ", " << sgn << ">(" << m << ", s);\n";
+      b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s[l]; }\n";
+    } else {  // one element per lane
+      decl("unsigned char", V);
+      ld_os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << m
+            << "[l] = " << bytes << "[(o + l * " << st[ld] << ") >> 1]; }\n";
+      b.os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v
+           << "[l] = hf_nibble<" << sgn << ">(" << m << "[l], (o + l * " << st[ld] << ") & 1); }\n";
     }
     return v;
   }
@@ -256,8 +314,8 @@ class Gen {
     vt.dt = HF_F32;
     *sc = load(b, 9000 + q, "float", HF_F32, vt, "A.qs" + std::to_string(q), e1);
     if (rc) *rc = load_f64(b, 9200 + q, vt, "A.qr" + std::to_string(q), e1);
-    vt.dt = Q.storage;
-    *zp = load(b, 9100 + q, "int", Q.storage, vt, "A.qz" + std::to_string(q), e1);
+    vt.dt = zp_dtype(Q.storage);
+    *zp = load(b, 9100 + q, "int", vt.dt, vt, "A.qz" + std::to_string(q), e1);
   }
 
   void lanes(Body &b, const std::string &dst, const char *reg, const std::string &expr) {
@@ -454,6 +512,7 @@ std::string store_call(hf_dtype dt, int V, const std::string &off, const std::st
     case HF_BF16: return "hf_st_h<" + v + ", false>(A.out, " + off + ", " + r + ");";
     case HF_F16: return "hf_st_h<" + v + ", true>(A.out, " + off + ", " + r + ");";
     case HF_S8: case HF_U8: return "hf_st_b<" + v + ">(A.out, " + off + ", " + r + ");";
+    case HF_S4: case HF_U4: return "hf_st_n<" + v + ">(A.out, " + off + ", " + r + ");";
     case HF_S32: return "hf_st_i32<" + v + ">(A.out, " + off + ", " + r + ");";
   }
   return "";
@@ -702,7 +761,7 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
   add(std::string(ctype(rt.dt)) + " *", "out");
   for (int q : P.quant_args) {
     add("const float *", "qs" + std::to_string(q));
-    add(std::string("const ") + ctype(g.quants[q].storage) + " *", "qz" + std::to_string(q));
+    add(std::string("const ") + ctype(zp_dtype(g.quants[q].storage)) + " *", "qz" + std::to_string(q));
     add("const double *", "qr" + std::to_string(q));
   }
   add("void *", "ws");

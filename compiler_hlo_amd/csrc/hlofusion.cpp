@@ -381,7 +381,7 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
     return true;
   };
   const hf::Type &rt = f->g.nodes[f->g.root].t;
-  const size_t rbytes = (size_t)(rt.numel() * hf::dtype_bytes(rt.dt));
+  const size_t rbytes = (size_t)hf::storage_bytes(rt.dt, rt.numel());
   const uintptr_t r0 = (uintptr_t)result;
   const uintptr_t r1 = r0 + (uintptr_t)rbytes;
   if (rt.numel() > 0 && (!result || (r0 & 15))) {
@@ -394,7 +394,7 @@ hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_pa
     if (pn < 0) continue;
     const hf::Type &pt = f->g.nodes[pn].t;
     if (pt.numel() == 0) continue;
-    uintptr_t p0 = (uintptr_t)params[k], p1 = p0 + (uintptr_t)(pt.numel() * hf::dtype_bytes(pt.dt));
+    uintptr_t p0 = (uintptr_t)params[k], p1 = p0 + (uintptr_t)hf::storage_bytes(pt.dt, pt.numel());
     if (!params[k] || (p0 & 15)) {
       set_err("parameter " + std::to_string(k) + " must be a non-NULL, 16-byte aligned device pointer");
       return HF_ERR_INVALID;

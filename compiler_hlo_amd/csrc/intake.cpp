@@ -15,14 +15,24 @@ namespace hf {
 
 void fail(hf_status st, const std::string &msg) { throw Error{st, msg}; }
 
-int dtype_bytes(hf_dtype dt) {
+int dtype_bits(hf_dtype dt) {
   switch (dt) {
-    case HF_F32: case HF_S32: return 4;
-    case HF_BF16: case HF_F16: return 2;
-    case HF_S8: case HF_U8: return 1;
+    case HF_F32: case HF_S32: return 32;
+    case HF_BF16: case HF_F16: return 16;
+    case HF_S8: case HF_U8: return 8;
+    case HF_S4: case HF_U4: return 4;
   }
   return 0;
 }
+
+// Whole bytes of one element (4-bit types count as one: callers that size
+// buffers use storage_bytes).
+int dtype_bytes(hf_dtype dt) { return dtype_bits(dt) >= 8 ? dtype_bits(dt) / 8 : 1; }
+
+// Bytes that hold n elements: 4-bit types pack two per byte.
+int64_t storage_bytes(hf_dtype dt, int64_t n) { return (n * dtype_bits(dt) + 7) / 8; }
+
+bool is_nibble(hf_dtype dt) { return dt == HF_S4 || dt == HF_U4; }
 
 bool is_float(hf_dtype dt) { return dt == HF_F32 || dt == HF_BF16 || dt == HF_F16; }
 
@@ -34,6 +44,8 @@ const char *dtype_name(hf_dtype dt) {
     case HF_S8: return "s8";
     case HF_U8: return "u8";
     case HF_S32: return "s32";
+    case HF_S4: return "s4";
+    case HF_U4: return "u4";
   }
   return "?";
 }
@@ -82,7 +94,7 @@ struct Ctx {
   [[noreturn]] void unsupported(const std::string &m) const { fail(HF_ERR_UNSUPPORTED, where() + m); }
 };
 
-bool valid_dtype(int dt) { return dt >= HF_F32 && dt <= HF_S32; }
+bool valid_dtype(int dt) { return dt >= HF_F32 && dt <= HF_U4; }
 
 std::string dims_str(const Type &t) {
   std::ostringstream s;
@@ -125,14 +137,18 @@ Type take_type(const hf_type &src, Graph &g, const Ctx &c) {
     if (t.dims[d] > 0 && n > (int64_t(1) << 40) / t.dims[d]) c.unsupported("array too large");
     n *= t.dims[d];
   }
-  if (n * dtype_bytes(t.dt) >= (int64_t(1) << 31)) c.unsupported("array of 2 GiB or more");
+  if (storage_bytes(t.dt, n) >= (int64_t(1) << 31)) c.unsupported("array of 2 GiB or more");
+  if (n >= (int64_t(1) << 31)) c.unsupported("array of 2^31 elements or more");
   if (src.quant) {
     const hf_quant &q = *src.quant;
-    if (t.dt != HF_S8 && t.dt != HF_U8)
-      c.unsupported("quantized storage type must be s8 or u8");
+    if (t.dt != HF_S8 && t.dt != HF_U8 && t.dt != HF_S4 && t.dt != HF_U4)
+      c.unsupported("quantized storage type must be s8, u8, s4 or u4");
     Quant qq;
     qq.storage = t.dt;
-    int32_t tmin = t.dt == HF_S8 ? -128 : 0, tmax = t.dt == HF_S8 ? 127 : 255;
+    int32_t tmin = 0, tmax = 255;
+    if (t.dt == HF_S8) tmin = -128, tmax = 127;
+    else if (t.dt == HF_S4) tmin = -8, tmax = 7;
+    else if (t.dt == HF_U4) tmin = 0, tmax = 15;
     qq.smin = q.has_storage_range ? q.storage_min : tmin;
     qq.smax = q.has_storage_range ? q.storage_max : tmax;
     if (!(tmin <= qq.smin && qq.smin < qq.smax && qq.smax <= tmax))
@@ -382,7 +398,7 @@ Graph intake(const hf_fusion_desc *desc) {
         if (n.attr.size() != 1 || n.attr[0] < 0 || n.attr[0] >= t.rank)
           c.invalid("0 <= iota_dimension < rank(output) violated (C1)");
         if (quantized) c.unsupported("quantized iota");
-        if (!is_float(t.dt) && t.dt != HF_S32) c.unsupported("iota of an 8-bit integer type");
+        if (!is_float(t.dt) && t.dt != HF_S32) c.unsupported("iota of an 8-bit or 4-bit integer type");
         // the index converts to f32 first: one rounding only while it is exact there
         if ((t.dt == HF_BF16 || t.dt == HF_F16) && !n.attr.empty() && t.dims[n.attr[0]] > (int64_t(1) << 24))
           c.unsupported("16-bit float iota longer than 2^24");

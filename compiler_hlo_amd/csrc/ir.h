@@ -17,7 +17,10 @@ struct Error {
 
 [[noreturn]] void fail(hf_status st, const std::string &msg);
 
+int dtype_bits(hf_dtype dt);
 int dtype_bytes(hf_dtype dt);
+int64_t storage_bytes(hf_dtype dt, int64_t n);
+bool is_nibble(hf_dtype dt);
 bool is_float(hf_dtype dt);
 const char *dtype_name(hf_dtype dt);
 const char *op_name(hf_op op);

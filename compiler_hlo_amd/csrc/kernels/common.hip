@@ -334,6 +334,53 @@ __device__ __forceinline__ void hf_st_b(void *base, int off, const int (&r)[V]) 
     for (int k = 0; k < V; ++k) p[k] = (unsigned char)r[k];
   }
 }
+// 4-bit elements (si4/ui4), two per byte in linear order with the even index
+// in the low half: element k of a run that starts at an even index sits at
+// bits 4k of the run's little-endian words.
+template <int V, bool SIGNED>
+__device__ __forceinline__ void hf_unpack_n(const hf_u32 (&w)[(V + 7) / 8], int (&r)[V]) {
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    const hf_u32 n = (w[k / 8] >> (4 * (k & 7))) & 0xFu;
+    r[k] = SIGNED ? (int)(n ^ 8u) - 8 : (int)n;
+  }
+}
+// One 4-bit element from its byte: the high half when its index is odd.
+template <bool SIGNED>
+__device__ __forceinline__ int hf_nibble(hf_u32 byte, int odd) {
+  const hf_u32 n = (odd ? byte >> 4 : byte) & 0xFu;
+  return SIGNED ? (int)(n ^ 8u) - 8 : (int)n;
+}
+// Store of V (even) 4-bit values at element offset off (even): whole bytes
+// only, so lanes never share a byte.
+template <int V>
+__device__ __forceinline__ void hf_st_n(void *base, int off, const int (&r)[V]) {
+  static_assert(V % 2 == 0, "4-bit stores move whole bytes");
+  unsigned char *p = (unsigned char *)base + (off >> 1);
+  if constexpr (V >= 8) {
+    hf_u32 w[V / 8];
+#pragma unroll
+    for (int k = 0; k < V / 8; ++k) {
+      hf_u32 x = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x |= ((hf_u32)r[8 * k + j] & 0xFu) << (4 * j);
+      w[k] = x;
+    }
+    if constexpr (V % 32 == 0) {
+#pragma unroll
+      for (int k = 0; k < V / 32; ++k)
+        hf_vst((hf_u32x4 *)p + k, hf_u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
+    } else if constexpr (V == 16) {
+      *(uint2 *)p = make_uint2(w[0], w[1]);
+    } else {
+      *(hf_u32 *)p = w[0];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < V / 2; ++k)
+      p[k] = (unsigned char)(((hf_u32)r[2 * k] & 0xFu) | (((hf_u32)r[2 * k + 1] & 0xFu) << 4));
+  }
+}
 template <int V>
 __device__ __forceinline__ void hf_st_i32(void *base, int off, const int (&r)[V]) {
   int *p = (int *)base + off;

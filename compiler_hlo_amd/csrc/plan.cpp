@@ -282,6 +282,16 @@ Access classify(const Graph &g, int p, const Index &E, int lane) {
 
 bool large(const Graph &g, int p) { return is_streaming(g, p); }
 
+// largest element width in bits among large params read contiguously along
+// the lane (0 if none)
+int stream_elem_bits(const Graph &g, const Ctx &c) {
+  int b = 0;
+  for (auto &pr : c.param_reads)
+    if (large(g, pr.first) && classify(g, pr.first, pr.second, c.lane) == CONTIG)
+      b = std::max(b, dtype_bits(g.nodes[pr.first].t.dt));
+  return b;
+}
+
 // largest element size among large params read contiguously along the lane
 int stream_elem_bytes(const Graph &g, const Ctx &c, int dflt) {
   int b = 0;
@@ -329,14 +339,14 @@ void algorithmic(const Graph &g, Plan &P) {
   for (int n = 0; n < (int)g.nodes.size(); ++n) {
     if (!used[n]) continue;
     const Node &nd = g.nodes[n];
-    if (nd.op == HF_PARAMETER) bytes += nd.t.numel() * dtype_bytes(nd.t.dt);
+    if (nd.op == HF_PARAMETER) bytes += storage_bytes(nd.t.dt, nd.t.numel());
     if (nd.t.quant >= 0 && (nd.op == HF_UNIFORM_QUANTIZE || nd.op == HF_PARAMETER)) qused[nd.t.quant] = 1;
   }
   for (size_t q = 0; q < g.quants.size(); ++q)
     if (qused[q] && g.quants[q].qdim >= 0)
       bytes += (long long)g.quants[q].scales.size() * (4 + dtype_bytes(g.quants[q].storage));
   const Type &rt = g.nodes[g.root].t;
-  bytes += rt.numel() * dtype_bytes(rt.dt);
+  bytes += storage_bytes(rt.dt, rt.numel());
   P.info.algorithmic_bytes = bytes;
 }
 
@@ -361,9 +371,18 @@ Plan plan_loop(const Graph &g, Ctx c) {
   const Type &rt = g.nodes[g.root].t;
   long long DL = c.lane >= 0 ? rt.dims[c.lane] : 1;
   int V = 1;
-  if (c.lane >= 0 && !c.general)
-    V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", 16), 16 / dtype_bytes(rt.dt))));
+  if (c.lane >= 0 && !c.general) {
+    // 128-bit lanes for the widest of the result and the streaming inputs
+    const int wbits = std::max(dtype_bits(rt.dt), stream_elem_bits(g, c));
+    V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", 128 / wbits), 128 / wbits)));
+  }
   c.V = V;
+  // A 4-bit result is stored a whole byte at a time: each lane needs an even
+  // run along the physically minor dim (then that dim is even as well).
+  if (is_nibble(rt.dt) && (c.lane < 0 || V % 2 != 0))
+    fail(HF_ERR_UNSUPPORTED,
+         std::string("a ") + dtype_name(rt.dt) +
+             " result needs an even physically minor dim read without a gather along it (lanes write whole bytes)");
   long long cols_v = DL / V;
   long long rows = DL > 0 ? rt.numel() / DL : 0;
   int block = 256;
@@ -411,7 +430,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
 bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
   const Type &rt = g.nodes[g.root].t;
   int lout = loop.lane;
-  if (lout < 0) return false;
+  if (lout < 0 || is_nibble(rt.dt)) return false;
   int lin = -1;
   bool any = false;
   // A large parameter whose contiguous dim is read with a plain variable other
@@ -521,6 +540,8 @@ Plan plan_reduce(const Graph &g) {
   const Node &R = g.nodes[g.reduce];
   int rin = R.opd[0];
   const Type &it = g.nodes[rin].t;
+  if (is_nibble(g.nodes[g.root].t.dt))
+    fail(HF_ERR_UNSUPPORTED, "4-bit results of a reduce (one output element per thread would share bytes)");
   Ctx c = make_ctx(g, rin, -1);
   // Physical order of the reduce input: taken from the largest parameter that
   // reads the input space through a pure permutation of its dims.

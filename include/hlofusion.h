@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define HF_ABI_VERSION 2
+#define HF_ABI_VERSION 3
 #define HF_MAX_RANK 8
 #define HF_MAX_OPERANDS 8               /* concatenate is variadic */
 #define HF_MAX_ATTR (3 * HF_MAX_RANK)   /* pad: low, high and interior per dim */
@@ -54,14 +54,25 @@ typedef enum {
   HF_ERR_NOMEM = 5
 } hf_status;
 
-/* Element types (StableHLO Specification, "Types": element types). */
+/* Element types (StableHLO Specification, "Types": element types).
+ * HF_S4 and HF_U4 are the 4-bit integers si4 and ui4 (ranges [-8, 7] and
+ * [0, 15]).  The pages give no memory packing for them; this library packs
+ * two elements per byte in physical (linear) order, the element with the even
+ * linear index in the low four bits, so an array of n elements occupies
+ * ceil(n / 2) bytes (the last byte's high half unused, and written as zero,
+ * when n is odd).  A 4-bit result is written only by the loop hero with an
+ * even number of elements per lane along an even physically minor dim, so
+ * that no two lanes share a byte; other 4-bit results are HF_ERR_UNSUPPORTED.
+ * 4-bit arrays can be read by every hero. */
 typedef enum {
   HF_F32 = 0,
   HF_BF16 = 1,
   HF_F16 = 2,
   HF_S8 = 3,
   HF_U8 = 4,
-  HF_S32 = 5
+  HF_S32 = 5,
+  HF_S4 = 6,
+  HF_U4 = 7
 } hf_dtype;
 
 /* Ops.  Semantics are those of the StableHLO Specification ("Ops") and of
@@ -148,7 +159,7 @@ typedef enum {
  * Specification, "Types": QuantizedTensorElementType, constraints C1-C13;
  * StableHLO Quantization, "Per-tensor quantization", "Per-axis
  * quantization").  The expressed type is f32; the storage type is the
- * hf_type's dtype (HF_S8 or HF_U8).  All arrays are HOST pointers read during
+ * hf_type's dtype (HF_S8, HF_U8, HF_S4 or HF_U4).  All arrays are HOST pointers read during
  * hf_fusion_create only; the library keeps its own copies. */
 typedef struct {
   int32_t quantization_dimension;  /* -1: per-tensor; else the sliced dim */
@@ -244,7 +255,8 @@ hf_status hf_fusion_plan(const hf_fusion *f, hf_plan_info *info);
 hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *len);
 
 /* Run the fusion.  params[i] is the DEVICE pointer of parameter i (dense, in
- * its declared layout, 16-byte aligned); result is the device pointer of the
+ * its declared layout, 16-byte aligned; numel * element size bytes, 4-bit
+ * types packed as described at hf_dtype); result is the device pointer of the
  * root buffer (dense, root layout, 16-byte aligned, not overlapping any
  * parameter).  The same parameter pointer may be passed twice.  stream is a
  * hipStream_t (NULL = the null stream).  The launch is asynchronous and

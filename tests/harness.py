@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 NP_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "s8": np.int8,
-              "u8": np.uint8, "s32": np.int32}
+              "u8": np.uint8, "s32": np.int32, "s4": np.uint8, "u4": np.uint8}  # s4/u4: packed bytes
 
 
 def to_device(buf: np.ndarray):

@@ -58,6 +58,103 @@ def test_quant_full():
     say("clamped fraction", clamped)
 
 
+@pytest.mark.parametrize("r,c", [(37, 160), (5, 48), (3, 2), (300, 4096)])
+def test_quant_s4_small(r, c):
+    """The per-axis requantize with si4 storage in and out: bytes bit-exact."""
+    say("quant s4", r, c)
+    spec, params, _ = W.quant_dequant_bias_requant_s4(r, c, seed=70 + r)
+    got, f = run_gpu(spec.nodes, params)
+    assert f.plan()["hero"] == "loop"
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "u8")
+
+
+def test_quant_s4_full():
+    spec, params, _ = W.quant_dequant_bias_requant_s4()
+    say("quant s4 full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    want = oracle.evaluate(spec.nodes, params)
+    assert_bitexact(got, want, "u8")
+    lo, hi = want & 0xF, want >> 4
+    say("clamped fraction", np.mean(np.isin(np.concatenate([lo, hi]), (7, 8))))
+
+
+def _four_bit_cases():
+    """(name, spec, params) for the 4-bit element paths of every hero."""
+    g = W.rng(71)
+    q = W.quant_type("s4", [0.05], [1])
+    qa = W.quant_type("s4", np.linspace(0.01, 0.1, 64).astype(np.float32), np.arange(64) % 16 - 8, qdim=1)
+    qu = W.quant_type("u4", [0.5], [8])
+    cases = []
+    s = W.Spec()
+    p = s.parameter(0, "s4", [100, 64], quant=qa)
+    s.op("uniform_dequantize", [p], "f32", [100, 64])
+    cases.append(("dequantize s4 per-axis, 2-byte runs", s, [W.integers(g, 3200, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "s4", [37, 33], quant=q)
+    s.op("uniform_dequantize", [p], "f32", [37, 33])
+    cases.append(("dequantize s4, odd dims, per element", s, [W.integers(g, 611, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "f32", [100, 64])
+    s.op("uniform_quantize", [p], "s4", [100, 64], quant=q)
+    cases.append(("quantize to s4", s, [W.normal_f32(g, 6400, 0.3)]))
+    s = W.Spec()
+    p = s.parameter(0, "f32", [100, 6])
+    s.op("uniform_quantize", [p], "u4", [100, 6], quant=qu)
+    cases.append(("quantize to u4, one byte per lane", s, [W.normal_f32(g, 600, 3.0)]))
+    s = W.Spec()
+    a = s.parameter(0, "s4", [64, 128], quant=q)
+    b = s.parameter(1, "s4", [64, 128], quant=W.quant_type("s4", [0.03], [-2]))
+    s.op("add", [a, b], "s4", [64, 128], quant=W.quant_type("s4", [0.1], [0]))
+    cases.append(("quantized add s4", s, [W.integers(g, 4096, 0, 255, np.uint8), W.integers(g, 4096, 0, 255, np.uint8)]))
+    for dt in ("s4", "u4"):
+        s = W.Spec()
+        p = s.parameter(0, dt, [64, 128])
+        s.convert(p, "f32", [64, 128])
+        cases.append(("convert %s" % dt, s, [W.integers(g, 4096, 0, 255, np.uint8)]))
+        s = W.Spec()
+        s.parameter(0, dt, [64, 128])
+        cases.append(("copy %s" % dt, s, [W.integers(g, 4096, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "f32", [256, 512])
+    t = s.transpose(p, [1, 0], "f32", [512, 256])
+    s.op("uniform_quantize", [t], "s4", [512, 256], quant=q)
+    cases.append(("transpose into s4 (loop)", s, [W.normal_f32(g, 256 * 512, 0.3)]))
+    s = W.Spec()
+    p = s.parameter(0, "s4", [200, 520], quant=q)
+    d = s.op("uniform_dequantize", [p], "f32", [200, 520])
+    s.transpose(d, [1, 0], "f32", [520, 200])
+    cases.append(("transpose of s4 (ragged tiles)", s, [W.integers(g, 52000, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "u4", [70, 4096], quant=qu)
+    d = s.op("uniform_dequantize", [p], "f32", [70, 4096])
+    s.reduce(d, [1], "add", 0.0, "f32", [70])
+    cases.append(("row sum over u4 (exact)", s, [W.integers(g, 143360, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "u4", [4100, 64], quant=qu)
+    d = s.op("uniform_dequantize", [p], "f32", [4100, 64])
+    s.reduce(d, [0], "max", float("-inf"), "f32", [64])
+    cases.append(("column max over u4", s, [W.integers(g, 131200, 0, 255, np.uint8)]))
+    s = W.Spec()
+    p = s.parameter(0, "s4", [0, 64], quant=q)
+    s.op("uniform_dequantize", [p], "f32", [0, 64])
+    cases.append(("empty s4", s, [np.zeros(0, np.uint8)]))
+    return cases
+
+
+@pytest.mark.parametrize("k", range(14))
+def test_four_bit_paths(k):
+    """si4/ui4 reads through every hero and 4-bit writes through the loop
+    hero: bit-exact against the oracle (dequantized values are small
+    multiples of their scale, so the sums here are exact)."""
+    name, s, params = _four_bit_cases()[k]
+    say("4-bit:", name)
+    got, f = run_gpu(s.nodes, params)
+    say("  hero", f.plan()["hero"], "V", f.plan()["vector_elems"])
+    want = oracle.evaluate(s.nodes, params)
+    dt = s.nodes[-1]["dtype"]
+    assert_bitexact(got, want, "u8" if dt in ("s4", "u4") else dt)
+
+
 def test_quant_zero_point_and_ties():
     """Per-tensor requantize with a non-zero output zero point, on values
     placed next to the rounding ties of y / scale."""

@@ -33,7 +33,7 @@ def test_exports_every_declared_function():
     lib = H.library()
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.hf_abi_version() == H.ABI_VERSION == 2
+    assert lib.hf_abi_version() == H.ABI_VERSION == 3
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -184,6 +184,58 @@ def test_quantized_elementwise_validation_and_expansion():
     s.op("abs", [a], "s8", [16], quant=W.quant_type("s8", [0.5], [1], storage_min=-100, storage_max=100))
     st, msg = _status(s.nodes)
     assert st == "HF_ERR_INVALID" and "storage" in msg
+
+
+def test_four_bit_types_validation_and_plans():
+    """si4/ui4: default storage ranges [-8, 7] and [0, 15]; byte counts pack
+    two elements per byte; a 4-bit result is written by the loop hero only,
+    with an even run per lane along an even physically minor dim."""
+    q = W.quant_type("s4", [0.05], [1])
+    s = W.Spec()
+    p = s.parameter(0, "f32", [100, 64])
+    s.op("uniform_quantize", [p], "s4", [100, 64], quant=q)
+    pl = plan_of(s)
+    assert pl["hero"] == "loop" and pl["vector_elems"] % 2 == 0
+    assert pl["algorithmic_bytes"] == 100 * 64 * 4 + 100 * 64 // 2
+    # an odd minor dim, a reduce result and an iota cannot be 4-bit
+    s = W.Spec()
+    p = s.parameter(0, "f32", [100, 63])
+    s.op("uniform_quantize", [p], "s4", [100, 63], quant=q)
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "even" in msg
+    s = W.Spec()
+    p = s.parameter(0, "f32", [64, 64])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [64])
+    s.op("uniform_quantize", [r], "s4", [64], quant=q)
+    st, msg = _status(s.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "4-bit" in msg
+    s = W.Spec()
+    s.iota(0, "u4", [16])
+    assert _status(s.nodes)[0] == "HF_ERR_UNSUPPORTED"
+    # storage range and zero points inside [-8, 7] / [0, 15]
+    for dt, zp, lo, hi, ok in (("s4", -8, None, None, True), ("s4", 8, None, None, False),
+                               ("u4", 15, None, None, True), ("u4", -1, None, None, False),
+                               ("s4", 0, -9, 7, False), ("u4", 0, 0, 16, False), ("s4", 2, -2, 5, True)):
+        s = W.Spec()
+        p = s.parameter(0, dt, [8, 32], quant=W.quant_type(dt, [0.5], [zp], storage_min=lo, storage_max=hi))
+        s.op("uniform_dequantize", [p], "f32", [8, 32])
+        assert (_status(s.nodes)[0] == "HF_OK") == ok, (dt, zp, lo, hi)
+    # 4-bit inputs are read by every hero; a transpose into 4-bit takes the loop
+    s = W.Spec()
+    p = s.parameter(0, "u4", [64, 4096], quant=W.quant_type("u4", [0.5], [8]))
+    d = s.op("uniform_dequantize", [p], "f32", [64, 4096])
+    s.reduce(d, [1], "add", 0.0, "f32", [64])
+    assert plan_of(s)["hero"] == "row_reduce"
+    s = W.Spec()
+    p = s.parameter(0, "s4", [256, 512], quant=q)
+    d = s.op("uniform_dequantize", [p], "f32", [256, 512])
+    s.transpose(d, [1, 0], "f32", [512, 256])
+    assert plan_of(s)["hero"] == "transpose"
+    s = W.Spec()
+    p = s.parameter(0, "f32", [256, 512])
+    t = s.transpose(p, [1, 0], "f32", [512, 256])
+    s.op("uniform_quantize", [t], "s4", [512, 256], quant=q)
+    assert plan_of(s)["hero"] == "loop"
 
 
 def test_argmax_validation():
@@ -367,7 +419,7 @@ def test_transpose_tile_arithmetic_of_the_pages_example():
 # --------------------------------------------------------------------------
 WORKLOADS = [W.loop_log_transpose_add, W.transpose_exp_f32, W.transpose_bf16_021,
              W.row_reduce_exp_add_bf16, W.column_reduce_max_f32, W.quant_dequant_bias_requant,
-             W.gelu_bf16]
+             W.gelu_bf16, W.quant_dequant_bias_requant_s4]
 
 
 @pytest.mark.parametrize("make", WORKLOADS, ids=lambda m: m.__name__)

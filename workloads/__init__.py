@@ -236,6 +236,30 @@ def quant_dequant_bias_requant(r=4096, c=4096, seed=6, out_scale=0.02, out_zp=0)
                           "bytes": 2 * r * c + 4 * c + 4 * c + 4 * c}
 
 
+def quant_dequant_bias_requant_s4(r=4096, c=4096, seed=13, out_scale=0.05, out_zp=0):
+    """The per-axis requantize of quant_dequant_bias_requant with si4 storage
+    in and out: q si4[r,c] is drawn as random bytes (two random 4-bit values
+    each), scales ~ U(0.001, 0.05), zero points U{-3..3}, bias f32[c] ~
+    N(0, 0.1) broadcast on dim 1, requantized per-tensor si4 (scale 0.05,
+    zero point 0)."""
+    g = rng(seed)
+    q = integers(g, (r * c + 1) // 2, 0, 255, np.uint8)
+    scales = uniform_f32(g, c, 0.001, 0.05)
+    zps = integers(g, c, -3, 3, np.int64)
+    bias = normal_f32(g, c, 0.1)
+    s = Spec()
+    qin = quant_type("s4", scales, zps, qdim=1)
+    qout = quant_type("s4", [out_scale], [out_zp])
+    p = s.parameter(0, "s4", [r, c], [1, 0], quant=qin)
+    bb = s.parameter(1, "f32", [c], [0])
+    d = s.op("uniform_dequantize", [p], "f32", [r, c])
+    bc = s.broadcast_in_dim(bb, [1], "f32", [r, c])
+    y = s.binary("add", d, bc, "f32", [r, c])
+    s.op("uniform_quantize", [y], "s4", [r, c], m2m=[1, 0], quant=qout)
+    return s, [q, bias], {"name": "quant_dequant_bias_requant_s4", "elements": r * c,
+                          "bytes": r * c + 9 * c}
+
+
 def transpose3d_exp_abs(d0=20, d1=160, d2=170, seed=8):
     """out = abs(transpose(exp(x), {2,1,0})), x f32[d0,d1,d2] ~ N(0,1): the
     transpose emitter's example on XLA:GPU Emitters ("Transpose emitter"),
