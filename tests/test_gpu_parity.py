@@ -841,6 +841,50 @@ def test_column_reduce_full_both_layouts():
 
 
 # --------------------------------------------------------------------------
+# launches recorded into a HIP graph
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("k", range(3))
+def test_launch_in_hip_graph(k):
+    """A launch recorded into a HIP graph (torch.cuda.graph) and replayed with
+    new inputs copied in, with an eager launch of the same handle between
+    replays: every replay equals the eager result bitwise.  The column
+    reduce's launch holds two kernels and the handle's workspace."""
+    import torch
+    import compiler_hlo_amd as H
+    make = [lambda seed: W.transpose_bf16_021(4, 64, 128, seed=seed),
+            lambda seed: W.row_reduce_exp_add_bf16(2, 8, 4096, seed=seed),
+            lambda seed: W.column_reduce_max_f32(4096, 512, seed=seed)][k]
+    spec, p0, _ = make(90)
+    say("graph", spec.nodes[-1]["op"], [nd["dims"] for nd in spec.nodes if nd["op"] == "parameter"])
+    f = H.Fusion(spec.nodes)
+    if k == 2:
+        assert f.plan()["hero"] == "column_reduce" and f.plan()["workspace_bytes"] > 0
+    static_in = [to_device(p) for p in p0]
+    static_out = f(*static_in)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f(*static_in, out=static_out)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        f(*static_in, out=static_out)
+    dt = spec.nodes[-1]["dtype"]
+    for seed in (91, 92, 93):
+        _, pk, _ = make(seed)
+        for t, p in zip(static_in, pk):
+            t.copy_(to_device(p))
+        static_out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = from_device(static_out, dt)
+        want, _ = run_gpu(spec.nodes, pk, fusion=f)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), seed
+    del graph
+
+
+# --------------------------------------------------------------------------
 # special values and exhaustive bf16 exp
 # --------------------------------------------------------------------------
 def test_special_values_max_min_exp_log():

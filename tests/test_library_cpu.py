@@ -36,6 +36,83 @@ def test_exports_every_declared_function():
     assert lib.hf_abi_version() == H.ABI_VERSION == 3
 
 
+C_CLIENT = r"""
+#include "hlofusion.h"
+#include <stdio.h>
+#include <string.h>
+
+static hf_type f32_2d(int64_t r, int64_t c) {
+  hf_type t;
+  memset(&t, 0, sizeof t);
+  t.dtype = HF_F32;
+  t.rank = 2;
+  t.dims[0] = r;
+  t.dims[1] = c;
+  return t;
+}
+
+int main(void) {
+  hf_node n[3];
+  hf_fusion_desc d;
+  hf_fusion *f = NULL;
+  hf_plan_info info;
+  hf_status st;
+  memset(n, 0, sizeof n);
+  n[0].op = HF_PARAMETER;
+  n[0].type = f32_2d(4096, 4096);
+  n[0].parameter_number = 0;
+  n[1].op = HF_EXP;
+  n[1].n_operands = 1;
+  n[1].operands[0] = 0;
+  n[1].type = f32_2d(4096, 4096);
+  n[2].op = HF_TRANSPOSE;
+  n[2].n_operands = 1;
+  n[2].operands[0] = 1;
+  n[2].type = f32_2d(4096, 4096);
+  n[2].n_attr = 2;
+  n[2].attr[0] = 1;
+  n[2].attr[1] = 0;
+  d.abi_version = HF_ABI_VERSION;
+  d.n_nodes = 3;
+  d.nodes = n;
+  d.root = 2;
+  d.n_params = 1;
+  st = hf_fusion_create(&d, HF_CREATE_PLAN_ONLY, &f);
+  if (st != HF_OK) {
+    printf("create failed: %s\n", hf_last_error());
+    return 1;
+  }
+  if (hf_fusion_plan(f, &info) != HF_OK) return 2;
+  printf("hero %d bytes %lld\n", (int)info.hero, (long long)info.algorithmic_bytes);
+  hf_fusion_destroy(f);
+  n[2].attr[1] = 1; /* not a permutation */
+  f = NULL;
+  st = hf_fusion_create(&d, HF_CREATE_PLAN_ONLY, &f);
+  printf("invalid %d %s null %d\n", (int)st, hf_last_error(), f == NULL);
+  printf("abi %d\n", (int)hf_abi_version());
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_plans_from_c(tmp_path):
+    """include/hlofusion.h compiles as strict C99 with every warning an error,
+    and a C program plans a fusion and sees a validation error through it."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.join(ROOT, "compiler_hlo_amd")
+    subprocess.check_call(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                           "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                           "-L", libdir, "-lhlofusion", "-Wl,-rpath," + libdir])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    lines = out.stdout.splitlines()
+    assert lines[0] == "hero 1 bytes 134217728"
+    assert lines[1].startswith("invalid 1 ") and "permutation" in lines[1] and lines[1].endswith("null 1")
+    assert lines[2] == "abi 3"
+
+
 def test_missing_library_fails_loudly(tmp_path):
     """Without libhlofusion.so the package refuses to import: no fallback."""
     pkg = tmp_path / "compiler_hlo_amd"
