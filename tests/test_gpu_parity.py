@@ -1040,8 +1040,10 @@ def test_gelu_bf16(shape):
     spec, params, _ = W.gelu_bf16(*shape)
     got, f = run_gpu(spec.nodes, params)
     assert f.plan()["hero"] == "loop"
-    d = assert_ulp(got, oracle.evaluate(spec.nodes, params), "bf16", 2)
-    say("gelu ulp histogram", np.bincount(d.astype(np.int64)))
+    # bit-exact: a product of two bf16 values is exact in f32, a sum of two
+    # bf16 values rounded to f32 and then to bf16 is the single bf16 rounding,
+    # and the bf16 tanh is correctly rounded on every input (exhaustive test)
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "bf16")
 
 
 # --------------------------------------------------------------------------
