@@ -208,6 +208,7 @@ class Gen {
         case HF_F16: b.os << "  hf_unpack_h<" << V << ", true>(" << m << ", " << v << ");\n"; break;
         case HF_S8: b.os << "  hf_unpack_b<" << V << ", true>(" << m << ", " << v << ");\n"; break;
         case HF_U8: b.os << "  hf_unpack_b<" << V << ", false>(" << m << ", " << v << ");\n"; break;
+        case HF_S4: case HF_U4: break;  // 4-bit arrays are loaded by load_nibbles
       }
     } else {  // one load per lane
       decl(ctype(dt), V);
