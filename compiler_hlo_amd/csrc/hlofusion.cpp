@@ -208,6 +208,7 @@ hf_status load_on_device(hf_fusion *f) {
     e = hipMalloc(&f->ws, (size_t)f->P.ws_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
   }
+  f->qdev.reserve(3 * f->P.quant_args.size());  // push_back below cannot throw
   for (int q : f->P.quant_args) {
     const hf::Quant &Q = f->g.quants[q];
     void *s = nullptr, *z = nullptr;
@@ -271,7 +272,9 @@ hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion
   *out = nullptr;
   // No exception crosses the C boundary.
   try {
-    std::unique_ptr<hf_fusion> f(new hf_fusion);
+    // The deleter frees whatever was loaded, on every early return and on
+    // exceptions alike.
+    std::unique_ptr<hf_fusion, void (*)(hf_fusion *)> f(new hf_fusion, release);
     f->g = hf::intake(desc);
     f->P = hf::make_plan(f->g);
     f->plan_only = flags & HF_CREATE_PLAN_ONLY;
@@ -284,10 +287,7 @@ hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion
       if (st != HF_OK) return st;
       if (!f->compile_only) {
         st = load_on_device(f.get());
-        if (st != HF_OK) {
-          release(f.release());
-          return st;
-        }
+        if (st != HF_OK) return st;
       }
     }
     *out = f.release();
