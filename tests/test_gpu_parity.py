@@ -840,6 +840,44 @@ def test_column_reduce_full_both_layouts():
     assert np.array_equal(got.view(np.uint32), got_c.view(np.uint32))
 
 
+@pytest.mark.parametrize("hero", ["row_reduce", "column_reduce"])
+def test_reduce_special_values(hero):
+    """max, min and add reductions over data with NaN, signed zeros and
+    infinities, through the row hero (rows of 16384: two rows per step) and
+    the column hero (many segments: the specials cross the fold kernel).
+    IEEE maximum/minimum propagate NaN and order -0 < +0; +inf + -inf is NaN.
+    Integer-valued data keeps the sums exact: bit-exact against the oracle."""
+    g = W.rng(95)
+    n_red, n_keep = 16384, 64
+    x = W.integers(g, n_red * n_keep, -100, 100, np.int64).astype(np.float32).reshape(n_keep, n_red)
+    nan, inf = np.float32("nan"), np.float32("inf")
+    x[0, 777] = nan                      # one NaN in the middle
+    x[1] = np.where(np.arange(n_red) % 2, -0.0, 0.0)
+    x[2] = -0.0                          # all -0
+    x[3] = -inf
+    x[4, 5], x[4, 9000] = inf, -inf      # inf - inf
+    x[5, -1] = nan                       # NaN last
+    x[6] = nan
+    x[7, 0] = nan                        # NaN first
+    x[8, 123] = inf
+    arr = x if hero == "row_reduce" else np.ascontiguousarray(x.T)   # [keep, red] or [red, keep]
+    dims = list(arr.shape)
+    rdim = 1 if hero == "row_reduce" else 0
+    for red, init in (("max", -np.inf), ("min", np.inf), ("add", 0.0)):
+        say("reduce specials", hero, red)
+        s = W.Spec()
+        p = s.parameter(0, "f32", dims)
+        s.reduce(p, [rdim], red, float(init), "f32", [n_keep])
+        got, f = run_gpu(s.nodes, [arr.ravel()])
+        assert f.plan()["hero"] == hero
+        assert_bitexact(got, oracle.evaluate(s.nodes, [arr.ravel()]), "f32")
+        if red == "max":
+            assert np.isnan(got[[0, 5, 6, 7]]).all() and got[8] == inf and got[3] == -inf
+            assert got[1] == 0 and not np.signbit(got[1]) and np.signbit(got[2])
+        if red == "add":
+            assert np.isnan(got[4]) and got[8] == inf
+
+
 # --------------------------------------------------------------------------
 # launches recorded into a HIP graph
 # --------------------------------------------------------------------------
