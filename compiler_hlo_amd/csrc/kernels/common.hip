@@ -54,24 +54,20 @@ __device__ __forceinline__ float hf_exp_for_bf16(float x) {
   return h * h;
 }
 
-// tanh of a value whose result is rounded to bf16.  For |x| < 0.5 the odd
-// Taylor series of tanh through the x^11 term (coefficients from the Bernoulli
-// numbers; the truncation error is below 2^-20 relative); otherwise
-// 1 - 2/(e^(2|x|) + 1) with the hardware exp2 and reciprocal, whose relative
-// error stays near 2^-20 and which is exactly 1 once e^(2|x|) overflows.  The
-// sign is restored last: tanh(-0) = -0, and a NaN stays NaN.  After rounding
-// to bf16 the result is within one bf16 ulp of the correctly rounded one.
+// tanh of a bf16 value whose result is rounded to bf16.  Below 2^-4 in
+// magnitude tanh(x) rounds to x itself (true for every bf16 input below
+// 0.0903).  Otherwise (e - 1) / (e + 1) with e = e^(2|x|) from the hardware
+// exp2 and reciprocal: there e - 1 >= 0.13, so the exp2 error stays near
+// 2^-20 relative in the quotient, far under half a bf16 ulp (2^-9).  |x| is
+// capped at 9, where the quotient already rounds to 1 and e stays finite; the
+// cap is IEEE minimum, so a NaN stays NaN.  The sign is restored last
+// (tanh(-0) = -0).  Exhaustive over the bf16 inputs the result rounds to the
+// correctly rounded value.
 __device__ __forceinline__ float hf_tanh_for_bf16(float x) {
-  const float a = __builtin_fabsf(x);
-  const float s = a * a;
-  float p = __builtin_fmaf(s, -8.8632355299021966e-3f, 2.1869488536155203e-2f);  // -1382/155925, 62/2835
-  p = __builtin_fmaf(s, p, -5.3968253968253968e-2f);                              // -17/315
-  p = __builtin_fmaf(s, p, 1.3333333333333333e-1f);                               // 2/15
-  p = __builtin_fmaf(s, p, -3.3333333333333333e-1f);                              // -1/3
-  const float small = __builtin_fmaf(a * s, p, a);
+  const float a = __builtin_elementwise_minimum(__builtin_fabsf(x), 9.0f);
   const float e = __builtin_amdgcn_exp2f(a * 2.8853900817779268f);  // 2 log2(e)
-  const float large = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
-  return __builtin_copysignf(a < 0.5f ? small : large, x);
+  const float t = (e - 1.0f) * __builtin_amdgcn_rcpf(e + 1.0f);
+  return __builtin_copysignf(a < 0.0625f ? a : t, x);
 }
 
 __device__ __forceinline__ int hf_clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
