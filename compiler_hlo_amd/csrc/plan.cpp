@@ -613,7 +613,11 @@ Plan plan_reduce(const Graph &g) {
     long long kv = K / V;
     int block, tpr;
     if (kv >= 64) {
-      block = (int)std::min<long long>(env_ll("HF_ROW_BLOCK", 512), pow2_floor(kv));
+      // 512 threads per row; 256 for max/argmax, whose per-row finish (a
+      // pair reduction and a serial combine over the waves) weighs more
+      // (measured 71% -> 80% of peak on bf16[8192,8192]; the float paths
+      // lost 1-20% at 256)
+      block = (int)std::min<long long>(env_ll("HF_ROW_BLOCK", op == HF_REDUCER_ARGMAX ? 256 : 512), pow2_floor(kv));
       tpr = block;
     } else {
       block = 256;
