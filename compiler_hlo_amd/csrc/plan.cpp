@@ -653,7 +653,9 @@ Plan plan_reduce(const Graph &g) {
     int V = c.general ? 1 : vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4)));
     c.V = V;
     long long Cc = J, Rr = K;
-    int cl = (int)std::min<long long>(env_ll("HF_COL_CL", 64), pow2_ceil(ceil_div(Cc, V)));
+    // 32 column lanes: 128-bit lanes over 512-byte row segments, 8 row lanes
+    // (measured 73% -> 76% of peak on f32[16384,4096] against 64 lanes)
+    int cl = (int)std::min<long long>(env_ll("HF_COL_CL", 32), pow2_ceil(ceil_div(Cc, V)));
     int block = 256;
     int rl = block / cl;
     long long cb = (long long)cl * V;
