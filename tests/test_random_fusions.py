@@ -1,0 +1,152 @@
+"""Seeded random fusions, compared with the oracle.
+
+Each case is a random graph over a rank 1-3 output space with random
+minor_to_major layouts: parameters read directly, transposed, broadcast or
+reversed, chains of elementwise ops that round identically on both sides
+(add, subtract, multiply, maximum, minimum, negate, abs, f32 <-> bf16
+converts), and sometimes a reduce (add over integer-valued f32, or max/min)
+followed by an elementwise epilogue.  Inputs are small integers, so every
+result, sums included, is exact: the comparison is bit-exact.  Fusions the
+library does not implement (a reduce whose dims are neither physically minor
+nor physically major) are counted and skipped.
+
+The CPU test plans and compiles every case for gfx950; the GPU tests run them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from harness import assert_bitexact, run_gpu
+
+N_CASES = 96        # seeds 1000.. : any shape
+N_HERO = 48         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
+BATCH = 24
+
+
+def _layout(g, rank):
+    return [int(d) for d in g.permutation(rank)] if g.random() < 0.5 else None
+
+
+def _values(g, dtype, n):
+    v = W.integers(g, n, -8, 8, np.int64).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else v
+
+
+def random_case(seed, hero_bias=False):
+    """(spec, params) of one random fusion.  With hero_bias the shapes are
+    tile-sized, the first parameter is read transposed and reductions favour
+    the physically major dims, so that the transpose and column-reduce heroes
+    come up often."""
+    g = W.rng(seed)
+    rank = int(g.integers(2, 4)) if hero_bias else int(g.integers(1, 4))
+    sizes = [33, 64, 96, 130, 257] if hero_bias else [1, 2, 3, 5, 8, 17, 33, 64, 96, 130]
+    while True:
+        dims = [int(g.choice(sizes)) for _ in range(rank)]
+        if math.prod(dims) <= 100_000:
+            break
+    dt = "f32" if g.random() < 0.6 else "bf16"
+    with_reduce = g.random() < 0.4
+    s = W.Spec()
+    params, vals = [], []
+    for p in range(int(g.integers(1, 4))):
+        kind = str(g.choice(["plain", "transpose", "broadcast", "reverse"]))
+        if hero_bias and p == 0:
+            kind = "transpose"
+        if kind == "transpose" and rank < 2:
+            kind = "plain"
+        if kind == "plain":
+            x = s.parameter(p, dt, dims, _layout(g, rank))
+            pdims = dims
+        elif kind == "transpose":
+            perm = [int(d) for d in g.permutation(rank)]
+            pdims = [0] * rank
+            for d in range(rank):
+                pdims[perm[d]] = dims[d]
+            x = s.transpose(s.parameter(p, dt, pdims, _layout(g, rank)), perm, dt, dims)
+        elif kind == "broadcast":
+            k = int(g.integers(0, rank + 1))
+            bd = sorted(int(d) for d in g.choice(rank, k, replace=False))
+            pdims = [dims[d] if g.random() < 0.8 else 1 for d in bd]
+            x = s.broadcast_in_dim(s.parameter(p, dt, pdims), bd, dt, dims)
+        else:
+            rd = sorted(int(d) for d in g.choice(rank, int(g.integers(1, rank + 1)), replace=False))
+            pdims = dims
+            x = s.reverse(s.parameter(p, dt, dims, _layout(g, rank)), rd, dt, dims)
+        vals.append(x)
+        params.append(_values(g, dt, math.prod(pdims)))
+    binary = ["add", "subtract", "maximum", "minimum"] + ([] if with_reduce else ["multiply"])
+    for _ in range(int(g.integers(1, 6))):
+        if g.random() < 0.7:
+            a, b = (int(i) for i in g.choice(len(vals), 2))
+            vals.append(s.binary(str(g.choice(binary)), vals[a], vals[b], dt, dims))
+        else:
+            vals.append(s.unary(str(g.choice(["negate", "abs"])), vals[int(g.integers(len(vals)))], dt, dims))
+    r = vals[-1]
+    for v in vals[:-1]:  # every value reaches the root
+        r = s.binary("add", r, v, dt, dims)
+    cur = dt
+    if g.random() < 0.3:
+        cur = "bf16" if dt == "f32" else "f32"
+        r = s.convert(r, cur, dims)
+    out_dims = dims
+    if with_reduce:
+        if hero_bias and g.random() < 0.6:  # the leading dims of the default layout
+            red = list(range(int(g.integers(1, rank))))
+            s.nodes[-1]["m2m"] = None
+        else:
+            red = sorted(int(d) for d in g.choice(rank, int(g.integers(1, rank + 1)), replace=False))
+        out_dims = [dims[d] for d in range(rank) if d not in red]
+        reducer = str(g.choice(["add", "max", "min"]))
+        if reducer == "add" and cur != "f32":
+            cur = "f32"
+            r = s.convert(r, cur, dims)
+        init = {"add": 0.0, "max": -np.inf, "min": np.inf}[reducer]
+        r = s.reduce(r, red, reducer, init, cur, out_dims)
+        if g.random() < 0.5:
+            r = s.unary(str(g.choice(["negate", "abs"])), r, cur, out_dims)
+    s.nodes[-1]["m2m"] = _layout(g, len(out_dims))
+    return s, params
+
+
+def _cases():
+    """(seed, hero_bias) of every case."""
+    return [(1000 + k, False) for k in range(N_CASES)] + [(2000 + k, True) for k in range(N_HERO)]
+
+
+def test_random_fusions_plan_and_compile():
+    import collections
+    import compiler_hlo_amd as H
+    ran = skipped = 0
+    heroes = collections.Counter()
+    for seed, bias in _cases():
+        s, params = random_case(seed, bias)
+        try:
+            f = H.Fusion(s.nodes, mode="compile")
+        except H.FusionError as e:
+            assert e.status == "HF_ERR_UNSUPPORTED", (seed, str(e))
+            skipped += 1
+            continue
+        heroes[f.plan()["hero"]] += 1
+        oracle.evaluate(s.nodes, params)
+        ran += 1
+    total = N_CASES + N_HERO
+    assert ran >= total * 3 // 4, (ran, skipped)
+    assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO) // BATCH))
+def test_random_fusions_gpu(batch):
+    import compiler_hlo_amd as H
+    for seed, bias in _cases()[batch * BATCH:(batch + 1) * BATCH]:
+        s, params = random_case(seed, bias)
+        try:
+            H.Fusion(s.nodes, mode="plan")
+        except H.FusionError:
+            continue
+        print("random fusion seed", seed, [nd["op"] for nd in s.nodes], flush=True)
+        got, f = run_gpu(s.nodes, params)
+        assert_bitexact(got, oracle.evaluate(s.nodes, params), s.nodes[-1]["dtype"])
