@@ -23,6 +23,7 @@ from harness import assert_bitexact, run_gpu
 
 N_CASES = 96        # seeds 1000.. : any shape
 N_HERO = 48         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
+N_WIDE = 48         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
 BATCH = 24
 
 
@@ -111,9 +112,98 @@ def random_case(seed, hero_bias=False):
     return s, params
 
 
+_STORAGE = {"s8": (-128, 127), "u8": (0, 255), "s4": (-8, 7), "u4": (0, 15)}
+
+
+def _storage_values(g, dt, n):
+    """Random storage values of n elements, packed two per byte for 4-bit."""
+    if dt in ("s4", "u4"):
+        return W.integers(g, (n + 1) // 2, 0, 255, np.uint8)
+    lo, hi = _STORAGE[dt]
+    return W.integers(g, n, lo, hi, np.int8 if dt == "s8" else np.uint8)
+
+
+def random_wide_case(seed):
+    """(spec, params): f32 values built by pad, concatenate and per-tensor or
+    per-axis dequantize (power-of-two scales, so every value and sum stays
+    exact), combined by exact elementwise ops, ending in a quantize to an 8-
+    or 4-bit type, a reduce, or neither."""
+    g = W.rng(seed)
+    rank = int(g.integers(1, 4))
+    while True:
+        dims = [int(g.choice([2, 3, 6, 9, 16, 31, 64, 100])) for _ in range(rank)]
+        if math.prod(dims) <= 100_000:
+            break
+    s = W.Spec()
+    params, vals = [], []
+    for p in range(int(g.integers(1, 4))):
+        kind = str(g.choice(["pad", "concatenate", "dequantize"]))
+        if kind == "pad":
+            inter = [int(g.integers(0, 2)) for _ in range(rank)]
+            pd, low, high = [], [], []
+            for d in range(rank):
+                n = int(g.integers(1, (dims[d] - 1) // (inter[d] + 1) + 2))
+                rem = dims[d] - ((n - 1) * (inter[d] + 1) + 1)
+                lo = int(g.integers(0, rem + 1))
+                pd.append(n), low.append(lo), high.append(rem - lo)
+            x = s.parameter(len(params), "f32", pd)
+            params.append(_values(g, "f32", math.prod(pd)))
+            v = s.constant(float(g.integers(-4, 5)), "f32", [])
+            vals.append(s.pad(x, v, low, high, inter, "f32", dims))
+        elif kind == "concatenate" and max(dims) >= 2:
+            d = int(np.argmax(dims))
+            a = int(g.integers(1, dims[d]))
+            parts = []
+            for ext in (a, dims[d] - a):
+                pdims = list(dims)
+                pdims[d] = ext
+                parts.append(s.parameter(len(params), "f32", pdims, _layout(g, rank)))
+                params.append(_values(g, "f32", math.prod(pdims)))
+            vals.append(s.concatenate(parts, d, "f32", dims))
+        else:
+            st = str(g.choice(list(_STORAGE)))
+            lo, hi = _STORAGE[st]
+            if g.random() < 0.5:
+                q = W.quant_type(st, [float(2.0 ** -int(g.integers(0, 4)))], [int(g.integers(lo, hi + 1))])
+            else:
+                qd = int(g.integers(rank))
+                n = dims[qd]
+                q = W.quant_type(st, [float(2.0 ** -int(k)) for k in g.integers(0, 4, n)],
+                                 [int(z) for z in g.integers(lo, hi + 1, n)], qdim=qd)
+            x = s.parameter(len(params), st, dims, quant=q)
+            params.append(_storage_values(g, st, math.prod(dims)))
+            vals.append(s.op("uniform_dequantize", [x], "f32", dims))
+    for _ in range(int(g.integers(0, 4))):
+        a, b = (int(i) for i in g.choice(len(vals), 2))
+        vals.append(s.binary(str(g.choice(["add", "subtract", "maximum", "minimum"])), vals[a], vals[b], "f32", dims))
+    r = vals[-1]
+    for v in vals[:-1]:
+        r = s.binary("add", r, v, "f32", dims)
+    end = str(g.choice(["quantize", "reduce", "none"]))
+    out_dims = dims
+    if end == "quantize":
+        st = str(g.choice(list(_STORAGE)))
+        lo, hi = _STORAGE[st]
+        q = W.quant_type(st, [float(g.choice([0.3, 0.5, 1.7, 2.0]))], [int(g.integers(lo, hi + 1))])
+        s.op("uniform_quantize", [r], st, dims, quant=q)
+    elif end == "reduce":
+        red = sorted(int(d) for d in g.choice(rank, int(g.integers(1, rank + 1)), replace=False))
+        out_dims = [dims[d] for d in range(rank) if d not in red]
+        reducer = str(g.choice(["add", "max", "min"]))
+        init = {"add": 0.0, "max": -np.inf, "min": np.inf}[reducer]
+        s.reduce(r, red, reducer, init, "f32", out_dims)
+    s.nodes[-1]["m2m"] = _layout(g, len(out_dims))
+    return s, params
+
+
+def _make(seed, series):
+    return random_wide_case(seed) if series == "wide" else random_case(seed, series == "hero")
+
+
 def _cases():
-    """(seed, hero_bias) of every case."""
-    return [(1000 + k, False) for k in range(N_CASES)] + [(2000 + k, True) for k in range(N_HERO)]
+    """(seed, series) of every case."""
+    return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
+            + [(3000 + k, "wide") for k in range(N_WIDE)])
 
 
 def test_random_fusions_plan_and_compile():
@@ -121,8 +211,8 @@ def test_random_fusions_plan_and_compile():
     import compiler_hlo_amd as H
     ran = skipped = 0
     heroes = collections.Counter()
-    for seed, bias in _cases():
-        s, params = random_case(seed, bias)
+    for seed, series in _cases():
+        s, params = _make(seed, series)
         try:
             f = H.Fusion(s.nodes, mode="compile")
         except H.FusionError as e:
@@ -132,21 +222,22 @@ def test_random_fusions_plan_and_compile():
         heroes[f.plan()["hero"]] += 1
         oracle.evaluate(s.nodes, params)
         ran += 1
-    total = N_CASES + N_HERO
+    total = N_CASES + N_HERO + N_WIDE
     assert ran >= total * 3 // 4, (ran, skipped)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
-    for seed, bias in _cases()[batch * BATCH:(batch + 1) * BATCH]:
-        s, params = random_case(seed, bias)
+    for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
+        s, params = _make(seed, series)
         try:
             H.Fusion(s.nodes, mode="plan")
         except H.FusionError:
             continue
         print("random fusion seed", seed, [nd["op"] for nd in s.nodes], flush=True)
         got, f = run_gpu(s.nodes, params)
-        assert_bitexact(got, oracle.evaluate(s.nodes, params), s.nodes[-1]["dtype"])
+        dt = s.nodes[-1]["dtype"]
+        assert_bitexact(got, oracle.evaluate(s.nodes, params), "u8" if dt in ("s4", "u4") else dt)
