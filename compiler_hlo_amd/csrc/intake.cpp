@@ -137,7 +137,8 @@ Type take_type(const hf_type &src, Graph &g, const Ctx &c) {
     if (t.dims[d] > 0 && n > (int64_t(1) << 40) / t.dims[d]) c.unsupported("array too large");
     n *= t.dims[d];
   }
-  if (storage_bytes(t.dt, n) >= (int64_t(1) << 31)) c.unsupported("array of 2 GiB or more");
+  // element indices of every array, byte offsets of the ones in memory (the
+  // parameters and the result: checked in intake)
   if (n >= (int64_t(1) << 31)) c.unsupported("array of 2^31 elements or more");
   if (src.quant) {
     const hf_quant &q = *src.quant;
@@ -274,6 +275,8 @@ Graph intake(const hf_fusion_desc *desc) {
       n.opd.push_back(o);
     }
     n.t = take_type(src.type, g, c);
+    if ((src.op == HF_PARAMETER || i == desc->root) && storage_bytes(n.t.dt, n.t.numel()) >= (int64_t(1) << 31))
+      c.unsupported("array of 2 GiB or more");
     if (src.n_attr < 0 || src.n_attr > HF_MAX_ATTR) c.invalid("n_attr out of range");
     for (int k = 0; k < src.n_attr; ++k) n.attr.push_back(src.attr[k]);
     n.param = src.parameter_number;

@@ -242,8 +242,10 @@ typedef struct {
 /* Validate, plan, generate, compile and load.  On success *out owns a handle
  * to free with hf_fusion_destroy.  Errors: HF_ERR_INVALID for a descriptor
  * that breaks an op's constraints (message names the node), HF_ERR_UNSUPPORTED
- * for a valid fusion this library does not implement, HF_ERR_COMPILE,
- * HF_ERR_HIP.  Nothing is left allocated on failure. */
+ * for a valid fusion this library does not implement (among them a parameter
+ * or result of 2 GiB or more, or any value of 2^31 elements or more: the
+ * kernels index with 32-bit offsets), HF_ERR_COMPILE, HF_ERR_HIP.  Nothing is
+ * left allocated on failure. */
 hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion **out);
 
 /* Copy the plan into *info. */

@@ -630,30 +630,68 @@ def test_empty_and_degenerate_shapes():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kind", ["loop", "transpose"])
+@pytest.mark.parametrize("kind", ["loop", "transpose", "transpose_narrow", "row_reduce", "column_reduce"])
 def test_largest_arrays_below_the_size_limit(kind):
     """f32[8191, 65536] is the largest 2-D f32 array below the 2 GiB limit:
-    32-bit offsets reach their maximum.  Sampled outputs against the oracle."""
-    n0, n1 = 8191, 65536
+    32-bit offsets reach their maximum.  f32[8188, 65536] (output rows a
+    multiple of four) takes the 32x128 transpose tiles.  Sampled outputs
+    against the oracle."""
+    n0, n1 = (8188 if kind == "transpose_narrow" else 8191), 65536
     say("largest arrays", kind, n0, n1)
     g = W.rng(92)
     x = W.uniform_f32(g, n0 * n1, -4.0, 4.0)
     s = W.Spec()
     p = s.parameter(0, "f32", [n0, n1])
     e = s.unary("exponential", p, "f32", [n0, n1])
-    if kind == "transpose":
+    if kind.startswith("transpose"):
         s.transpose(e, [1, 0], "f32", [n1, n0])
         odims = [n1, n0]
+    elif kind.endswith("reduce"):
+        d = 1 if kind == "row_reduce" else 0
+        s.reduce(e, [d], "add", 0.0, "f32", [n1 - d * (n1 - n0)])
     else:
         odims = [n0, n1]
     got, f = run_gpu(s.nodes, [x])
-    assert f.plan()["hero"] == kind
-    pts = np.stack([g.integers(0, odims[0], 20000), g.integers(0, odims[1], 20000)], 1)
-    pts = np.concatenate([pts, [[0, 0], [odims[0] - 1, odims[1] - 1], [odims[0] - 1, 0], [0, odims[1] - 1]]])
-    want, _ = oracle.evaluate_points(s.nodes, [x], pts)
-    lin = pts[:, 0] * odims[1] + pts[:, 1]
-    assert_ulp(got[lin], want.astype(np.float32), "f32", 2)
+    plan = f.plan()
+    assert plan["hero"] == kind.replace("_narrow", "")
+    if kind == "transpose_narrow":
+        assert (plan["tile_rows"], plan["tile_cols"], plan["block_threads"]) == (128, 32, 1024), plan
+    if kind.endswith("reduce"):
+        nout = n0 if kind == "row_reduce" else n1
+        idx = np.concatenate([g.integers(0, nout, 300 if kind == "row_reduce" else 3000), [0, nout - 1]])
+        _check_sum(got, s, [x], idx[:, None])
+    else:
+        pts = np.stack([g.integers(0, odims[0], 20000), g.integers(0, odims[1], 20000)], 1)
+        pts = np.concatenate([pts, [[0, 0], [odims[0] - 1, odims[1] - 1], [odims[0] - 1, 0], [0, odims[1] - 1]]])
+        want, _ = oracle.evaluate_points(s.nodes, [x], pts)
+        lin = pts[:, 0] * odims[1] + pts[:, 1]
+        assert_ulp(got[lin], want.astype(np.float32), "f32", 2)
     del x, got
+
+
+def test_largest_four_bit_array():
+    """s4[32767, 65536] requantized to u4 after a per-tensor dequantize: 2^31 -
+    65536 elements, the most below the 2^31 element limit, so nibble indices
+    and byte offsets both reach their maximum (the f32 values between, 8 GiB,
+    never reach memory).  Sampled outputs, bit-exact."""
+    n0, n1 = 32767, 65536
+    say("largest four-bit array", n0, n1)
+    g = W.rng(93)
+    q = np.frombuffer(bytearray(g.bytes(n0 * n1 // 2)), np.uint8)
+    s = W.Spec()
+    p = s.parameter(0, "s4", [n0, n1], quant=W.quant_type("s4", [0.25], [-1]))
+    d = s.op("uniform_dequantize", [p], "f32", [n0, n1])
+    s.op("uniform_quantize", [d], "u4", [n0, n1], quant=W.quant_type("u4", [0.5], [7]))
+    got, f = run_gpu(s.nodes, [q])
+    assert f.plan()["hero"] == "loop"
+    assert got.dtype == np.uint8 and got.size == n0 * n1 // 2
+    pts = np.stack([g.integers(0, n0, 20000), g.integers(0, n1, 20000)], 1)
+    pts = np.concatenate([pts, [[0, 0], [n0 - 1, n1 - 1], [n0 - 1, n1 - 2], [0, 1]]])
+    want, _ = oracle.evaluate_points(s.nodes, [q], pts)
+    lin = pts[:, 0] * n1 + pts[:, 1]
+    nib = (got[lin // 2] >> (4 * (lin % 2))) & 15
+    assert np.array_equal(nib.astype(np.float64), want)
+    del q, got
 
 
 # --------------------------------------------------------------------------

@@ -350,7 +350,32 @@ def test_size_limit():
     p = big.parameter(0, "f32", [8192, 65536])
     big.unary("exponential", p, "f32", [8192, 65536])
     st, msg = _status(big.nodes)
-    assert st == "HF_ERR_UNSUPPORTED" and "2 GiB" in msg
+    assert st == "HF_ERR_UNSUPPORTED" and "2 GiB" in msg and "node 0" in msg
+    # the byte limit holds for the arrays in memory only: an f32 value of
+    # 2 GiB or more between a bf16 parameter and a bf16 result is fine
+    mid = W.Spec()
+    p = mid.parameter(0, "bf16", [8192, 65536])
+    c = mid.convert(p, "f32", [8192, 65536])
+    mid.convert(mid.unary("exponential", c, "f32", [8192, 65536]), "bf16", [8192, 65536])
+    assert _status(mid.nodes) == ("HF_OK", "")
+    big_param = W.Spec()
+    p = big_param.parameter(0, "f32", [8192, 65536])
+    big_param.convert(p, "bf16", [8192, 65536])
+    st, msg = _status(big_param.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "2 GiB" in msg and "node 0" in msg
+    big_root = W.Spec()
+    p = big_root.parameter(0, "bf16", [8192, 65536])
+    big_root.convert(p, "f32", [8192, 65536])
+    st, msg = _status(big_root.nodes)
+    assert st == "HF_ERR_UNSUPPORTED" and "2 GiB" in msg and "node 1" in msg
+    # the element limit holds for every value
+    for n0, ok_want in ((32767, True), (32768, False)):
+        q = W.Spec()
+        p = q.parameter(0, "s4", [n0, 65536], quant=W.quant_type("s4", [0.25], [-1]))
+        d = q.op("uniform_dequantize", [p], "f32", [n0, 65536])
+        q.op("uniform_quantize", [d], "u4", [n0, 65536], quant=W.quant_type("u4", [0.5], [7]))
+        st, msg = _status(q.nodes)
+        assert (st == "HF_OK") == ok_want and (ok_want or "2^31 elements" in msg), (n0, st, msg)
 
 
 def test_index_transform_validation():
