@@ -370,11 +370,25 @@ Plan plan_loop(const Graph &g, Ctx c) {
   P.hero = HF_HERO_LOOP;
   const Type &rt = g.nodes[g.root].t;
   long long DL = c.lane >= 0 ? rt.dims[c.lane] : 1;
+  // Whether the fusion also reads small arrays along the columns (per-axis
+  // quantization parameters, a broadcast bias): every thread then holds V
+  // elements of each of them in registers.
+  bool small = false;
+  for (auto &pr : c.param_reads)
+    if (!is_streaming(g, pr.first)) small = true;
+  for (const Quant &q : g.quants)
+    if (q.qdim >= 0) small = true;
   int V = 1;
   if (c.lane >= 0 && !c.general) {
-    // 128-bit lanes for the widest of the result and the streaming inputs
+    // 128-bit lanes for the widest of the result and the streaming inputs,
+    // except where every stream is 4-bit and column data is read: 32 elements
+    // a lane then make few, register-heavy waves for what is mostly VALU work
+    // (the per-axis s4 requantize with a bias measured 10.8 us at 32, 8.8 at
+    // 16, 8.6 at 8 and 8.3 at 4 elements a lane; a per-tensor s4 requantize
+    // keeps 32: 6.7 us against 8.1 at 16).
     const int wbits = std::max(dtype_bits(rt.dt), stream_elem_bits(g, c));
-    V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", 128 / wbits), 128 / wbits)));
+    const int vdef = small && wbits <= 4 ? 4 : 128 / wbits;
+    V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", vdef), 128 / wbits)));
   }
   c.V = V;
   // A 4-bit result is stored a whole byte at a time: each lane needs an even
@@ -395,11 +409,6 @@ Plan plan_loop(const Graph &g, Ctx c) {
   // quantization parameters, a broadcast bias) shares that column data among
   // the waves through L1, and each thread keeps it in registers over four
   // rows, whose loads it issues together.
-  bool small = false;
-  for (auto &pr : c.param_reads)
-    if (!is_streaming(g, pr.first)) small = true;
-  for (const Quant &q : g.quants)
-    if (q.qdim >= 0) small = true;
   const long long tpr_cap = env_ll("HF_LOOP_TPR", 64);
   if (cols_v >= tpr_cap) {
     tpr = tpr_cap;
