@@ -86,7 +86,6 @@ struct Body {
   int tmp = 0;
   int nmem = 0;
   bool tile = false;
-  bool raw_root = false;  // the root's value is returned before its rounding
   bool rleaf = false;     // the context's leaf is a reduced value passed in (hf_rv)
 };
 
@@ -103,18 +102,14 @@ class Gen {
 
   // Emits (once) the struct, fetch and compute functions of the partition
   // rooted at `node` with lanes along `lane`; returns the function name.
-  // With `raw`, the root's own rounding to a 16-bit float type is left to the
-  // caller (which rounds and packs pairs in one step).
-  std::string fn(int ci, int node, int lane, bool raw = false) {
-    std::string name = "hf_c" + std::to_string(ci) + "_n" + std::to_string(node) + "_l" + std::to_string(lane + 1) +
-                       (raw ? "_raw" : "");
+  std::string fn(int ci, int node, int lane) {
+    std::string name = "hf_c" + std::to_string(ci) + "_n" + std::to_string(node) + "_l" + std::to_string(lane + 1);
     if (done_.count(name)) return name;
     done_[name] = true;
     const Ctx &c = P_.ctx[ci];
     const Type &t = g_.nodes[node].t;
     Body b;
     b.root = node;
-    b.raw_root = raw;
     b.lane = lane;
     b.V = c.V;
     b.tile = c.leaf >= 0 && P_.hero == HF_HERO_TRANSPOSE;
@@ -369,7 +364,7 @@ class Gen {
         a.push_back(val(ci, b, nd.opd[k], operand_index(g_, n, (int)k, E, &general)));
       }
       auto A0 = [&](const char *f) { return std::string(f) + "(" + a[0] + "[l])"; };
-      auto rnd = [&](hf_dtype dt, const std::string &e) { return b.raw_root && n == b.root ? e : hf::rnd(dt, e); };
+      auto rnd = [&](hf_dtype dt, const std::string &e) { return hf::rnd(dt, e); };
       const std::string x = a.empty() ? "" : a[0] + "[l]";
       const std::string y = a.size() > 1 ? a[1] + "[l]" : "";
       switch (nd.op) {
@@ -679,32 +674,7 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         else ix << "  (void)r;\n";
       }
       zero_dims(ix, it, set);
-      // A row sum of bf16 values converted to f32 (init not -0) accumulates
-      // packed bf16 pairs: the pair is rounded and packed by one conversion
-      // and added to the f32 accumulator by one two-term dot product with
-      // (1, 1), which keeps denormals and rounds like two f32 additions.  A
-      // zero sum is then always +0, the IEEE result when init is +0.
-      bool packed = false;
-      if (is_row && R.reducer == HF_REDUCER_ADD && !(R.init == 0.0 && std::signbit(R.init)) && c.V % 2 == 0 &&
-          env_flag("HF_RR_PACKED", true)) {
-        const Node &cv = g.nodes[P.rin];
-        if (cv.op == HF_CONVERT && cv.t.dt == HF_F32 && c.root == P.rin) {
-          const Type &yt = g.nodes[cv.opd[0]].t;
-          packed = yt.dt == HF_BF16 && yt.quant < 0;
-        }
-      }
-      if (is_row) glue << "#define HF_RR_PACKED " << (packed ? 1 : 0) << "\n";
-      if (packed) {
-        const int y = g.nodes[P.rin].opd[0];
-        std::string fy = gen.fn(0, y, c.lane, true);
-        types << "typedef hf_R_" << fy << " hf_regs_t;\n";
-        glue << "__device__ __forceinline__ void hf_rr_eval_fetch(const HfArgs &A, int row, int kv, hf_regs_t &R) {\n"
-             << ix.str() << "  " << fy << "_fetch(A" << call_args(it) << ", R);\n}\n";
-        glue << "__device__ __forceinline__ void hf_rr_eval(const HfArgs &A, int row, int kv, const hf_regs_t &R, "
-                "hf_u32 (&hf_res)[HF_V / 2]) {\n"
-             << ix.str() << "  float hf_y[HF_V];\n  " << fy << "(A" << call_args(it) << ", R, hf_y);\n"
-             << "#pragma unroll\n  for (int k = 0; k < HF_V / 2; ++k) hf_res[k] = hf_pack_bf16x2(hf_y[2 * k], hf_y[2 * k + 1]);\n}\n";
-      } else {
+      {
         std::string f = gen.fn(0, c.root, c.lane);
         types << "typedef hf_R_" << f << " hf_regs_t;\n";
         glue_pair(glue, is_row ? "hf_rr_eval" : "hf_cr_eval", is_row ? "int row, int kv" : "int r, int c", "hf_regs_t",

@@ -13,9 +13,8 @@
 // within lane groups by cross-lane shuffles.
 //
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
-// (vectors per row), HF_TPR, HF_RR_PACKED, hf_regs_t,
-// hf_rr_eval_fetch(A, row, kv, R), hf_rr_eval(A, row, kv, R, x) (HF_V floats,
-// or HF_V/2 packed bf16 pairs), hf_rr_store(A, row, acc); for max/argmax
+// (vectors per row), HF_TPR, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
+// hf_rr_eval(A, row, kv, R, x) (HF_V floats), hf_rr_store(A, row, acc); for max/argmax
 // (HF_OP 3) HF_ARG_V0, HF_ARG_K0 and hf_rr_store_arg(A, row, index).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
@@ -74,17 +73,6 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     }
   }
 #else
-#if HF_RR_PACKED
-  // The evaluated row elements arrive as packed bf16 pairs (a sum of bf16
-  // values converted to f32): one dot-product step adds a pair.
-  constexpr int NX = HF_V / 2;
-  typedef hf_u32 xval_t;
-  auto acc_add = [](float a, hf_u32 x) { return hf_acc_bf16x2(a, x); };
-#else
-  constexpr int NX = HF_V;
-  typedef float xval_t;
-  auto acc_add = [](float a, float x) { return hf_red<HF_OP>(a, x); };
-#endif
 #if HF_TPR == HF_BLOCK
   // Two result slots, alternating between a workgroup's consecutive steps, so
   // that one barrier per step is enough.
@@ -93,12 +81,12 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int ITERS = (HF_KV + HF_BLOCK - 1) / HF_BLOCK;
   // acc[r] holds row row0 + r; rows past the end are neither read nor stored
-  auto finish = [&](int row0, const float (&acc)[RR][NX], int slot) {
+  auto finish = [&](int row0, const float (&acc)[RR][HF_V], int slot) {
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
       float s = acc[r][0];
 #pragma unroll
-      for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[r][v]);
+      for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[r][v]);
       s = hf_wave_reduce<HF_OP>(s);
       if (lane == 0) part[slot][r][wave] = s;
     }
@@ -130,20 +118,20 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     auto consume = [&](int row, int k, const hf_regs_t(&R)[ITERS], int slot) {
       float s = hf_red_identity<HF_OP>();
       {
-        xval_t x[NX];
+        float x[HF_V];
         hf_rr_eval(A, row, (int)threadIdx.x, R[0], x);
-        float acc[NX];
+        float acc[HF_V];
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[v] = acc_add(hf_red_identity<HF_OP>(), x[v]);
+        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(hf_red_identity<HF_OP>(), x[v]);
 #pragma unroll
         for (int b = 1; b < ITERS; ++b) {
           hf_rr_eval(A, row, b * HF_BLOCK + (int)threadIdx.x, R[b], x);
 #pragma unroll
-          for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+          for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
         }
         s = acc[0];
 #pragma unroll
-        for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
+        for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[v]);
       }
       s = hf_wave_reduce<HF_OP>(s);
       if (lane == 0) part[slot][0][wave] = s;
@@ -191,11 +179,11 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     constexpr int NB = ITERS < NB0 ? ITERS : NB0;
     int slot = 0;
     for (int row0 = blockIdx.x * RR; row0 < HF_ROWS; row0 += gridDim.x * RR, slot ^= 1) {
-      float acc[RR][NX];
+      float acc[RR][HF_V];
 #pragma unroll
       for (int r = 0; r < RR; ++r)
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[r][v] = hf_red_identity<HF_OP>();
+        for (int v = 0; v < HF_V; ++v) acc[r][v] = hf_red_identity<HF_OP>();
       for (int it0 = 0; it0 < ITERS; it0 += NB) {
         hf_regs_t R[RR][NB];
 #pragma unroll
@@ -210,10 +198,10 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
 #pragma unroll
           for (int r = 0; r < RR; ++r) {
             if ((RR == 1 || row0 + r < HF_ROWS) && (ITERS % NB == 0 || it0 + b < ITERS)) {
-              xval_t x[NX];
+              float x[HF_V];
               hf_rr_eval(A, row0 + r, (it0 + b) * HF_BLOCK + (int)threadIdx.x, R[r][b], x);
 #pragma unroll
-              for (int v = 0; v < NX; ++v) acc[r][v] = acc_add(acc[r][v], x[v]);
+              for (int v = 0; v < HF_V; ++v) acc[r][v] = hf_red<HF_OP>(acc[r][v], x[v]);
             }
           }
         }
@@ -226,16 +214,16 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     static_assert(RR == 1, "rows of unequal chunks take one row per step");
     int slot = 0;
     for (int row = blockIdx.x; row < HF_ROWS; row += gridDim.x, slot ^= 1) {
-      float acc[1][NX];
+      float acc[1][HF_V];
 #pragma unroll
-      for (int v = 0; v < NX; ++v) acc[0][v] = hf_red_identity<HF_OP>();
+      for (int v = 0; v < HF_V; ++v) acc[0][v] = hf_red_identity<HF_OP>();
       for (int kv = threadIdx.x; kv < HF_KV; kv += HF_BLOCK) {
         hf_regs_t R1;
         hf_rr_eval_fetch(A, row, kv, R1);
-        xval_t x[NX];
+        float x[HF_V];
         hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[0][v] = acc_add(acc[0][v], x[v]);
+        for (int v = 0; v < HF_V; ++v) acc[0][v] = hf_red<HF_OP>(acc[0][v], x[v]);
       }
       finish(row, acc, slot);
     }
@@ -247,22 +235,22 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
   const int rloc = threadIdx.x / HF_TPR;
   for (int row0 = blockIdx.x * RPB; row0 < HF_ROWS; row0 += gridDim.x * RPB) {
     const int row = row0 + rloc;
-    float acc[NX];
+    float acc[HF_V];
 #pragma unroll
-    for (int v = 0; v < NX; ++v) acc[v] = hf_red_identity<HF_OP>();
+    for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
     if (row < HF_ROWS) {
       for (int kv = sub; kv < HF_KV; kv += HF_TPR) {
         hf_regs_t R1;
         hf_rr_eval_fetch(A, row, kv, R1);
-        xval_t x[NX];
+        float x[HF_V];
         hf_rr_eval(A, row, kv, R1, x);
 #pragma unroll
-        for (int v = 0; v < NX; ++v) acc[v] = acc_add(acc[v], x[v]);
+        for (int v = 0; v < HF_V; ++v) acc[v] = hf_red<HF_OP>(acc[v], x[v]);
       }
     }
     float s = acc[0];
 #pragma unroll
-    for (int v = 1; v < NX; ++v) s = hf_red<HF_OP>(s, acc[v]);
+    for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[v]);
     s = hf_group_reduce<HF_OP, HF_TPR>(s);
     if (sub == 0 && row < HF_ROWS) hf_rr_store(A, row, s);
   }

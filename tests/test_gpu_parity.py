@@ -370,6 +370,28 @@ def test_row_reduce_pipelined_option(monkeypatch):
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
 
 
+@pytest.mark.parametrize("rows", [0, 1, 2, 3, 130])
+def test_row_reduce_bf16_short_rows(rows):
+    """Sums of short bf16 rows (2 to 32 lanes per row, rank-0 results among
+    them), integer-valued so that every order gives the same f32: bit-exact.
+    A single row of 8 once came out as +0: the packed accumulate read a
+    v_dot2c_f32_bf16 result too soon after the instruction."""
+    g = W.rng(96 + rows)
+    for cols in (4, 8, 12, 16, 24, 40, 64, 128):
+        for double in (False, True):
+            shape = [cols] if rows == 0 else [rows, cols]
+            s = W.Spec()
+            p = s.parameter(0, "bf16", shape)
+            y = s.binary("add", p, p, "bf16", shape) if double else p
+            c = s.convert(y, "f32", shape)
+            s.reduce(c, [len(shape) - 1], "add", 0.0, "f32", shape[:-1])
+            v = W.integers(g, int(np.prod(shape)), -8, 8, np.int64).astype(np.float32)
+            x = (v.view(np.uint32) >> 16).astype(np.uint16)
+            got, f = run_gpu(s.nodes, [x])
+            assert f.plan()["hero"] == "row_reduce"
+            assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
 def test_row_reduce_bf16_intermediates_loop():
     """The reduce operand y = add(exp x, b) itself (a bf16 loop fusion) is
     within 1 bf16 ulp of the oracle elementwise."""
