@@ -21,9 +21,9 @@ import oracle
 import workloads as W
 from harness import assert_bitexact, run_gpu
 
-N_CASES = 96        # seeds 1000.. : any shape
-N_HERO = 48         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
-N_WIDE = 48         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
+N_CASES = 192       # seeds 1000.. : any shape
+N_HERO = 96         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
+N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
 BATCH = 24
 
 
