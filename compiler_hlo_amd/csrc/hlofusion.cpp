@@ -12,6 +12,7 @@
 #include <fstream>
 #include <map>
 #include <memory>
+#include <atomic>
 #include <mutex>
 #include <sstream>
 #include <string>
@@ -141,7 +142,10 @@ hf_status compile(const std::string &src, std::vector<char> *code) {
     return HF_ERR_COMPILE;
   }
   if (!cpath.empty()) {
-    std::string tmp = cpath + ".tmp" + std::to_string((long)getpid());
+    // unique per process and call: threads of one process may compile the
+    // same source at once
+    static std::atomic<unsigned long> tmp_seq{0};
+    std::string tmp = cpath + ".tmp" + std::to_string((long)getpid()) + "." + std::to_string(tmp_seq.fetch_add(1));
     std::ofstream f(tmp, std::ios::binary);
     f.write(code->data(), (std::streamsize)code->size());
     f.close();

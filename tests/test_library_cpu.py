@@ -584,3 +584,36 @@ def test_reciprocal_double_quotient_equals_ieee_f32_division():
             y2 = (yy.view(np.int32) + off).view(np.float32)
             got = (y2.astype(np.float64) * (1.0 / np.float64(s))).astype(np.float32)
             assert np.array_equal(got.view(np.uint32), (y2 / s).view(np.uint32))
+
+
+def test_code_object_cache_dir_under_concurrent_creates(tmp_path, monkeypatch):
+    """HF_CACHE_DIR: eight threads compile the same three fusions at once.
+    Each distinct source leaves exactly one code object and no temporary
+    file; a fresh process then creates the same fusions from the directory."""
+    import os
+    import subprocess
+    import sys
+    from concurrent.futures import ThreadPoolExecutor
+    monkeypatch.setenv("HF_CACHE_DIR", str(tmp_path))
+    specs = []
+    for n in (1000, 1001, 1002):   # sizes that no other test compiles in this process
+        s = W.Spec()
+        p = s.parameter(0, "f32", [n])
+        s.unary("exponential", p, "f32", [n])
+        specs.append(s)
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        plans = list(pool.map(lambda k: H.Fusion(specs[k % 3].nodes, mode="compile").plan()["hero"], range(24)))
+    assert plans == ["loop"] * 24
+    files = sorted(os.listdir(tmp_path))
+    assert len(files) == 3 and all(f.endswith(".co") for f in files), files
+    code = ("import sys; sys.path.insert(0, %r); import compiler_hlo_amd as H, workloads as W\n"
+            "for n in (1000, 1001, 1002):\n"
+            "    s = W.Spec(); p = s.parameter(0, 'f32', [n]); s.unary('exponential', p, 'f32', [n])\n"
+            "    assert H.Fusion(s.nodes, mode='compile').plan()['hero'] == 'loop'\n"
+            "print('ok')\n") % ROOT
+    stamps = {f: os.stat(tmp_path / f).st_mtime_ns for f in files}
+    env = dict(os.environ, HF_CACHE_DIR=str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+    # read from the directory, not compiled and written again
+    assert {f: os.stat(tmp_path / f).st_mtime_ns for f in os.listdir(tmp_path)} == stamps

@@ -10,7 +10,13 @@ result, sums included, is exact: the comparison is bit-exact.  Fusions the
 library does not implement (a reduce whose dims are neither physically minor
 nor physically major) are counted and skipped.
 
-The CPU test plans and compiles every case for gfx950; the GPU tests run them.
+Four series: any shape; tile-sized shapes biased toward the transpose and
+column-reduce heroes; pad, concatenate and quantized storage; and big shapes
+(dims up to 16384, up to 4M elements) for the whole-workgroup row paths, many
+column segments and the wide transpose tiles.
+
+The CPU test plans and compiles every case for gfx950 (and runs the oracle on
+all but the big ones); the GPU tests run them.
 """
 import math
 
@@ -24,6 +30,7 @@ from harness import assert_bitexact, run_gpu
 N_CASES = 192       # seeds 1000.. : any shape
 N_HERO = 96         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
 N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
+N_BIG = 24          # seeds 4000.. : dims up to 16384, 0.2M-4M elements
 BATCH = 24
 
 
@@ -36,17 +43,24 @@ def _values(g, dtype, n):
     return (v.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else v
 
 
-def random_case(seed, hero_bias=False):
+def random_case(seed, hero_bias=False, big=False):
     """(spec, params) of one random fusion.  With hero_bias the shapes are
     tile-sized, the first parameter is read transposed and reductions favour
     the physically major dims, so that the transpose and column-reduce heroes
-    come up often."""
+    come up often.  With big (and hero_bias) the dims reach 16384 and the
+    arrays 4M elements: whole-workgroup rows, many column segments and the
+    wide transpose tiles."""
     g = W.rng(seed)
     rank = int(g.integers(2, 4)) if hero_bias else int(g.integers(1, 4))
-    sizes = [33, 64, 96, 130, 257] if hero_bias else [1, 2, 3, 5, 8, 17, 33, 64, 96, 130]
+    if big:
+        sizes, cap = [2, 7, 64, 130, 1024, 2048, 4100, 8192, 16384], 4_000_000
+    elif hero_bias:
+        sizes, cap = [33, 64, 96, 130, 257], 100_000
+    else:
+        sizes, cap = [1, 2, 3, 5, 8, 17, 33, 64, 96, 130], 100_000
     while True:
         dims = [int(g.choice(sizes)) for _ in range(rank)]
-        if math.prod(dims) <= 100_000:
+        if math.prod(dims) <= cap and (not big or math.prod(dims) >= 200_000):
             break
     dt = "f32" if g.random() < 0.6 else "bf16"
     with_reduce = g.random() < 0.4
@@ -197,38 +211,49 @@ def random_wide_case(seed):
 
 
 def _make(seed, series):
-    return random_wide_case(seed) if series == "wide" else random_case(seed, series == "hero")
+    if series == "wide":
+        return random_wide_case(seed)
+    return random_case(seed, series in ("hero", "big"), series == "big")
 
 
 def _cases():
     """(seed, series) of every case."""
     return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
-            + [(3000 + k, "wide") for k in range(N_WIDE)])
+            + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)])
 
 
 def test_random_fusions_plan_and_compile():
+    """Every case plans and compiles (in parallel: create is thread-safe and
+    releases the GIL), unsupported ones fail with HF_ERR_UNSUPPORTED only, and
+    all four heroes come up."""
     import collections
+    import os
+    from concurrent.futures import ThreadPoolExecutor
     import compiler_hlo_amd as H
-    ran = skipped = 0
-    heroes = collections.Counter()
-    for seed, series in _cases():
-        s, params = _make(seed, series)
+    cases = [(seed, series) + _make(seed, series) for seed, series in _cases()]
+
+    def create(case):
+        seed, series, s, params = case
         try:
-            f = H.Fusion(s.nodes, mode="compile")
+            return H.Fusion(s.nodes, mode="compile").plan()["hero"]
         except H.FusionError as e:
             assert e.status == "HF_ERR_UNSUPPORTED", (seed, str(e))
-            skipped += 1
-            continue
-        heroes[f.plan()["hero"]] += 1
-        oracle.evaluate(s.nodes, params)
-        ran += 1
-    total = N_CASES + N_HERO + N_WIDE
-    assert ran >= total * 3 // 4, (ran, skipped)
+            return None
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as pool:
+        heroes_of = list(pool.map(create, cases))
+    heroes = collections.Counter(h for h in heroes_of if h)
+    for (seed, series, s, params), h in zip(cases, heroes_of):
+        if h and series != "big":  # the big cases' oracle runs with their GPU test
+            oracle.evaluate(s.nodes, params)
+    ran = sum(1 for h in heroes_of if h)
+    total = N_CASES + N_HERO + N_WIDE + N_BIG
+    assert ran >= total * 3 // 4, (ran, total - ran)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
