@@ -54,11 +54,6 @@ hf_dtype zp_dtype(hf_dtype storage) {
 }
 const char *rtype(const Type &t) { return reg_is_float(t) ? "float" : "int"; }
 
-bool env_flag(const char *name, bool dflt) {  // tuning and A/B switches
-  const char *v = std::getenv(name);
-  return v ? std::atoi(v) != 0 : dflt;
-}
-
 std::string rnd(hf_dtype dt, const std::string &x) {
   if (dt == HF_BF16) return "hf_rnd_bf16(" + x + ")";
   if (dt == HF_F16) return "hf_rnd_f16(" + x + ")";

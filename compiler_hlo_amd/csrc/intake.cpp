@@ -109,7 +109,7 @@ std::string dims_str(const Type &t) {
 Type take_type(const hf_type &src, Graph &g, const Ctx &c) {
   Type t;
   if (!valid_dtype(src.dtype)) c.invalid("unknown element type");
-  t.dt = src.dtype;
+  t.dt = (hf_dtype)src.dtype;
   if (src.rank < 0 || src.rank > HF_MAX_RANK) c.invalid("rank out of range [0, 8]");
   t.rank = src.rank;
   for (int d = 0; d < t.rank; ++d) {
@@ -263,11 +263,13 @@ Graph intake(const hf_fusion_desc *desc) {
 
   for (int i = 0; i < desc->n_nodes; ++i) {
     const hf_node &src = desc->nodes[i];
-    Ctx c{i, src.op};
+    // the enum-valued fields are plain integers at the boundary: each is
+    // range-checked before it becomes an enum
     if (src.op < HF_PARAMETER || src.op > HF_CONCATENATE)
       fail(HF_ERR_INVALID, "node " + std::to_string(i) + ": unknown op");
+    Ctx c{i, (hf_op)src.op};
     Node &n = g.nodes[i];
-    n.op = src.op;
+    n.op = (hf_op)src.op;
     if (src.n_operands < 0 || src.n_operands > HF_MAX_OPERANDS) c.invalid("n_operands out of range");
     for (int k = 0; k < src.n_operands; ++k) {
       int o = src.operands[k];
@@ -281,7 +283,8 @@ Graph intake(const hf_fusion_desc *desc) {
     for (int k = 0; k < src.n_attr; ++k) n.attr.push_back(src.attr[k]);
     n.param = src.parameter_number;
     n.cst = src.constant;
-    n.reducer = src.reducer;
+    n.reducer = src.reducer >= HF_REDUCER_ADD && src.reducer <= HF_REDUCER_ARGMAX ? (hf_reducer)src.reducer
+                                                                                  : HF_REDUCER_ADD;  // checked if HF_REDUCE
     n.init = src.init_value;
 
     const Type &t = n.t;
@@ -460,10 +463,10 @@ Graph intake(const hf_fusion_desc *desc) {
         break;
       case HF_REDUCE: {
         if (src.reducer < HF_REDUCER_ADD || src.reducer > HF_REDUCER_ARGMAX) c.invalid("unknown reducer");
+        need_operands(src, src.reducer == HF_REDUCER_ARGMAX ? 2 : 1, c);
         const Type &o = opt(0);
         if (src.reducer == HF_REDUCER_ARGMAX) {
           // variadic max/argmax: {values, indices} -> the index of the maximum
-          need_operands(src, 2, c);
           const Node &ix = g.nodes[n.opd[1]];
           if (!is_float(o.dt) || o.quant >= 0) c.unsupported("argmax values must be floating point");
           if (!ix.t.same_shape(o)) c.invalid("all inputs must have the same dimensions");
@@ -474,7 +477,6 @@ Graph intake(const hf_fusion_desc *desc) {
           if (n.cst != std::floor(n.cst) || n.cst < INT32_MIN || n.cst > INT32_MAX)
             c.invalid("the index init value must be an s32 value");
         } else {
-          need_operands(src, 1, c);
           if (t.dt != o.dt)
             c.invalid("element_type(inputs) = element_type(init_values) = result type violated (C2, C8)");
           if (!is_float(t.dt) || o.quant >= 0) c.unsupported("only floating-point reductions are supported");

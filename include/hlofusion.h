@@ -176,7 +176,7 @@ typedef struct {
  * layout {rank-1, ..., 0} ("Default minor-to-major ordering").  Layouts are
  * physical only for parameters and the root; other nodes are virtual. */
 typedef struct {
-  hf_dtype dtype;
+  int32_t dtype;                          /* an hf_dtype value */
   int32_t rank;                           /* 0 .. HF_MAX_RANK */
   int64_t dims[HF_MAX_RANK];              /* >= 0; size 0 is valid */
   int32_t has_layout;
@@ -187,7 +187,7 @@ typedef struct {
 /* One node of the fusion computation.  Operands are indices of EARLIER nodes
  * (the array is in topological order). */
 typedef struct {
-  hf_op op;
+  int32_t op;                   /* an hf_op value */
   int32_t n_operands;
   int32_t operands[HF_MAX_OPERANDS];
   hf_type type;                 /* result type, stated explicitly */
@@ -197,7 +197,7 @@ typedef struct {
   int64_t attr[HF_MAX_ATTR];    /* permutation | broadcast_dimensions | dimensions |
                                    iota_dimension | pad's low, high, interior |
                                    concatenate's dimension */
-  hf_reducer reducer;           /* HF_REDUCE */
+  int32_t reducer;              /* HF_REDUCE: an hf_reducer value */
   double init_value;            /* HF_REDUCE (for HF_REDUCER_ARGMAX: the value
                                    init; `constant` holds the index init) */
 } hf_node;
