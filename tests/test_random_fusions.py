@@ -10,10 +10,12 @@ result, sums included, is exact: the comparison is bit-exact.  Fusions the
 library does not implement (a reduce whose dims are neither physically minor
 nor physically major) are counted and skipped.
 
-Four series: any shape; tile-sized shapes biased toward the transpose and
-column-reduce heroes; pad, concatenate and quantized storage; and big shapes
-(dims up to 16384, up to 4M elements) for the whole-workgroup row paths, many
-column segments and the wide transpose tiles.
+Four bit-exact series: any shape; tile-sized shapes biased toward the
+transpose and column-reduce heroes; pad, concatenate and quantized storage;
+and big shapes (dims up to 16384, up to 4M elements) for the whole-workgroup
+row paths, many column segments and the wide transpose tiles.  A fifth
+series puts one exp, log or tanh among exactly rounding ops and compares
+within the bound the result allows.
 
 The CPU test plans and compiles every case for gfx950 (and runs the oracle on
 all but the big ones); the GPU tests run them.
@@ -31,6 +33,7 @@ N_CASES = 192       # seeds 1000.. : any shape
 N_HERO = 96         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
 N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
 N_BIG = 24          # seeds 4000.. : dims up to 16384, 0.2M-4M elements
+N_TRANS = 48        # seeds 5000.. : one exp, log or tanh, compared within its bound
 BATCH = 24
 
 
@@ -210,6 +213,82 @@ def random_wide_case(seed):
     return s, params
 
 
+def random_trans_case(seed):
+    """(spec, params, check): one exp, log or tanh (f32 or bf16) inside a
+    random fusion, between exactly rounding ops.  Its operand is exact
+    (a parameter read plainly, transposed or reversed, maybe added to a
+    second one; abs(.) + 1 for log); after it come an optional negate or abs,
+    an optional convert, and an optional reduce.  check(got, spec, params)
+    compares with the bound the result allows: 2 f32 ulp (the transcendental's
+    own), 1 bf16 ulp once a bf16 rounding follows it, and for a sum the
+    summation bound 2^-20 * sum|terms|."""
+    g = W.rng(seed)
+    rank = int(g.integers(1, 4))
+    while True:
+        dims = [int(g.choice([1, 2, 3, 5, 8, 17, 33, 64, 96, 130, 257])) for _ in range(rank)]
+        if math.prod(dims) <= 100_000:
+            break
+    dt = "f32" if g.random() < 0.6 else "bf16"
+    s = W.Spec()
+    params, vals = [], []
+    for p in range(int(g.integers(1, 3))):
+        kind = str(g.choice(["plain", "transpose", "reverse"]))
+        if kind == "transpose" and rank > 1:
+            perm = [int(d) for d in g.permutation(rank)]
+            pdims = [0] * rank
+            for d in range(rank):
+                pdims[perm[d]] = dims[d]
+            x = s.transpose(s.parameter(p, dt, pdims, _layout(g, rank)), perm, dt, dims)
+        elif kind == "reverse":
+            rd = sorted(int(d) for d in g.choice(rank, int(g.integers(1, rank + 1)), replace=False))
+            x = s.reverse(s.parameter(p, dt, dims, _layout(g, rank)), rd, dt, dims)
+        else:
+            x = s.parameter(p, dt, dims, _layout(g, rank))
+        vals.append(x)
+        params.append(_values(g, dt, math.prod(dims)))
+    x = vals[0] if len(vals) == 1 else s.binary(str(g.choice(["add", "maximum"])), vals[0], vals[1], dt, dims)
+    op = str(g.choice(["exponential", "log", "tanh"]))
+    if op == "log":
+        x = s.binary("add", s.unary("abs", x, dt, dims), s.constant(1.0, dt, dims), dt, dims)
+    y = s.unary(op, x, dt, dims)
+    if g.random() < 0.4:
+        y = s.unary(str(g.choice(["negate", "abs"])), y, dt, dims)
+    cur = dt
+    if g.random() < 0.3:
+        cur = "bf16" if dt == "f32" else "f32"
+        y = s.convert(y, cur, dims)
+    tol_dt = "bf16" if "bf16" in (dt, cur) else "f32"
+    red = None
+    out_dims = dims
+    if g.random() < 0.4:
+        red = sorted(int(d) for d in g.choice(rank, int(g.integers(1, rank + 1)), replace=False))
+        reducer = str(g.choice(["add", "max", "min"]))
+        if reducer == "add" and cur != "f32":
+            cur = "f32"
+            y = s.convert(y, cur, dims)
+        out_dims = [dims[d] for d in range(rank) if d not in red]
+        init = {"add": 0.0, "max": -np.inf, "min": np.inf}[reducer]
+        s.reduce(y, red, reducer, init, cur, out_dims)
+    s.nodes[-1]["m2m"] = _layout(g, len(out_dims))
+    is_sum = red is not None and s.nodes[-1]["reducer"] == "add"
+
+    def check(got):
+        import itertools
+        if not is_sum:
+            from harness import assert_ulp
+            assert_ulp(got, oracle.evaluate(s.nodes, params), cur, 1 if tol_dt == "bf16" else 2)
+            return
+        rn = s.nodes[-1]
+        pts = (np.array(list(itertools.product(*[range(d) for d in out_dims])), dtype=np.int64)
+               if out_dims else np.zeros((1, 0), np.int64))
+        vals_, aux = oracle.evaluate_points(s.nodes, params, pts)
+        lin = oracle.linear_indices(out_dims, rn["m2m"] or oracle.default_m2m(len(out_dims)), pts) if out_dims else np.zeros(1, np.int64)
+        gv = got[lin].astype(np.float64)
+        bound = 2.0 ** -20 * aux[:, 0] + (2.0 ** -8 if tol_dt == "bf16" else 0.0) * aux[:, 0]
+        assert np.all(np.abs(gv - aux[:, 1]) <= bound), float(np.max(np.abs(gv - aux[:, 1]) - bound))
+    return s, params, check
+
+
 def _make(seed, series):
     if series == "wide":
         return random_wide_case(seed)
@@ -266,3 +345,35 @@ def test_random_fusions_gpu(batch):
         got, f = run_gpu(s.nodes, params)
         dt = s.nodes[-1]["dtype"]
         assert_bitexact(got, oracle.evaluate(s.nodes, params), "u8" if dt in ("s4", "u4") else dt)
+
+
+def test_random_transcendental_fusions_plan_and_check_oracle():
+    """Every transcendental case plans (or is HF_ERR_UNSUPPORTED), and each
+    case's checker accepts the oracle's own result."""
+    import compiler_hlo_amd as H
+    planned = 0
+    for k in range(N_TRANS):
+        s, params, check = random_trans_case(5000 + k)
+        try:
+            H.Fusion(s.nodes, mode="plan")
+        except H.FusionError as e:
+            assert e.status == "HF_ERR_UNSUPPORTED", (5000 + k, str(e))
+            continue
+        planned += 1
+        check(oracle.evaluate(s.nodes, params))
+    assert planned >= N_TRANS * 3 // 4
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", range(N_TRANS // BATCH))
+def test_random_transcendental_fusions_gpu(batch):
+    import compiler_hlo_amd as H
+    for k in range(batch * BATCH, (batch + 1) * BATCH):
+        s, params, check = random_trans_case(5000 + k)
+        try:
+            H.Fusion(s.nodes, mode="plan")
+        except H.FusionError:
+            continue
+        print("random transcendental fusion seed", 5000 + k, [nd["op"] for nd in s.nodes], flush=True)
+        got, _ = run_gpu(s.nodes, params)
+        check(got)
