@@ -3,8 +3,8 @@
 Each case is a random graph over a rank 1-3 output space with random
 minor_to_major layouts: parameters read directly, transposed, broadcast or
 reversed, chains of elementwise ops that round identically on both sides
-(add, subtract, multiply, maximum, minimum, negate, abs, f32 <-> bf16
-converts), and sometimes a reduce (add over integer-valued f32, or max/min)
+(add, subtract, multiply, maximum, minimum, negate, abs, converts between
+f32 and bf16 or f16), and sometimes a reduce (add over integer-valued f32, or max/min)
 followed by an elementwise epilogue.  Inputs are small integers, so every
 result, sums included, is exact: the comparison is bit-exact.  Fusions the
 library does not implement (a reduce whose dims are neither physically minor
@@ -43,7 +43,15 @@ def _layout(g, rank):
 
 def _values(g, dtype, n):
     v = W.integers(g, n, -8, 8, np.int64).astype(np.float32)
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
     return (v.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else v
+
+
+def _half(seed, dt):
+    """A 16-bit float type becomes f16 for some seeds (drawn from a stream of
+    its own, so that every other draw of the case stays as it was)."""
+    return "f16" if dt == "bf16" and W.rng(seed + 7_000_000).random() < 0.4 else dt
 
 
 def random_case(seed, hero_bias=False, big=False):
@@ -65,7 +73,7 @@ def random_case(seed, hero_bias=False, big=False):
         dims = [int(g.choice(sizes)) for _ in range(rank)]
         if math.prod(dims) <= cap and (not big or math.prod(dims) >= 200_000):
             break
-    dt = "f32" if g.random() < 0.6 else "bf16"
+    dt = _half(seed, "f32" if g.random() < 0.6 else "bf16")
     with_reduce = g.random() < 0.4
     s = W.Spec()
     params, vals = [], []
@@ -107,7 +115,7 @@ def random_case(seed, hero_bias=False, big=False):
         r = s.binary("add", r, v, dt, dims)
     cur = dt
     if g.random() < 0.3:
-        cur = "bf16" if dt == "f32" else "f32"
+        cur = _half(seed + 1, "bf16") if dt == "f32" else "f32"
         r = s.convert(r, cur, dims)
     out_dims = dims
     if with_reduce:
