@@ -72,7 +72,7 @@ uint64_t fnv1a(const std::string &s, uint64_t h = 1469598103934665603ull) {
 // the op semantics define), no fast-math, packed FP32 instructions disabled.
 const std::vector<const char *> &rtc_options() {
   static const std::vector<const char *> o = {
-      "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+      "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-fno-slp-vectorize",
       "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"};
   return o;
 }

@@ -392,6 +392,17 @@ def test_row_reduce_bf16_short_rows(rows):
             assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
 
 
+def test_f16_chain_that_crashed_the_device_compiler():
+    """The f16 negate/multiply chain on a rank-5 transposed read whose kernel
+    once aborted the device compiler: now bit-exact against the oracle."""
+    from test_library_cpu import _f16_negate_multiply_chain
+    s = _f16_negate_multiply_chain()
+    v = W.integers(W.rng(97), 17 * 4 * 3 * 16, -8, 8, np.int64).astype(np.float16)
+    x = v.view(np.uint16)
+    got, f = run_gpu(s.nodes, [x])
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f16")
+
+
 def test_row_reduce_bf16_intermediates_loop():
     """The reduce operand y = add(exp x, b) itself (a bf16 loop fusion) is
     within 1 bf16 ulp of the oracle elementwise."""

@@ -617,3 +617,25 @@ def test_code_object_cache_dir_under_concurrent_creates(tmp_path, monkeypatch):
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
     # read from the directory, not compiled and written again
     assert {f: os.stat(tmp_path / f).st_mtime_ns for f in os.listdir(tmp_path)} == stamps
+
+
+def _f16_negate_multiply_chain():
+    """An f16 chain (negate, subtract, multiply, adds) on a rank-5 transposed
+    read: with SLP vectorization on, the device compiler aborted on it
+    ("Cannot select" of an i32 -> v2f32 bitcast) under -packed-fp32-ops."""
+    dims_in, dims = [17, 4, 3, 16, 1], [16, 3, 4, 17, 1]
+    s = W.Spec()
+    p = s.parameter(0, "f16", dims_in)
+    t = s.transpose(p, [3, 2, 1, 0, 4], "f16", dims)
+    n = s.unary("negate", t, "f16", dims)
+    d = s.binary("subtract", t, n, "f16", dims)
+    m = s.binary("multiply", d, n, "f16", dims)
+    a = s.binary("add", m, t, "f16", dims)
+    b = s.binary("add", a, n, "f16", dims)
+    s.binary("add", b, d, "f16", dims, m2m=[0, 3, 4, 2, 1])
+    return s
+
+
+def test_f16_chain_that_crashed_the_device_compiler_compiles():
+    f = H.Fusion(_f16_negate_multiply_chain().nodes, mode="compile")
+    assert f.plan()["hero"] == "loop"

@@ -10,10 +10,11 @@ result, sums included, is exact: the comparison is bit-exact.  Fusions the
 library does not implement (a reduce whose dims are neither physically minor
 nor physically major) are counted and skipped.
 
-Four bit-exact series: any shape; tile-sized shapes biased toward the
+Five bit-exact series: any shape; tile-sized shapes biased toward the
 transpose and column-reduce heroes; pad, concatenate and quantized storage;
-and big shapes (dims up to 16384, up to 4M elements) for the whole-workgroup
-row paths, many column segments and the wide transpose tiles.  A fifth
+big shapes (dims up to 16384, up to 4M elements) for the whole-workgroup
+row paths, many column segments and the wide transpose tiles; and rank 4-6
+spaces with size-1 dims, for layout normalisation.  A sixth
 series puts one exp, log or tanh among exactly rounding ops and compares
 within the bound the result allows.
 
@@ -33,6 +34,7 @@ N_CASES = 192       # seeds 1000.. : any shape
 N_HERO = 96         # seeds 2000.. : tile-sized shapes, a transposed read, major-dim reduces
 N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
 N_BIG = 24          # seeds 4000.. : dims up to 16384, 0.2M-4M elements
+N_RANK = 24         # seeds 6000.. : rank 4-6 with size-1 dims
 N_TRANS = 48        # seeds 5000.. : one exp, log or tanh, compared within its bound
 BATCH = 24
 
@@ -54,7 +56,7 @@ def _half(seed, dt):
     return "f16" if dt == "bf16" and W.rng(seed + 7_000_000).random() < 0.4 else dt
 
 
-def random_case(seed, hero_bias=False, big=False):
+def random_case(seed, hero_bias=False, big=False, high_rank=False):
     """(spec, params) of one random fusion.  With hero_bias the shapes are
     tile-sized, the first parameter is read transposed and reductions favour
     the physically major dims, so that the transpose and column-reduce heroes
@@ -63,7 +65,11 @@ def random_case(seed, hero_bias=False, big=False):
     wide transpose tiles."""
     g = W.rng(seed)
     rank = int(g.integers(2, 4)) if hero_bias else int(g.integers(1, 4))
-    if big:
+    if high_rank:
+        rank = int(g.integers(4, 7))
+    if high_rank:
+        sizes, cap = [1, 1, 2, 3, 4, 5, 8, 16, 17], 100_000
+    elif big:
         sizes, cap = [2, 7, 64, 130, 1024, 2048, 4100, 8192, 16384], 4_000_000
     elif hero_bias:
         sizes, cap = [33, 64, 96, 130, 257], 100_000
@@ -300,13 +306,14 @@ def random_trans_case(seed):
 def _make(seed, series):
     if series == "wide":
         return random_wide_case(seed)
-    return random_case(seed, series in ("hero", "big"), series == "big")
+    return random_case(seed, series in ("hero", "big"), series == "big", series == "rank")
 
 
 def _cases():
     """(seed, series) of every case."""
     return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
-            + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)])
+            + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)]
+            + [(6000 + k, "rank") for k in range(N_RANK)])
 
 
 def test_random_fusions_plan_and_compile():
@@ -334,13 +341,13 @@ def test_random_fusions_plan_and_compile():
         if h and series != "big":  # the big cases' oracle runs with their GPU test
             oracle.evaluate(s.nodes, params)
     ran = sum(1 for h in heroes_of if h)
-    total = N_CASES + N_HERO + N_WIDE + N_BIG
+    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK
     assert ran >= total * 3 // 4, (ran, total - ran)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
