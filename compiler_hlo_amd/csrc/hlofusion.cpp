@@ -285,7 +285,11 @@ hf_status hf_fusion_create(const hf_fusion_desc *desc, uint32_t flags, hf_fusion
     f->compile_only = flags & HF_CREATE_COMPILE_ONLY;
     if (!f->plan_only) {
       std::string prelude = k_src_common;
-      f->source = hf::generate_source(f->g, f->P, prelude, hero_text(f->P.hero));
+      // The source text names the compiler options too, so that anything
+      // keyed on the text (measurements of a kernel) changes with them.
+      std::string opts = "// hiprtc options:";
+      for (const char *o : rtc_options()) opts += std::string(" ") + o;
+      f->source = opts + "\n" + hf::generate_source(f->g, f->P, prelude, hero_text(f->P.hero));
       dump(f.get());
       hf_status st = compile(f->source, &f->code);
       if (st != HF_OK) return st;
