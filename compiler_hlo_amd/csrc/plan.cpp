@@ -595,12 +595,22 @@ Plan plan_reduce(const Graph &g) {
       if (k < nk && !red[order[k]]) minor_red = false;
       if (k < nj && red[order[k]]) minor_kept = false;
     }
+    // Kept dims on both sides of one physically contiguous block of reduced
+    // dims: a column reduce over the kept dims flattened in physical order
+    // (the physically major kept dims act as a batch).  Each lane's vector
+    // still lies along the minor kept dim, and the index maps delinearize
+    // the flattened column over every kept dim.
+    size_t first = order.size(), last = 0;
+    for (size_t k = 0; k < order.size(); ++k)
+      if (red[order[k]]) first = std::min(first, k), last = k;
+    const bool batched_col = !red[order[0]] && last - first + 1 == nk;
     if (minor_red) row = true;
-    else if (minor_kept) row = false;
+    else if (minor_kept || batched_col) row = false;
     else
       fail(HF_ERR_UNSUPPORTED,
            "node " + std::to_string(g.reduce) +
-               " (reduce): reduced dimensions are neither the physically minor nor the physically major ones");
+               " (reduce): reduced dimensions are neither the physically minor ones nor one physically contiguous block "
+               "after the minor kept ones");
   }
   // K: elements per output (0 when a reduced dim is empty: every output is
   // init); J: outputs

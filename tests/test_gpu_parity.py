@@ -911,6 +911,29 @@ def test_column_reduce_full_both_layouts():
     assert np.array_equal(got.view(np.uint32), got_c.view(np.uint32))
 
 
+@pytest.mark.parametrize("dims,red,m2m", [([3, 50, 40], [1], None), ([2, 3, 1000, 64], [2], None),
+                                          ([5, 7, 9], [2], [0, 2, 1]), ([4, 6, 5, 32], [1, 2], None),
+                                          ([8, 4096, 512], [1], None), ([3, 130, 7], [1], None)])
+def test_column_reduce_batched(dims, red, m2m):
+    """Reduced dims that form one physically contiguous block with kept dims
+    on both sides: a column reduce over the kept dims flattened in physical
+    order, the major kept dims acting as a batch.  Sum of integers (exact in
+    any order) and max, bit-exact against the oracle."""
+    say("column reduce batched", dims, red, m2m)
+    g = W.rng(98)
+    n = int(np.prod(dims))
+    out = [d for k, d in enumerate(dims) if k not in red]
+    for reducer, init in (("add", 0.0), ("max", float("-inf"))):
+        s = W.Spec()
+        p = s.parameter(0, "f32", dims, m2m)
+        s.reduce(p, red, reducer, init, "f32", out)
+        x = (W.integers(g, n, -8, 8, np.int64).astype(np.float32) if reducer == "add"
+             else W.normal_f32(g, n))
+        got, f = run_gpu(s.nodes, [x])
+        assert f.plan()["hero"] == "column_reduce", f.plan()
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
 @pytest.mark.parametrize("hero", ["row_reduce", "column_reduce"])
 def test_reduce_special_values(hero):
     """max, min and add reductions over data with NaN, signed zeros and
