@@ -975,6 +975,56 @@ def test_reduce_special_values(hero):
 # --------------------------------------------------------------------------
 # launches recorded into a HIP graph
 # --------------------------------------------------------------------------
+def test_concurrent_launches_from_threads_on_streams():
+    """Four host threads, each with its own stream (default priority) and
+    its own handles of a loop, a transpose, a row reduce and a column reduce
+    (the column reduce's workspace belongs to its handle), launch 20 rounds
+    at once.  Every output equals the single-threaded result bitwise, and the
+    oracle where exact."""
+    import threading
+    import torch
+    import compiler_hlo_amd as H
+    from harness import from_device, to_device
+    makers = [lambda: W.transpose_exp_f32(512, 768, seed=71),
+              lambda: W.row_reduce_exp_add_bf16(2, 16, 4096, seed=72),
+              lambda: W.column_reduce_max_f32(2048, 1024, seed=73),
+              lambda: W.quant_dequant_bias_requant(300, 4096, seed=74)]
+    cases = [mk() for mk in makers]
+    ref = []
+    for spec, params, _ in cases:
+        got, f = run_gpu(spec.nodes, params)
+        ref.append(got)
+    assert_bitexact(ref[2], oracle.evaluate(cases[2][0].nodes, cases[2][1]), "f32")
+    assert_bitexact(ref[3], oracle.evaluate(cases[3][0].nodes, cases[3][1]), "s8")
+    outs, errors = {}, []
+
+    def worker(t):
+        try:
+            stream = torch.cuda.Stream()
+            fs = [H.Fusion(spec.nodes) for spec, _, _ in cases]
+            devs = [[to_device(p) for p in params] for _, params, _ in cases]
+            with torch.cuda.stream(stream):
+                res = [f(*d, stream=stream) for f, d in zip(fs, devs)]
+                for _ in range(19):
+                    for f, d, r in zip(fs, devs, res):
+                        f(*d, out=r, stream=stream)
+            stream.synchronize()
+            outs[t] = [from_device(r, spec.nodes[-1]["dtype"]) for r, (spec, _, _) in zip(res, cases)]
+        except Exception as e:  # reported by the main thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    assert sorted(outs) == [0, 1, 2, 3]
+    for t in range(4):
+        for k in range(4):
+            assert np.array_equal(outs[t][k].view(np.uint8), ref[k].view(np.uint8)), (t, k)
+
+
 @pytest.mark.parametrize("k", range(3))
 def test_launch_in_hip_graph(k):
     """A launch recorded into a HIP graph (torch.cuda.graph) and replayed with
