@@ -15,7 +15,8 @@ transpose and column-reduce heroes; pad, concatenate and quantized storage;
 big shapes (dims up to 16384, up to 4M elements) for the whole-workgroup
 row paths, many column segments and the wide transpose tiles; and rank 4-6
 spaces with size-1 dims, for layout normalisation (the pad, concatenate and
-quantized series as well).  A sixth
+quantized series as well).  The first two also run with NaN, +-inf and +-0
+in the inputs (NaN positions compare, other elements bitwise).  A sixth
 series puts one exp, log or tanh among exactly rounding ops and compares
 within the bound the result allows.
 
@@ -37,6 +38,7 @@ N_WIDE = 96         # seeds 3000.. : pad, concatenate, quantized and 4-bit stora
 N_BIG = 24          # seeds 4000.. : dims up to 16384, 0.2M-4M elements
 N_RANK = 24         # seeds 6000.. : rank 4-6 with size-1 dims
 N_WRANK = 24        # seeds 7000.. : the pad/concatenate/quantized series at rank 4-5
+N_SPECIAL = 24      # seeds 8000.. : the first two series with NaN, +-inf and +-0 in the inputs
 N_TRANS = 48        # seeds 5000.. : one exp, log or tanh, compared within its bound
 BATCH = 24
 
@@ -306,7 +308,34 @@ def random_trans_case(seed):
     return s, params, check
 
 
+_SPECIALS = {"f32": [np.float32(v).view(np.uint32) for v in (np.nan, np.inf, -np.inf, -0.0, 0.0)],
+             "bf16": [0x7FC0, 0x7F80, 0xFF80, 0x8000, 0x0000],
+             "f16": [0x7E00, 0x7C00, 0xFC00, 0x8000, 0x0000]}
+
+
+def _with_specials(seed, s, params):
+    """About 2% of every float parameter's elements set to NaN, +-inf or +-0
+    (from a stream of their own).  IEEE arithmetic propagates them alike in
+    any order (NaN positions compare, not payloads)."""
+    out = []
+    for k, (nd, x) in enumerate(zip([nd for nd in s.nodes if nd["op"] == "parameter"], params)):
+        dt = nd["dtype"]
+        if dt not in _SPECIALS or x.size == 0:
+            out.append(x)
+            continue
+        g = W.rng(seed + 8_000_000 + k)
+        x = x.copy()
+        idx = g.choice(x.size, max(1, x.size // 50), replace=False)
+        bits = x.view(np.uint32 if dt == "f32" else np.uint16)
+        bits[idx] = np.asarray(_SPECIALS[dt], dtype=bits.dtype)[g.integers(0, 5, idx.size)]
+        out.append(x)
+    return out
+
+
 def _make(seed, series):
+    if series == "special":
+        s, params = random_case(seed, seed % 2 == 1)
+        return s, _with_specials(seed, s, params)
     if series in ("wide", "wrank"):
         return random_wide_case(seed, series == "wrank")
     return random_case(seed, series in ("hero", "big"), series == "big", series == "rank")
@@ -316,7 +345,8 @@ def _cases():
     """(seed, series) of every case."""
     return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
             + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)]
-            + [(6000 + k, "rank") for k in range(N_RANK)] + [(7000 + k, "wrank") for k in range(N_WRANK)])
+            + [(6000 + k, "rank") for k in range(N_RANK)] + [(7000 + k, "wrank") for k in range(N_WRANK)]
+            + [(8000 + k, "special") for k in range(N_SPECIAL)])
 
 
 def test_random_fusions_plan_and_compile():
@@ -344,13 +374,13 @@ def test_random_fusions_plan_and_compile():
         if h and series != "big":  # the big cases' oracle runs with their GPU test
             oracle.evaluate(s.nodes, params)
     ran = sum(1 for h in heroes_of if h)
-    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK
+    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL
     assert ran >= total * 2 // 3, (ran, total - ran)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
