@@ -18,7 +18,8 @@ spaces with size-1 dims, for layout normalisation (the pad, concatenate and
 quantized series as well).  The first two also run with NaN, +-inf and +-0
 in the inputs (NaN positions compare, other elements bitwise).  A sixth
 series puts one exp, log or tanh among exactly rounding ops and compares
-within the bound the result allows.
+within the bound the result allows (half of it with special values in the
+inputs).
 
 The CPU test plans and compiles every case for gfx950 (and runs the oracle on
 all but the big ones); the GPU tests run them.
@@ -232,7 +233,7 @@ def random_wide_case(seed, high_rank=False):
     return s, params
 
 
-def random_trans_case(seed):
+def random_trans_case(seed, specials=False):
     """(spec, params, check): one exp, log or tanh (f32 or bf16) inside a
     random fusion, between exactly rounding ops.  Its operand is exact
     (a parameter read plainly, transposed or reversed, maybe added to a
@@ -290,6 +291,8 @@ def random_trans_case(seed):
         s.reduce(y, red, reducer, init, cur, out_dims)
     s.nodes[-1]["m2m"] = _layout(g, len(out_dims))
     is_sum = red is not None and s.nodes[-1]["reducer"] == "add"
+    if specials and not is_sum:  # a sum's bound needs finite terms
+        params = _with_specials(seed, s, params)
 
     def check(got):
         import itertools
@@ -401,7 +404,7 @@ def test_random_transcendental_fusions_plan_and_check_oracle():
     import compiler_hlo_amd as H
     planned = 0
     for k in range(N_TRANS):
-        s, params, check = random_trans_case(5000 + k)
+        s, params, check = random_trans_case(5000 + k, specials=k >= BATCH)
         try:
             H.Fusion(s.nodes, mode="plan")
         except H.FusionError as e:
@@ -417,7 +420,7 @@ def test_random_transcendental_fusions_plan_and_check_oracle():
 def test_random_transcendental_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for k in range(batch * BATCH, (batch + 1) * BATCH):
-        s, params, check = random_trans_case(5000 + k)
+        s, params, check = random_trans_case(5000 + k, specials=k >= BATCH)  # the second batch: NaN, inf, +-0
         try:
             H.Fusion(s.nodes, mode="plan")
         except H.FusionError:
