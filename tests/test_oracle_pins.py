@@ -373,20 +373,74 @@ def test_exp_bf16_exhaustive():
     assert np.all(np.isnan(out[~fin & np.isnan(x)]))
 
 
-def test_special_values():
-    """IEEE 754-2019 maximum and the special values of exp and log."""
-    vals = [float("nan"), -0.0, 0.0, float("-inf"), float("inf"), 1.5]
+# IEEE 754-2019 maximum and minimum over {NaN, -0, +0, -inf, +inf, 1.5},
+# written out by hand (row = lhs, column = rhs): NaN propagates from either
+# side, and -0 orders below +0.
+_SPECIALS = [float("nan"), -0.0, 0.0, float("-inf"), float("inf"), 1.5]
+_MAXIMUM_TABLE = [
+    ["nan", "nan", "nan", "nan", "nan", "nan"],
+    ["nan", "-0", "+0", "-0", "inf", "1.5"],
+    ["nan", "+0", "+0", "+0", "inf", "1.5"],
+    ["nan", "-0", "+0", "-inf", "inf", "1.5"],
+    ["nan", "inf", "inf", "inf", "inf", "inf"],
+    ["nan", "1.5", "1.5", "1.5", "inf", "1.5"],
+]
+_MINIMUM_TABLE = [
+    ["nan", "nan", "nan", "nan", "nan", "nan"],
+    ["nan", "-0", "-0", "-inf", "-0", "-0"],
+    ["nan", "-0", "+0", "-inf", "+0", "+0"],
+    ["nan", "-inf", "-inf", "-inf", "-inf", "-inf"],
+    ["nan", "-0", "+0", "-inf", "inf", "1.5"],
+    ["nan", "-0", "+0", "-inf", "1.5", "1.5"],
+]
+
+
+def _spelled(v: float) -> str:
+    if math.isnan(v):
+        return "nan"
+    if v == 0:
+        return "-0" if math.copysign(1, v) < 0 else "+0"
+    if math.isinf(v):
+        return "inf" if v > 0 else "-inf"
+    return repr(v)
+
+
+@pytest.mark.parametrize("op,table", [("maximum", _MAXIMUM_TABLE), ("minimum", _MINIMUM_TABLE)])
+def test_maximum_minimum_special_value_tables(op, table):
+    """StableHLO Specification, "maximum" / "minimum": the IEEE-754 operations
+    (2019 edition: NaN-propagating, -0 < +0), against tables spelled out by
+    hand."""
+    vals = _SPECIALS
     a = np.array([v for v in vals for _ in vals], np.float32)
     b = np.array([w for _ in vals for w in vals], np.float32)
-    got = _binary("maximum", a.reshape(6, 6), b.reshape(6, 6)).ravel()
-    for x, y, r in zip(a.tolist(), b.tolist(), got.tolist()):
-        if math.isnan(x) or math.isnan(y):
-            assert math.isnan(r)
-        elif x == 0 and y == 0:
-            want_neg = math.copysign(1, x) < 0 and math.copysign(1, y) < 0
-            assert r == 0 and (math.copysign(1, r) < 0) == want_neg
-        else:
-            assert r == max(x, y)
+    got = _binary(op, a.reshape(6, 6), b.reshape(6, 6)).ravel()
+    spelled = [_spelled(v) for v in got.tolist()]
+    want = [c for row in table for c in row]
+    assert spelled == want
+
+
+@pytest.mark.parametrize("reducer,row,want", [
+    ("min", [0.0, -0.0], "-0"), ("min", [-0.0, 0.0], "-0"), ("min", [0.0, 0.0], "+0"),
+    ("min", [3.0, float("nan"), -5.0], "nan"), ("min", [float("nan")] * 3, "nan"),
+    ("min", [float("inf"), float("inf")], "inf"), ("min", [], "inf"),
+    ("max", [-0.0, 0.0], "+0"), ("max", [0.0, -0.0], "+0"), ("max", [-0.0, -0.0], "-0"),
+    ("max", [3.0, float("nan"), -5.0], "nan"), ("max", [-5.0, 2.0, float("nan")], "nan"),
+])
+def test_reduce_min_max_signed_zeros_and_nan(reducer, row, want):
+    """reduce with maximum / minimum (StableHLO Specification, "reduce"): the
+    order-free fold of the IEEE operations from init (+inf for min, -inf for
+    max).  Rows over {+0, -0} and rows holding NaN, spelled out by hand."""
+    init = float("inf") if reducer == "min" else float("-inf")
+    n = len(row)
+    s = Spec()
+    p = s.parameter(0, "f32", [1, n])
+    s.reduce(p, [1], reducer, init, "f32", [1])
+    got = ev(s, [np.array(row, np.float32)])
+    assert _spelled(float(got[0])) == want
+
+
+def test_special_values():
+    """The special values of exp and log."""
     x = np.array([1.0, 0.0, -0.0, -1.0, float("inf"), float("nan")], np.float32)
     s = Spec()
     p = s.parameter(0, "f32", [6])
