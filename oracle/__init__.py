@@ -32,7 +32,7 @@ _SRC = os.path.join(_HERE, "hlo_oracle.c")
 _LIB = os.path.join(_HERE, "libhlo_oracle.so")
 
 MAX_RANK = 8
-MAX_OPERANDS = 8
+MAX_OPERANDS = 9
 MAX_ATTR = 24
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "s32": 4, "u8": 5, "s4": 6, "u4": 7}
 # Host buffers: one element per item, except s4/u4, which are packed two per
@@ -51,7 +51,8 @@ OPS = {
     "minimum": 10, "negate": 11, "abs": 12, "convert": 13,
     "broadcast_in_dim": 14, "reshape": 15, "transpose": 16,
     "uniform_dequantize": 17, "uniform_quantize": 18, "reduce": 19, "dot": 20,
-    "reverse": 21, "iota": 22, "pad": 23, "concatenate": 24,
+    "reverse": 21, "iota": 22, "pad": 23, "concatenate": 24, "slice": 25,
+    "dynamic_slice": 26,
 }
 REDUCERS = {"add": 0, "max": 1, "min": 2, "argmax": 3}
 
@@ -165,6 +166,10 @@ class _Graph:
                 attr = [nd["iota_dimension"]]
             elif nd["op"] == "concatenate":
                 attr = [nd["dimension"]]
+            elif nd["op"] == "slice":
+                attr = list(nd["start_indices"]) + list(nd["limit_indices"]) + list(nd["strides"])
+            elif nd["op"] == "dynamic_slice":
+                attr = list(nd["slice_sizes"])
             else:
                 attr = nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", [])))
             c.n_attr = len(attr)

@@ -27,9 +27,11 @@
  *     minor-to-major ordering", "Array indexing".
  *   StableHLO Specification: "Types" (quantized element types and their
  *     constraints), Ops add, broadcast_in_dim, convert, dot_general,
- *     exponential, log, maximum, minimum, multiply, reduce, reshape,
- *     reduce_precision, round_nearest_even, tanh.
- *   Operation semantics: Reduce, BroadcastInDim, ConvertElementType, Collapse.
+ *     dynamic_slice, exponential, log, maximum, minimum, multiply, reduce,
+ *     reshape, reduce_precision, round_nearest_even, tanh; "Programs" (the
+ *     start_indices and limit_indices attributes of slice).
+ *   Operation semantics: Reduce, BroadcastInDim, ConvertElementType, Collapse,
+ *     DynamicSlice.
  *   StableHLO Quantization: "Per-tensor quantization", "Per-axis quantization".
  *   XLA:GPU Emitters: "Indexing transforms" (transpose as an output-to-input
  *     index map).
@@ -41,7 +43,7 @@
 #include <string.h>
 
 #define OR_MAX_RANK 8
-#define OR_MAX_OPERANDS 8
+#define OR_MAX_OPERANDS 9 /* dynamic_slice: the operand and one start index per dim */
 #define OR_MAX_ATTR 24
 
 /* element types */
@@ -57,7 +59,8 @@ enum {
   OR_MAXIMUM = 9, OR_MINIMUM = 10, OR_NEGATE = 11, OR_ABS = 12,
   OR_CONVERT = 13, OR_BROADCAST_IN_DIM = 14, OR_RESHAPE = 15,
   OR_TRANSPOSE = 16, OR_DEQUANTIZE = 17, OR_QUANTIZE = 18, OR_REDUCE = 19,
-  OR_DOT = 20, OR_REVERSE = 21, OR_IOTA = 22, OR_PAD = 23, OR_CONCATENATE = 24
+  OR_DOT = 20, OR_REVERSE = 21, OR_IOTA = 22, OR_PAD = 23, OR_CONCATENATE = 24,
+  OR_SLICE = 25, OR_DYNAMIC_SLICE = 26
 };
 
 enum { OR_RED_ADD = 0, OR_RED_MAX = 1, OR_RED_MIN = 2, OR_RED_ARGMAX = 3 };
@@ -84,7 +87,8 @@ typedef struct {
   double constant;             /* OR_CONSTANT: scalar, broadcast over type */
   int32_t n_attr;              /* permutation | broadcast dims | reduce dims |
                                   reverse dims | iota dim | pad low, high,
-                                  interior | concatenate dim */
+                                  interior | concatenate dim | slice start,
+                                  limit, strides | dynamic_slice sizes */
   int64_t attr[OR_MAX_ATTR];
   int32_t reducer;             /* OR_REDUCE */
   double init;                 /* OR_REDUCE */
@@ -463,6 +467,31 @@ static int eval(const graph *g, int n, const int64_t *idx, long double *out, aux
       set_err("concatenate index out of range", n);
       return -2;
     }
+    case OR_SLICE: {
+      /* result[i] = operand[start_indices + i * strides]; attr holds
+       * start_indices[rank], limit_indices[rank], strides[rank] */
+      const int r = t->rank;
+      for (int d = 0; d < r; ++d) oidx[d] = nd->attr[d] + idx[d] * nd->attr[2 * r + d];
+      return eval(g, nd->operands[0], oidx, out, NULL);
+    }
+    case OR_DYNAMIC_SLICE: {
+      /* adjusted_start_indices = clamp(0, start_indices, shape(operand) -
+       * slice_sizes); operand_index = adjusted_start_indices + result_index.
+       * Operand 1 + d is the rank-0 start index of dim d; attr holds
+       * slice_sizes[rank]. */
+      const or_type *ot = &g->nodes[nd->operands[0]].type;
+      const int64_t none[OR_MAX_RANK] = {0};
+      for (int d = 0; d < ot->rank; ++d) {
+        long double sv;
+        if ((rc = eval(g, nd->operands[1 + d], none, &sv, NULL))) return rc;
+        int64_t start = (int64_t)sv;
+        const int64_t hi = ot->dims[d] - nd->attr[d];
+        if (start < 0) start = 0;
+        if (start > hi) start = hi;
+        oidx[d] = start + idx[d];
+      }
+      return eval(g, nd->operands[0], oidx, out, NULL);
+    }
     case OR_DEQUANTIZE: {
       const or_type *qt = &g->nodes[nd->operands[0]].type;
       if ((rc = eval(g, nd->operands[0], idx, &a, NULL))) return rc;
@@ -522,6 +551,30 @@ static int check(const graph *g, int root) {
         int64_t rd = nd->attr[d];
         if (rd < 0 || rd >= nd->type.rank) { set_err("broadcast dim range", n); return -1; }
         if (ot->dims[d] != 1 && ot->dims[d] != nd->type.dims[rd]) { set_err("broadcast dim size", n); return -1; }
+      }
+    }
+    if (nd->op == OR_SLICE) {
+      const or_type *ot = &g->nodes[nd->operands[0]].type;
+      const int r = ot->rank;
+      if (nd->n_attr != 3 * r || nd->type.rank != r) { set_err("slice attributes", n); return -1; }
+      for (int d = 0; d < r; ++d) {
+        const int64_t st = nd->attr[d], lim = nd->attr[r + d], step = nd->attr[2 * r + d];
+        if (st < 0 || st > lim || lim > ot->dims[d] || step < 1) { set_err("slice bounds", n); return -1; }
+        if (nd->type.dims[d] != (lim - st + step - 1) / step) { set_err("slice result dims", n); return -1; }
+      }
+    }
+    if (nd->op == OR_DYNAMIC_SLICE) {
+      const or_type *ot = &g->nodes[nd->operands[0]].type;
+      if (nd->n_operands != 1 + ot->rank || nd->n_attr != ot->rank || nd->type.rank != ot->rank) {
+        set_err("dynamic_slice operands", n);
+        return -1;
+      }
+      for (int d = 0; d < ot->rank; ++d) {
+        if (g->nodes[nd->operands[1 + d]].type.rank != 0) { set_err("start index not rank 0", n); return -1; }
+        if (nd->attr[d] < 0 || nd->attr[d] > ot->dims[d] || nd->type.dims[d] != nd->attr[d]) {
+          set_err("dynamic_slice sizes", n);
+          return -1;
+        }
       }
     }
     if (nd->op == OR_RESHAPE && num_elements(&nd->type) != num_elements(&g->nodes[nd->operands[0]].type)) {

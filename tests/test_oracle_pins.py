@@ -824,6 +824,91 @@ def test_index_transforms_against_numpy():
 
 
 # --------------------------------------------------------------------------
+# slice and dynamic_slice (StableHLO Specification, "dynamic_slice";
+# Operation semantics, DynamicSlice; the start_indices / limit_indices
+# attributes of slice in "Programs")
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("key,dtype", [("dynamic_slice", "s32"), ("dynamic_slice_1d", "f32"),
+                                       ("dynamic_slice_2d", "f32")])
+@pytest.mark.parametrize("starts_as", ["parameters", "constants"])
+def test_dynamic_slice_page_examples(key, dtype, starts_as):
+    G = GOLD[key]
+    x = np.array(G["operand"], {"s32": np.int32, "f32": np.float32}[dtype])
+    s = Spec()
+    p = s.parameter(0, dtype, list(x.shape))
+    params = [x]
+    starts = []
+    for d, v in enumerate(G["start_indices"]):
+        if starts_as == "parameters":
+            starts.append(s.parameter(1 + d, "s32", []))
+            params.append(np.array(v, np.int32))
+        else:
+            starts.append(s.constant(v, "s32", []))
+    s.dynamic_slice(p, starts, G["slice_sizes"], dtype)
+    assert ev(s, params).reshape(G["slice_sizes"]).tolist() == G["result"]
+
+
+def test_dynamic_slice_clamps_starts_against_numpy():
+    """Brute force on small shapes: every start from -3 to dim + 2 (so both
+    clamps are hit) and every size 0..dim, against numpy basic slicing of
+    the start clamped into [0, dim - size]."""
+    g = rng(73)
+    for shape in [(5,), (3, 4), (2, 3, 4)]:
+        x = g.standard_normal(shape).astype(np.float32)
+        r = len(shape)
+        for _ in range(40):
+            sizes = [int(g.integers(0, n + 1)) for n in shape]
+            starts = [int(g.integers(-3, n + 3)) for n in shape]
+            s = Spec()
+            p = s.parameter(0, "f32", list(shape))
+            st = [s.parameter(1 + d, "s32", []) for d in range(r)]
+            s.dynamic_slice(p, st, sizes, "f32")
+            got = ev(s, [x] + [np.array(v, np.int32) for v in starts]).reshape(sizes)
+            lo = [min(max(v, 0), n - z) for v, n, z in zip(starts, shape, sizes)]
+            want = x[tuple(slice(a, a + z) for a, z in zip(lo, sizes))]
+            assert np.array_equal(got, want), (shape, starts, sizes)
+
+
+def test_slice_against_numpy_strides_and_layouts():
+    """slice(x, start, limit, strides) = x[start:limit:strides] per dim, the
+    result shape ceil((limit - start) / strides); operand and result in
+    row-major and column-major layouts."""
+    g = rng(74)
+    for shape in [(7,), (5, 6), (3, 4, 5)]:
+        x = g.standard_normal(shape).astype(np.float32)
+        r = len(shape)
+        for _ in range(30):
+            start = [int(g.integers(0, n + 1)) for n in shape]
+            limit = [int(g.integers(a, n + 1)) for a, n in zip(start, shape)]
+            strides = [int(g.integers(1, 4)) for _ in shape]
+            out = [-(-(b - a) // k) for a, b, k in zip(start, limit, strides)]
+            want = x[tuple(slice(a, b, k) for a, b, k in zip(start, limit, strides))]
+            assert list(want.shape) == out
+            for m2m_in, m2m_out in ((None, None), (list(range(r)), None), (None, list(range(r)))):
+                s = Spec()
+                p = s.parameter(0, "f32", list(shape), m2m_in)
+                s.slice(p, start, limit, strides, "f32", out, m2m_out)
+                xin = x.ravel() if m2m_in is None else x.transpose().ravel()
+                got = ev(s, [xin])
+                got = got.reshape(out) if m2m_out is None else got.reshape(out[::-1]).transpose()
+                assert np.array_equal(got, want), (shape, start, limit, strides, m2m_in, m2m_out)
+
+
+def test_slice_equals_dynamic_slice_with_constant_starts():
+    g = rng(75)
+    x = g.standard_normal((6, 9)).astype(np.float32)
+    for start, size in (([1, 2], [3, 5]), ([0, 0], [6, 9]), ([5, 8], [1, 1]), ([2, 3], [0, 4])):
+        a = Spec()
+        p = a.parameter(0, "f32", [6, 9])
+        a.slice(p, start, [s + z for s, z in zip(start, size)], [1, 1], "f32", size)
+        b = Spec()
+        p = b.parameter(0, "f32", [6, 9])
+        c = [b.constant(v, "s32", []) for v in start]
+        b.dynamic_slice(p, c, size, "f32")
+        assert np.array_equal(ev(a, [x]), ev(b, [x]))
+
+
+# --------------------------------------------------------------------------
 # Variadic max/argmax reduce (Operation semantics, "Variadic Reduce")
 # --------------------------------------------------------------------------
 def _argmax_spec(dims, rdim, dtype="f32", init=float("-inf"), index_init=-1):

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs and neutral fusion descriptions.
 
-This module is shared by the tests, the benchmark, the oracle binding and the
-product binding.  It holds NO arithmetic of the method: no layout mapping, no
+The tests, the benchmark and the smoke check use this module to build the
+inputs and the node lists that they hand both to the product binding and to
+the oracle; neither of those two imports it.  It holds NO arithmetic of the method: no layout mapping, no
 rounding, no op semantics.  It only
 
   * draws random buffers from numpy's PCG64 with fixed seeds, directly in
@@ -100,6 +101,15 @@ class Spec:
 
     def concatenate(self, inputs, dimension, dtype, dims, m2m=None) -> int:
         return self.op("concatenate", list(inputs), dtype, dims, m2m, dimension=int(dimension))
+
+    def slice(self, x, start, limit, strides, dtype, dims, m2m=None) -> int:
+        return self.op("slice", [x], dtype, dims, m2m, start_indices=list(start),
+                       limit_indices=list(limit), strides=list(strides))
+
+    def dynamic_slice(self, x, starts, sizes, dtype, m2m=None) -> int:
+        """`starts`: one rank-0 integer node per dim of x."""
+        return self.op("dynamic_slice", [x] + list(starts), dtype, list(sizes), m2m,
+                       slice_sizes=list(sizes))
 
     def argmax(self, x, rdim, dims, index_init=-1, init=float("-inf"), m2m=None) -> int:
         """Variadic max/argmax reduce over `rdim` of x with an iota index
