@@ -31,9 +31,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhlofusion.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_RANK = 8
-MAX_OPERANDS = 8
+MAX_OPERANDS = 9
 MAX_ATTR = 3 * MAX_RANK
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2, "s8": 3, "u8": 4, "s32": 5, "s4": 6, "u4": 7}
 DTYPE_BITS = {"f32": 32, "bf16": 16, "f16": 16, "s8": 8, "u8": 8, "s32": 32, "s4": 4, "u4": 4}
@@ -49,7 +49,7 @@ OPS = {
     "tanh": 10, "negate": 11, "abs": 12, "convert": 13, "broadcast_in_dim": 14,
     "reshape": 15, "transpose": 16, "uniform_dequantize": 17,
     "uniform_quantize": 18, "reduce": 19, "reverse": 20, "iota": 21, "pad": 22,
-    "concatenate": 23,
+    "concatenate": 23, "slice": 24, "dynamic_slice": 25,
 }
 REDUCERS = {"add": 0, "max": 1, "min": 2, "argmax": 3}
 HEROES = {0: "loop", 1: "transpose", 2: "row_reduce", 3: "column_reduce"}
@@ -105,6 +105,10 @@ def node_attr(nd: dict) -> list:
         return [int(nd["iota_dimension"])]
     if nd["op"] == "concatenate":
         return [int(nd["dimension"])]
+    if nd["op"] == "slice":
+        return list(nd["start_indices"]) + list(nd["limit_indices"]) + list(nd["strides"])
+    if nd["op"] == "dynamic_slice":
+        return list(nd["slice_sizes"])
     return list(nd.get("permutation", nd.get("broadcast_dimensions", nd.get("dimensions", []))))
 
 

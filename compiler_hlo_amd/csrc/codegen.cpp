@@ -186,7 +186,8 @@ class Gen {
       ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
       b.os << "  { const " << reg << " s = " << elem_value(dt, m) << ";\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
-    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V * es >= 4) {  // contiguous: raw vector load
+    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V * es >= 4 && E[ld].add % V == 0 &&
+               E[ld].dyn.empty()) {  // contiguous and aligned: raw vector load
       const int nb = V * es;
       decl("hf_u32", nb / 4);
       ld_os << "  hf_raw_ld<" << nb << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off << ") * "
@@ -238,7 +239,7 @@ class Gen {
       ld_os << "  " << m << " = " << bytes << "[(" << off << ") >> 1];\n";
       b.os << "  { const int s = hf_nibble<" << sgn << ">(" << m << ", (" << off << ") & 1);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
-    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V % 2 == 0) {
+    } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V % 2 == 0 && E[ld].add % V == 0 && E[ld].dyn.empty()) {
       decl("hf_u32", (V + 7) / 8);
       if (V >= 8) {
         ld_os << "  hf_raw_ld<" << V / 2 << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off
@@ -354,7 +355,10 @@ class Gen {
       b.os << args << ", R." << m << ", " << v << ");\n";
     } else {
       std::vector<std::string> a;
-      for (size_t k = 0; k < nd.opd.size(); ++k) {
+      // a dynamic_slice reads its start indices at launch (HfArgs), so only
+      // its operand is evaluated here
+      const size_t nk = nd.op == HF_DYNAMIC_SLICE ? 1 : nd.opd.size();
+      for (size_t k = 0; k < nk; ++k) {
         bool general = false;
         a.push_back(val(ci, b, nd.opd[k], operand_index(g_, n, (int)k, E, &general)));
       }
@@ -363,7 +367,8 @@ class Gen {
       const std::string x = a.empty() ? "" : a[0] + "[l]";
       const std::string y = a.size() > 1 ? a[1] + "[l]" : "";
       switch (nd.op) {
-        case HF_TRANSPOSE: case HF_BROADCAST_IN_DIM: case HF_RESHAPE: case HF_REVERSE:
+        case HF_TRANSPOSE: case HF_BROADCAST_IN_DIM: case HF_RESHAPE: case HF_REVERSE: case HF_SLICE:
+        case HF_DYNAMIC_SLICE:
           v = a[0];  // pure index transforms
           break;
         case HF_IOTA: {  // the index along iota_dimension
@@ -731,6 +736,28 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
     add("const double *", "qr" + std::to_string(q));
   }
   add("void *", "ws");
+  // dynamic_slice start indices held in parameters: read once per launch and
+  // clamped into [0, dim(operand) - slice_size]
+  for (int n = 0; n < (int)g.nodes.size(); ++n) {
+    const Node &nd = g.nodes[n];
+    if (!nd.live || nd.op != HF_DYNAMIC_SLICE) continue;
+    const Type &ot = g.nodes[nd.opd[0]].t;
+    for (int d = 0; d < ot.rank; ++d) {
+      const Node &si = g.nodes[nd.opd[1 + d]];
+      const long long hi = ot.dims[d] - nd.attr[d];
+      if (si.op != HF_PARAMETER || hi <= 0) continue;
+      const std::string p = "hf_a_p" + std::to_string(si.param);
+      std::string v;
+      switch (si.t.dt) {
+        case HF_S4: v = "hf_nibble<true>(" + p + "[0], 0)"; break;
+        case HF_U4: v = "hf_nibble<false>(" + p + "[0], 0)"; break;
+        default: v = "(int)" + p + "[0]"; break;
+      }
+      const std::string name = dyn_start_name(n, d).substr(2);  // without "A."
+      fields << "  int " << name << ";\n";
+      init << ", hf_clampi(" << v << ", 0, " << hi << ")";
+    }
+  }
   src << "struct HfArgs {\n" << fields.str() << "};\n";
   src << "#define HF_KERNEL_PARAMS " << params.str() << "\n";
   src << "#define HF_ARGS_INIT {" << init.str() << "}\n";

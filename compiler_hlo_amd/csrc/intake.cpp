@@ -76,6 +76,8 @@ const char *op_name(hf_op op) {
     case HF_IOTA: return "iota";
     case HF_PAD: return "pad";
     case HF_CONCATENATE: return "concatenate";
+    case HF_SLICE: return "slice";
+    case HF_DYNAMIC_SLICE: return "dynamic_slice";
   }
   return "?";
 }
@@ -265,7 +267,7 @@ Graph intake(const hf_fusion_desc *desc) {
     const hf_node &src = desc->nodes[i];
     // the enum-valued fields are plain integers at the boundary: each is
     // range-checked before it becomes an enum
-    if (src.op < HF_PARAMETER || src.op > HF_CONCATENATE)
+    if (src.op < HF_PARAMETER || src.op > HF_DYNAMIC_SLICE)
       fail(HF_ERR_INVALID, "node " + std::to_string(i) + ": unknown op");
     Ctx c{i, (hf_op)src.op};
     Node &n = g.nodes[i];
@@ -316,7 +318,17 @@ Graph intake(const hf_fusion_desc *desc) {
         break;
       case HF_CONSTANT:
         need_operands(src, 0, c);
-        if (!is_float(t.dt) || quantized) c.unsupported("only floating-point constants are supported");
+        if (quantized) c.unsupported("quantized constants");
+        if (!is_float(t.dt)) {
+          // integer constants serve as dynamic_slice start indices (checked
+          // against their users below)
+          if (t.rank != 0) c.unsupported("integer constants must be rank 0 (dynamic_slice start indices)");
+          const double lo = t.dt == HF_S32 ? INT32_MIN : t.dt == HF_S8 ? -128 : t.dt == HF_S4 ? -8 : 0;
+          const double hi = t.dt == HF_S32 ? INT32_MAX : t.dt == HF_S8 ? 127 : t.dt == HF_U8 ? 255
+                          : t.dt == HF_S4 ? 7 : 15;
+          if (n.cst != std::floor(n.cst) || n.cst < lo || n.cst > hi)
+            c.invalid("the constant is not a value of its integer element type");
+        }
         break;
       case HF_LOG: case HF_EXP: case HF_TANH: case HF_NEGATE: case HF_ABS:
         need_operands(src, 1, c);
@@ -449,6 +461,47 @@ Graph intake(const hf_fusion_desc *desc) {
         if (t.dims[cd] != total) c.invalid("dim(result, dimension) = sum of dim(inputs..., dimension) violated (C6)");
         break;
       }
+      case HF_SLICE: {
+        // start_indices, limit_indices (the attributes "Programs" names) and
+        // strides; the op's own section lies in the part of the pages that
+        // is cut off, so the constraints are those of its definition:
+        // result[i] = operand[start + i * strides].
+        need_operands(src, 1, c);
+        const Type &o = opt(0);
+        if (t.dt != o.dt) c.invalid("element_type(operand) = element_type(result) violated");
+        if (quantized || o.quant >= 0) c.unsupported("slice of quantized values");
+        if ((int)n.attr.size() != 3 * o.rank || o.rank != t.rank)
+          c.invalid("size(start_indices) = size(limit_indices) = size(strides) = rank(operand) violated");
+        for (int d = 0; d < o.rank; ++d) {
+          const int64_t st = n.attr[d], lim = n.attr[o.rank + d], step = n.attr[2 * o.rank + d];
+          if (!(0 <= st && st <= lim && lim <= o.dims[d])) c.invalid("0 <= start_indices <= limit_indices <= shape(operand) violated");
+          if (step < 1) c.invalid("0 < strides violated");
+          if (t.dims[d] != (lim - st + step - 1) / step)
+            c.invalid("shape(result) = ceil((limit_indices - start_indices) / strides) violated");
+        }
+        break;
+      }
+      case HF_DYNAMIC_SLICE: {
+        // StableHLO Specification, "dynamic_slice", constraints C1-C5
+        if (n.opd.empty()) c.invalid("expects the operand and one start index per dimension (C2)");
+        const Type &o = opt(0);
+        if (t.dt != o.dt) c.invalid("element_type(operand) = element_type(result) violated (C1)");
+        if (quantized || o.quant >= 0) c.unsupported("dynamic_slice of quantized values");
+        if ((int)n.opd.size() != 1 + o.rank || (int)n.attr.size() != o.rank)
+          c.invalid("size(start_indices) = size(slice_sizes) = rank(operand) violated (C2)");
+        if (t.rank != o.rank) c.invalid("shape(result) = slice_sizes violated (C5)");
+        for (int d = 0; d < o.rank; ++d) {
+          const Node &si = g.nodes[n.opd[1 + d]];
+          if (si.t.rank != 0 || is_float(si.t.dt) || si.t.quant >= 0)
+            c.invalid("start_indices must be 0-dimensional tensors of integer type (I2)");
+          if (si.t.dt != opt(1).dt) c.invalid("same(type(start_indices...)) violated (C3)");
+          if (si.op != HF_PARAMETER && si.op != HF_CONSTANT)
+            c.unsupported("start indices must be parameters or constants");
+          if (n.attr[d] < 0 || n.attr[d] > o.dims[d]) c.invalid("0 <= slice_sizes <= shape(operand) violated (C4)");
+          if (t.dims[d] != n.attr[d]) c.invalid("shape(result) = slice_sizes violated (C5)");
+        }
+        break;
+      }
       case HF_UNIFORM_DEQUANTIZE:
         need_operands(src, 1, c);
         if (opt(0).quant < 0) c.invalid("operand must have a quantized element type");
@@ -522,6 +575,20 @@ Graph intake(const hf_fusion_desc *desc) {
       if (g.reduce >= 0)
         fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (reduce): a fusion holds at most one reduce (its hero)");
       g.reduce = i;
+    }
+  }
+  // An integer constant is only ever a dynamic_slice start index.
+  for (int i = 0; i < (int)g.nodes.size(); ++i) {
+    const Node &nd = g.nodes[i];
+    if (!nd.live || nd.op != HF_CONSTANT || is_float(nd.t.dt)) continue;
+    if (i == g.root) fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) + " (constant): an integer constant as the root");
+    for (int u : nd.users) {
+      const Node &un = g.nodes[u];
+      bool start = un.op == HF_DYNAMIC_SLICE;
+      if (start && un.opd[0] == i) start = false;
+      if (!start)
+        fail(HF_ERR_UNSUPPORTED, "node " + std::to_string(i) +
+                                     " (constant): integer constants are supported as dynamic_slice start indices only");
     }
   }
   // Everything that depends on the reduce is its epilogue, evaluated once per

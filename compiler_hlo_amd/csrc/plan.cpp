@@ -15,11 +15,32 @@ namespace hf {
 std::string term_str(const Term &t) {
   switch (t.k) {
     case Term::ZERO: return "0";
-    case Term::VAR: return "i" + std::to_string(t.var);
+    case Term::VAR: {
+      if (!t.add && t.dyn.empty()) return "i" + std::to_string(t.var);
+      std::string s = "(i" + std::to_string(t.var);
+      if (t.add) s += " + " + std::to_string(t.add);
+      if (!t.dyn.empty()) s += " + " + t.dyn;
+      return s + ")";
+    }
     case Term::EXPR: return "(" + t.e + ")";
   }
   return "0";
 }
+
+Term shifted(const Term &t, long long c, const std::string &dyn) {
+  if (!c && dyn.empty()) return t;
+  Term r = t;
+  if (t.k == Term::VAR) {
+    r.add += c;
+    if (!dyn.empty()) r.dyn = r.dyn.empty() ? dyn : r.dyn + " + " + dyn;
+    return r;
+  }
+  r.k = Term::EXPR;
+  r.e = (t.k == Term::ZERO ? std::string("0") : term_str(t)) + " + " + std::to_string(c) + (dyn.empty() ? "" : " + " + dyn);
+  return r;
+}
+
+std::string dyn_start_name(int n, int d) { return "A.ds" + std::to_string(n) + "_" + std::to_string(d); }
 
 std::string index_key(const Index &E) {
   std::string s;
@@ -119,6 +140,38 @@ Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general,
       if (moves_with_lane(E[cd], lane)) *general = true;
       return O;
     }
+    case HF_SLICE: {
+      // operand_index = start_indices + result_index * strides
+      Index O = E;
+      const int r = ot.rank;
+      for (int d = 0; d < r; ++d) {
+        const long long st = nd.attr[d], step = nd.attr[2 * r + d];
+        if (step == 1 || nd.t.dims[d] <= 1) {
+          O[d] = shifted(E[d], st, "");
+          continue;
+        }
+        O[d] = expr(term_str(E[d]) + " * " + std::to_string(step) + " + " + std::to_string(st));
+        if (moves_with_lane(E[d], lane)) *general = true;
+      }
+      return O;
+    }
+    case HF_DYNAMIC_SLICE: {
+      // operand_index = clamp(0, start_indices, shape(operand) - slice_sizes)
+      // + result_index (StableHLO Specification, "dynamic_slice").  A
+      // constant start is clamped here; a parameter start is read and clamped
+      // by the kernel at launch (dyn_start_name); a dim sliced whole has the
+      // start 0 either way.
+      if (k > 0) return Index();  // a start index: rank 0
+      Index O = E;
+      for (int d = 0; d < ot.rank; ++d) {
+        const long long hi = ot.dims[d] - nd.attr[d];
+        if (hi <= 0) continue;
+        const Node &si = g.nodes[nd.opd[1 + d]];
+        if (si.op == HF_CONSTANT) O[d] = shifted(E[d], std::min<long long>(std::max<long long>((long long)si.cst, 0), hi), "");
+        else O[d] = shifted(E[d], 0, dyn_start_name(n, d));
+      }
+      return O;
+    }
     case HF_TRANSPOSE: {
       // result dim d is operand dim perm[d]
       Index O(ot.rank);
@@ -179,7 +232,10 @@ void visit(const Graph &g, Ctx &c, int n, const Index &E) {
     return;
   }
   if (nd.op == HF_CONSTANT) return;
-  for (size_t k = 0; k < nd.opd.size(); ++k)
+  // a dynamic_slice's start indices are read once per launch (kernel
+  // arguments), not through the prologue
+  const size_t nk = nd.op == HF_DYNAMIC_SLICE ? 1 : nd.opd.size();
+  for (size_t k = 0; k < nk; ++k)
     visit(g, c, nd.opd[k], operand_index(g, n, (int)k, E, &c.general, c.lane));
 }
 
@@ -301,6 +357,19 @@ int stream_elem_bytes(const Graph &g, const Ctx &c, int dflt) {
   return b ? b : dflt;
 }
 
+// The largest power of two <= V that divides the static offset (a slice
+// start) of every parameter read along the lane, so that raw vector loads
+// stay aligned.  Reads with a run-time offset along the lane load one
+// element per lane whatever V is.
+int align_lanes(const Ctx &c, int V) {
+  if (c.lane < 0) return V;
+  for (auto &pr : c.param_reads)
+    for (const Term &t : pr.second)
+      if (t.k == Term::VAR && t.var == c.lane)
+        while (V > 1 && t.add % V != 0) V /= 2;
+  return V;
+}
+
 bool all_coalesced(const Graph &g, const Ctx &c) {
   for (auto &pr : c.param_reads) {
     if (!large(g, pr.first)) continue;
@@ -330,16 +399,30 @@ bool exclusive(const Graph &g, int s) {
   return true;
 }
 
+// Algorithmic bytes: each parameter element the fusion needs read once, the
+// result written once.  A parameter read through a slice needs only the
+// elements its index maps reach, at most the evaluation space of each map;
+// the rest of it is never touched.
 void algorithmic(const Graph &g, Plan &P) {
   long long bytes = 0;
-  std::vector<char> used(g.nodes.size(), 0), qused(g.quants.size(), 0);
-  for (Ctx &c : P.ctx)
-    for (int n = 0; n < (int)g.nodes.size(); ++n)
+  const int N = (int)g.nodes.size();
+  std::vector<char> used(N, 0), qused(g.quants.size(), 0), start_param(N, 0);
+  std::vector<long long> reach(N, 0);
+  for (Ctx &c : P.ctx) {
+    for (int n = 0; n < N; ++n)
       if (c.in_ctx[n]) used[n] = 1;
-  for (int n = 0; n < (int)g.nodes.size(); ++n) {
-    if (!used[n]) continue;
+    const long long space = g.nodes[c.root].t.numel();
+    for (auto &pr : c.param_reads) reach[pr.first] += space;
+  }
+  for (int n = 0; n < N; ++n)
+    if (used[n] && g.nodes[n].op == HF_DYNAMIC_SLICE)
+      for (size_t k = 1; k < g.nodes[n].opd.size(); ++k)
+        if (g.nodes[g.nodes[n].opd[k]].op == HF_PARAMETER) start_param[g.nodes[n].opd[k]] = 1;
+  for (int n = 0; n < N; ++n) {
     const Node &nd = g.nodes[n];
-    if (nd.op == HF_PARAMETER) bytes += storage_bytes(nd.t.dt, nd.t.numel());
+    if (start_param[n] && !used[n]) bytes += storage_bytes(nd.t.dt, 1);
+    if (!used[n]) continue;
+    if (nd.op == HF_PARAMETER) bytes += storage_bytes(nd.t.dt, std::min<long long>(nd.t.numel(), reach[n] ? reach[n] : nd.t.numel()));
     if (nd.t.quant >= 0 && (nd.op == HF_UNIFORM_QUANTIZE || nd.op == HF_PARAMETER)) qused[nd.t.quant] = 1;
   }
   for (size_t q = 0; q < g.quants.size(); ++q)
@@ -389,6 +472,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
     const int wbits = std::max(dtype_bits(rt.dt), stream_elem_bits(g, c));
     const int vdef = small && wbits <= 4 ? 4 : 128 / wbits;
     V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", vdef), 128 / wbits)));
+    V = align_lanes(c, V);
   }
   c.V = V;
   // A 4-bit result is stored a whole byte at a time: each lane needs an even
@@ -490,8 +574,8 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     P.lane_in = lin;
     P.lane_out = lout;
     long long DU = rt.dims[lout], DW = rt.dims[lin];
-    int vout = vec_width(DU, std::max(1, 16 / dtype_bytes(rt.dt)));
-    int vin = vec_width(DW, std::max(1, 16 / stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt))));
+    int vout = align_lanes(st, vec_width(DU, std::max(1, 16 / dtype_bytes(rt.dt))));
+    int vin = align_lanes(ld, vec_width(DW, std::max(1, 16 / stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt)))));
     ld.V = vin;
     st.V = vout;
     const long long in_row_bytes = DW * stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt));
@@ -628,7 +712,7 @@ Plan plan_reduce(const Graph &g) {
     c = make_ctx(g, rin, c.lane);
     int V = 1;
     if (c.lane >= 0 && !c.general)
-      V = vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4)));
+      V = align_lanes(c, vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4))));
     c.V = V;
     long long kv = K / V;
     int block, tpr;
@@ -670,7 +754,7 @@ Plan plan_reduce(const Graph &g) {
   } else {
     P.hero = HF_HERO_COLUMN_REDUCE;
     c = make_ctx(g, rin, order[0]);
-    int V = c.general ? 1 : vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4)));
+    int V = c.general ? 1 : align_lanes(c, vec_width(it.dims[c.lane], std::max(1, 16 / stream_elem_bytes(g, c, 4))));
     c.V = V;
     long long Cc = J, Rr = K;
     // 32 column lanes: 128-bit lanes over 512-byte row segments, 8 row lanes

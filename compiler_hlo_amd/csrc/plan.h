@@ -13,15 +13,24 @@ namespace hf {
 // One component of an index vector, as a function of the variables of the
 // space it is expressed in (i0, i1, ...): a variable, the constant 0 (a
 // broadcast or size-1 dimension), or a general expression (after a reshape
-// that is not a pure insertion/removal of size-1 dimensions).
+// that is not a pure insertion/removal of size-1 dimensions).  A variable may
+// carry an offset (a slice): `add` is known on the host, `dyn` names a
+// wave-uniform value the kernel reads at launch (a dynamic_slice start).
 struct Term {
   enum Kind { ZERO, VAR, EXPR } k = ZERO;
   int var = -1;
   std::string e;
+  long long add = 0;
+  std::string dyn;
 };
 using Index = std::vector<Term>;
 
 std::string term_str(const Term &t);
+// t + c + dyn (dyn: "" or the name of a run-time offset)
+Term shifted(const Term &t, long long c, const std::string &dyn);
+// Name of the kernel value holding the clamped start index of dim d of the
+// dynamic_slice node n ("" when the start is known on the host).
+std::string dyn_start_name(int n, int d);
 std::string index_key(const Index &E);
 Index identity_index(int rank);
 
@@ -66,8 +75,6 @@ struct Plan {
   long long grid = 1;
   int lds_bytes = 0;
   long long ws_bytes = 0;     // workspace (column reduce)
-  long long ws_counter_off = 0;
-  int ws_counters = 0;
   bool empty = false;         // nothing to launch (zero-size result)
   hf_plan_info info{};
   std::vector<int> quant_args;  // quant indices passed as per-axis arrays

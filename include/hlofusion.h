@@ -38,9 +38,10 @@
 extern "C" {
 #endif
 
-#define HF_ABI_VERSION 3
+#define HF_ABI_VERSION 4
 #define HF_MAX_RANK 8
-#define HF_MAX_OPERANDS 8               /* concatenate is variadic */
+#define HF_MAX_OPERANDS 9               /* concatenate is variadic; dynamic_slice takes the
+                                           operand and one start index per dim */
 #define HF_MAX_ATTR (3 * HF_MAX_RANK)   /* pad: low, high and interior per dim */
 #define HF_MAX_PARAMS 16
 #define HF_MAX_NODES 256
@@ -108,6 +109,18 @@ typedef enum {
  *                         operand element, else padding_value.
  *   HF_CONCATENATE        concatenate, operands = inputs (1..HF_MAX_OPERANDS),
  *                         attr[0] = dimension.
+ *   HF_SLICE              slice, attr = start_indices[rank], limit_indices[rank],
+ *                         strides[rank] (the attribute names of "Programs"):
+ *                         result[i] = operand[start + i * strides], with
+ *                         0 <= start <= limit <= dim(operand), strides >= 1 and
+ *                         dim(result) = ceil((limit - start) / strides).
+ *   HF_DYNAMIC_SLICE      dynamic_slice, operands = {operand, start index of
+ *                         dim 0, ..., of dim rank-1}, attr = slice_sizes[rank]:
+ *                         result[i] = operand[clamp(0, start, dim(operand) -
+ *                         slice_sizes) + i] (StableHLO Specification,
+ *                         "dynamic_slice").  The start indices are rank-0
+ *                         integer parameters or constants of one type; a
+ *                         parameter is read on the device at every launch.
  * The elementwise ops (add ... abs) also take per-tensor quantized operands
  * and results of one baseline type: the operands are dequantized, the op runs
  * on the f32 values and its result is quantized to the result type (each op's
@@ -137,7 +150,9 @@ typedef enum {
   HF_REVERSE = 20,
   HF_IOTA = 21,
   HF_PAD = 22,
-  HF_CONCATENATE = 23
+  HF_CONCATENATE = 23,
+  HF_SLICE = 24,
+  HF_DYNAMIC_SLICE = 25
 } hf_op;
 
 /* HF_REDUCER_ARGMAX is the variadic max/argmax reduce of Operation semantics
@@ -192,11 +207,13 @@ typedef struct {
   int32_t operands[HF_MAX_OPERANDS];
   hf_type type;                 /* result type, stated explicitly */
   int32_t parameter_number;     /* HF_PARAMETER */
-  double constant;              /* HF_CONSTANT */
+  double constant;              /* HF_CONSTANT (an integer constant is rank 0 and
+                                   serves only as a dynamic_slice start index) */
   int32_t n_attr;
   int64_t attr[HF_MAX_ATTR];    /* permutation | broadcast_dimensions | dimensions |
                                    iota_dimension | pad's low, high, interior |
-                                   concatenate's dimension */
+                                   concatenate's dimension | slice's start, limit,
+                                   strides | dynamic_slice's slice_sizes */
   int32_t reducer;              /* HF_REDUCE: an hf_reducer value */
   double init_value;            /* HF_REDUCE (for HF_REDUCER_ARGMAX: the value
                                    init; `constant` holds the index init) */

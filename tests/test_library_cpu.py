@@ -33,7 +33,7 @@ def test_exports_every_declared_function():
     lib = H.library()
     for name in sorted(declared):
         assert hasattr(lib, name), name
-    assert lib.hf_abi_version() == H.ABI_VERSION == 3
+    assert lib.hf_abi_version() == H.ABI_VERSION == 4
 
 
 C_CLIENT = r"""
@@ -110,7 +110,7 @@ def test_header_is_c99_and_plans_from_c(tmp_path):
     lines = out.stdout.splitlines()
     assert lines[0] == "hero 1 bytes 134217728"
     assert lines[1].startswith("invalid 1 ") and "permutation" in lines[1] and lines[1].endswith("null 1")
-    assert lines[2] == "abi 3"
+    assert lines[2] == "abi 4"
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -418,6 +418,95 @@ def test_index_transform_validation():
         v = s.constant(0.5, "f32", [])
         s.pad(r, v, [1, -1], [0, 2], [0, 1], "f32", [8, 4])
     assert st(ok) == ("HF_OK", "")
+
+
+def test_slice_validation():
+    """slice (start/limit/strides) and dynamic_slice (StableHLO Specification,
+    "dynamic_slice", C1-C5) constraints; integer constants only as start
+    indices."""
+    def st(build):
+        s = W.Spec()
+        build(s)
+        return _status(s.nodes)
+    def sl(start, limit, strides, out):
+        def b(s):
+            p = s.parameter(0, "f32", [6, 8])
+            s.slice(p, start, limit, strides, "f32", out)
+        return st(b)
+    assert sl([1, 2], [5, 8], [1, 3], [4, 2]) == ("HF_OK", "")
+    assert sl([0, 0], [6, 8], [4, 5], [2, 2]) == ("HF_OK", "")
+    assert sl([3, 0], [2, 8], [1, 1], [0, 8])[0] == "HF_ERR_INVALID"          # start > limit
+    assert sl([0, 0], [7, 8], [1, 1], [7, 8])[0] == "HF_ERR_INVALID"          # limit > dim
+    assert sl([0, 0], [6, 8], [0, 1], [6, 8])[0] == "HF_ERR_INVALID"          # stride 0
+    assert "ceil" in sl([0, 0], [6, 8], [4, 3], [2, 2])[1]                    # 8/3 -> 3 columns
+    def ds(sizes, out, start_dtypes=("s32", "s32"), nstarts=2, const=False):
+        def b(s):
+            p = s.parameter(0, "f32", [6, 8])
+            if const:
+                starts = [s.constant(1, start_dtypes[k], []) for k in range(nstarts)]
+            else:
+                starts = [s.parameter(1 + k, start_dtypes[k], []) for k in range(nstarts)]
+            s.dynamic_slice(p, starts, sizes, "f32")
+            s.nodes[-1]["dims"] = list(out)
+        return st(b)
+    assert ds([2, 3], [2, 3]) == ("HF_OK", "")
+    assert ds([2, 3], [2, 3], ("u8", "u8")) == ("HF_OK", "")
+    assert ds([2, 3], [2, 3], const=True) == ("HF_OK", "")
+    assert "(C2)" in ds([2, 3], [2, 3], nstarts=1)[1]
+    assert "(C3)" in ds([2, 3], [2, 3], ("s32", "s8"))[1]
+    assert "(C4)" in ds([7, 3], [7, 3])[1]
+    assert "(C5)" in ds([2, 3], [3, 2])[1]
+    assert "(I2)" in ds([2, 3], [2, 3], ("f32", "f32"))[1]
+    def int_const_elsewhere(s):
+        p = s.parameter(0, "f32", [4])
+        c = s.constant(2, "s32", [4])
+        s.binary("add", p, p, "f32", [4])
+        s.nodes.append(s.nodes[c])
+    assert st(int_const_elsewhere)[0] == "HF_ERR_UNSUPPORTED"
+    def computed_start(s):
+        p = s.parameter(0, "f32", [6, 8])
+        a = s.parameter(1, "s32", [])
+        b = s.convert(s.parameter(2, "f32", []), "f32", [])
+        s.dynamic_slice(p, [a, a], [2, 2], "f32")
+        s.nodes[-1]["operands"][2] = b
+    assert st(computed_start)[0] == "HF_ERR_INVALID"
+
+
+def test_slice_plans():
+    """A slice keeps 128-bit lanes when its start along the minor dim is a
+    multiple of the vector width and counts only the elements it reads; a
+    dynamic start along the minor dim reads one element per lane."""
+    s = W.Spec()
+    p = s.parameter(0, "f32", [64, 256])
+    s.slice(p, [3, 8], [40, 200], [1, 1], "f32", [37, 192])
+    pl = plan_of(s)
+    assert pl["hero"] == "loop" and pl["vector_elems"] == 4
+    assert pl["algorithmic_bytes"] == 2 * 37 * 192 * 4
+    s = W.Spec()
+    p = s.parameter(0, "f32", [64, 256])
+    s.slice(p, [3, 6], [40, 198], [1, 1], "f32", [37, 192])
+    assert plan_of(s)["vector_elems"] == 2
+    s = W.Spec()
+    p = s.parameter(0, "bf16", [64, 256])
+    a, b = s.parameter(1, "s32", []), s.parameter(2, "s32", [])
+    s.dynamic_slice(p, [a, b], [16, 128], "bf16")
+    pl = plan_of(s)
+    assert pl["algorithmic_bytes"] == 2 * 16 * 128 * 2 + 8
+    src = H.Fusion(s.nodes, mode="compile").source()
+    assert "hf_clampi((int)hf_a_p1[0], 0, 48)" in src and "hf_clampi((int)hf_a_p2[0], 0, 128)" in src
+    # a start along a dim sliced whole is 0 whatever the parameter holds
+    s = W.Spec()
+    p = s.parameter(0, "f32", [64, 256])
+    a, b = s.parameter(1, "s32", []), s.parameter(2, "s32", [])
+    s.dynamic_slice(p, [a, b], [16, 256], "f32")
+    src = H.Fusion(s.nodes, mode="compile").source()
+    assert "hf_a_p2[0]" not in src and "hf_raw_ld<16, true>" in src
+    # the transposed read of a slice still picks the transpose hero
+    s = W.Spec()
+    p = s.parameter(0, "f32", [512, 512])
+    q = s.slice(p, [0, 64], [512, 448], [1, 1], "f32", [512, 384])
+    s.transpose(q, [1, 0], "f32", [384, 512])
+    assert plan_of(s)["hero"] == "transpose"
 
 
 def test_reduce_epilogue_is_planned_as_a_second_context():
