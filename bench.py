@@ -58,6 +58,8 @@ class Case:
             self.params = transform(self.params)
         self.fusion = H.Fusion(self.spec.nodes)
         self.plan = self.fusion.plan()
+        # one workspace: every launch of the case runs on one stream
+        self.ws = torch.empty(max(1, self.plan["workspace_bytes"]), dtype=torch.uint8, device="cuda")
         self.bytes = self.plan["algorithmic_bytes"]
         work = self.bytes
         if sets is None:
@@ -66,7 +68,7 @@ class Case:
         base = device_params(self.params)
         for s in range(sets):
             ins = base if s == 0 else [t.clone() for t in base]
-            out = self.fusion(*ins)
+            out = self.fusion(*ins, workspace=self.ws)
             self.sets.append((ins, out))
         torch.cuda.synchronize()
         self.k = 0
@@ -74,7 +76,8 @@ class Case:
     def launch(self, stream):
         ins, out = self.sets[self.k % len(self.sets)]
         self.k += 1
-        self.fusion.launch_ptrs([t.data_ptr() for t in ins], out.data_ptr(), stream.cuda_stream)
+        self.fusion.launch_ptrs([t.data_ptr() for t in ins], out.data_ptr(), stream.cuda_stream,
+                                self.ws.data_ptr() if self.plan["workspace_bytes"] else 0)
 
 
 def copy_case(dtype, dims):

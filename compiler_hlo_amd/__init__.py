@@ -137,8 +137,9 @@ def _load():
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.hf_fusion_launch.restype = ctypes.c_int
     lib.hf_fusion_launch.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
-                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    lib.hf_fusion_destroy.restype = None
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.hf_fusion_destroy.restype = ctypes.c_int
     lib.hf_fusion_destroy.argtypes = [ctypes.c_void_p]
     lib.hf_last_error.restype = ctypes.c_char_p
     lib.hf_abi_version.restype = ctypes.c_int32
@@ -260,15 +261,26 @@ class Fusion:
         _check(_lib.hf_fusion_source(self._h, buf, n.value + 1, ctypes.byref(n)))
         return buf.value.decode()
 
-    def launch_ptrs(self, param_ptrs, out_ptr: int, stream: int = 0):
-        """Launch with raw device pointers (ints) on a raw hipStream_t."""
+    @property
+    def workspace_bytes(self) -> int:
+        """Scratch bytes a launch needs (0 for most plans)."""
+        return self.plan()["workspace_bytes"]
+
+    def launch_ptrs(self, param_ptrs, out_ptr: int, stream: int = 0, workspace: int = 0):
+        """Launch with raw device pointers (ints) on a raw hipStream_t;
+        `workspace` is a device pointer of workspace_bytes bytes (0 when none
+        is needed)."""
         arr = (ctypes.c_void_p * max(1, len(param_ptrs)))(*param_ptrs)
         _check(_lib.hf_fusion_launch(self._h, arr, len(param_ptrs), ctypes.c_void_p(out_ptr),
-                                     ctypes.c_void_p(stream)))
+                                     ctypes.c_void_p(workspace), ctypes.c_void_p(stream)))
 
-    def __call__(self, *params, out=None, stream=None):
+    def __call__(self, *params, out=None, stream=None, workspace=None):
         """Run on torch tensors (flat, physical order, on the GPU); returns the
-        result tensor (allocated with torch.empty if `out` is None)."""
+        result tensor (allocated with torch.empty if `out` is None).  A plan
+        that needs a workspace takes `workspace` (a uint8 GPU tensor of at
+        least workspace_bytes) or, when it is None, a fresh one from torch's
+        allocator on the launch stream, which the allocator reuses only after
+        this launch on that stream."""
         import torch
         if len(params) != self.n_params:
             raise ValueError("expected %d parameters, got %d" % (self.n_params, len(params)))
@@ -294,12 +306,29 @@ class Fusion:
             raise ValueError("out must be a dense GPU tensor of %d %s items" % (n_out, tdt))
         if stream is None:
             stream = torch.cuda.current_stream()
-        self.launch_ptrs([p.data_ptr() for p in params], out.data_ptr(), stream.cuda_stream)
+        ws_ptr = 0
+        nws = self._ws_bytes()
+        if nws:
+            if workspace is None:
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty(nws, dtype=torch.uint8, device=out.device)
+            elif not workspace.is_cuda or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nws:
+                raise ValueError("workspace must be a dense GPU tensor of at least %d bytes" % nws)
+            ws_ptr = workspace.data_ptr()
+        self.launch_ptrs([p.data_ptr() for p in params], out.data_ptr(), stream.cuda_stream, ws_ptr)
         return out
 
+    def _ws_bytes(self) -> int:
+        if not hasattr(self, "_nws"):
+            self._nws = self.workspace_bytes
+        return self._nws
+
     def close(self):
+        """Destroy the handle (waits for the device first).  Raises
+        FusionError if the library could not release it (the handle then
+        stays open)."""
         if getattr(self, "_h", None):
-            _lib.hf_fusion_destroy(self._h)
+            _check(_lib.hf_fusion_destroy(self._h))
             self._h = None
 
     def __del__(self):

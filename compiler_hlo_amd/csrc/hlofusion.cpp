@@ -35,7 +35,6 @@ struct hf_fusion {
   hipModule_t mod = nullptr;
   hipFunction_t fn = nullptr;
   hipFunction_t fold = nullptr;  // column reduce: segment fold kernel
-  void *ws = nullptr;
   std::vector<void *> qdev;  // scales, zero points per per-axis quant type
 };
 
@@ -181,10 +180,12 @@ void dump(const hf_fusion *f) {
   std::ofstream(std::string(d) + "/" + name + ".plan.txt") << plan_text(f);
 }
 
+// Frees what create made.  The caller has made sure that no launch of the
+// handle is still running (hf_fusion_destroy waits for the device first; a
+// handle that failed inside create was never launched).
 void release(hf_fusion *f) {
   if (!f) return;
   if (f->mod) (void)hipModuleUnload(f->mod);
-  if (f->ws) (void)hipFree(f->ws);
   for (void *p : f->qdev)
     if (p) (void)hipFree(p);
   delete f;
@@ -207,10 +208,6 @@ hf_status load_on_device(hf_fusion *f) {
   if (f->P.fold_grid > 0) {
     e = hipModuleGetFunction(&f->fold, f->mod, f->P.fold_name.c_str());
     if (e != hipSuccess) return hip_fail(e, "hipModuleGetFunction(fold)");
-  }
-  if (f->P.ws_bytes > 0) {
-    e = hipMalloc(&f->ws, (size_t)f->P.ws_bytes);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
   }
   f->qdev.reserve(3 * f->P.quant_args.size());  // push_back below cannot throw
   for (int q : f->P.quant_args) {
@@ -237,6 +234,136 @@ hf_status load_on_device(hf_fusion *f) {
       return hip_fail(e, "hipMemcpy(zero points)");
     if ((e = hipMemcpy(rc, rb.data(), n * 8, hipMemcpyHostToDevice)) != hipSuccess)
       return hip_fail(e, "hipMemcpy(reciprocal scales)");
+  }
+  return HF_OK;
+}
+
+// The launch behind the entry points.  check_ws: the workspace is the
+// caller's and is checked like the other buffers (the library's own scratch
+// memory is not).
+hf_status launch(hf_fusion *f, const void *const *params, int32_t n_params, void *result, void *workspace,
+                 bool check_ws, void *stream) {
+  if (!f) {
+    set_err("NULL handle");
+    return HF_ERR_INVALID;
+  }
+  if (f->plan_only || f->compile_only || !f->fn) {
+    set_err("the handle was created without loading a kernel (plan-only or compile-only)");
+    return HF_ERR_INVALID;
+  }
+  if (n_params != f->g.n_params || (n_params > 0 && !params)) {
+    set_err("expected " + std::to_string(f->g.n_params) + " parameter pointers, got " + std::to_string(n_params));
+    return HF_ERR_INVALID;
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != f->device) {
+    set_err("the current device differs from the device the fusion was created on");
+    return HF_ERR_INVALID;
+  }
+  // A buffer must be device memory of this device (or managed memory), with
+  // its whole extent inside one allocation: anything else is rejected here,
+  // before a kernel could fault on it.
+  auto check_buffer = [&](const void *p, size_t bytes, const std::string &what) -> bool {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the failed query to the next call
+      set_err(what + " is not device memory");
+      return false;
+    }
+    const bool managed = a.isManaged || a.type == hipMemoryTypeManaged;
+    if (!managed && (a.type != hipMemoryTypeDevice || a.device != f->device)) {
+      set_err(what + " is not device memory of the fusion's device");
+      return false;
+    }
+    if (!managed) {
+      hipDeviceptr_t base = nullptr;
+      size_t size = 0;
+      if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err(what + ": hipMemGetAddressRange failed");
+        return false;
+      }
+      if ((uintptr_t)p + bytes > (uintptr_t)base + size) {
+        set_err(what + " extends past the end of its allocation");
+        return false;
+      }
+    }
+    return true;
+  };
+  const hf::Type &rt = f->g.nodes[f->g.root].t;
+  const size_t rbytes = (size_t)hf::storage_bytes(rt.dt, rt.numel());
+  const uintptr_t r0 = (uintptr_t)result;
+  const uintptr_t r1 = r0 + (uintptr_t)rbytes;
+  if (rt.numel() > 0 && (!result || (r0 & 15))) {
+    set_err("result must be a non-NULL, 16-byte aligned device pointer");
+    return HF_ERR_INVALID;
+  }
+  if (rt.numel() > 0 && !check_buffer(result, rbytes, "the result")) return HF_ERR_INVALID;
+  for (int k = 0; k < n_params; ++k) {
+    int pn = f->g.param_node[k];
+    if (pn < 0) continue;
+    const hf::Type &pt = f->g.nodes[pn].t;
+    if (pt.numel() == 0) continue;
+    uintptr_t p0 = (uintptr_t)params[k], p1 = p0 + (uintptr_t)hf::storage_bytes(pt.dt, pt.numel());
+    if (!params[k] || (p0 & 15)) {
+      set_err("parameter " + std::to_string(k) + " must be a non-NULL, 16-byte aligned device pointer");
+      return HF_ERR_INVALID;
+    }
+    if (!check_buffer(params[k], (size_t)(p1 - p0), "parameter " + std::to_string(k))) return HF_ERR_INVALID;
+    if (rt.numel() > 0 && p0 < r1 && r0 < p1) {
+      set_err("the result buffer overlaps parameter " + std::to_string(k));
+      return HF_ERR_INVALID;
+    }
+  }
+  // The workspace: scratch for this launch only (a column reduce's segment
+  // partials), in the caller's memory, so that launches in flight at the
+  // same time never share it.
+  const size_t wbytes = (size_t)f->P.ws_bytes;
+  if (wbytes > 0 && check_ws) {
+    const uintptr_t w0 = (uintptr_t)workspace, w1 = w0 + wbytes;
+    if (!workspace || (w0 & 15)) {
+      set_err("this fusion needs a workspace of " + std::to_string(wbytes) +
+              " bytes: a non-NULL, 16-byte aligned device pointer");
+      return HF_ERR_INVALID;
+    }
+    if (!check_buffer(workspace, wbytes, "the workspace")) return HF_ERR_INVALID;
+    if (rt.numel() > 0 && w0 < r1 && r0 < w1) {
+      set_err("the workspace overlaps the result buffer");
+      return HF_ERR_INVALID;
+    }
+    for (int k = 0; k < n_params; ++k) {
+      int pn = f->g.param_node[k];
+      if (pn < 0) continue;
+      const hf::Type &pt = f->g.nodes[pn].t;
+      const uintptr_t p0 = (uintptr_t)params[k], p1 = p0 + (uintptr_t)hf::storage_bytes(pt.dt, pt.numel());
+      if (pt.numel() > 0 && p0 < w1 && w0 < p1) {
+        set_err("the workspace overlaps parameter " + std::to_string(k));
+        return HF_ERR_INVALID;
+      }
+    }
+  }
+  if (f->P.empty) return HF_OK;
+  // Kernel arguments, in the generated kernel's order: parameters, result,
+  // the per-axis quantization arrays, the workspace.  On the stack: a launch
+  // allocates nothing.
+  constexpr int kMaxArgs = HF_MAX_NODES + 1 + 3 * HF_MAX_NODES + 1;
+  void *vals[kMaxArgs];
+  void *ptrs[kMaxArgs];
+  int na = 0;
+  for (int k = 0; k < n_params; ++k) vals[na++] = const_cast<void *>(params[k]);
+  vals[na++] = result;
+  for (void *q : f->qdev) vals[na++] = q;
+  vals[na++] = wbytes > 0 ? workspace : nullptr;
+  for (int k = 0; k < na; ++k) ptrs[k] = &vals[k];
+  e = hipModuleLaunchKernel(f->fn, (unsigned)f->P.grid, 1, 1, (unsigned)f->P.block, 1, 1, 0, (hipStream_t)stream,
+                            ptrs, nullptr);
+  if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
+  if (f->fold) {
+    e = hipModuleLaunchKernel(f->fold, (unsigned)f->P.fold_grid, 1, 1, 256, 1, 1, 0, (hipStream_t)stream, ptrs,
+                              nullptr);
+    if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(fold)");
   }
   return HF_OK;
 }
@@ -338,105 +465,26 @@ hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *le
   return HF_OK;
 }
 
-hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params, void *result, void *stream) {
-  if (!f) {
-    set_err("NULL handle");
-    return HF_ERR_INVALID;
-  }
-  if (f->plan_only || f->compile_only || !f->fn) {
-    set_err("the handle was created without loading a kernel (plan-only or compile-only)");
-    return HF_ERR_INVALID;
-  }
-  if (n_params != f->g.n_params || (n_params > 0 && !params)) {
-    set_err("expected " + std::to_string(f->g.n_params) + " parameter pointers, got " + std::to_string(n_params));
-    return HF_ERR_INVALID;
-  }
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != f->device) {
-    set_err("the current device differs from the device the fusion was created on");
-    return HF_ERR_INVALID;
-  }
-  // A buffer must be device memory of this device (or managed memory), with
-  // its whole extent inside one allocation: anything else is rejected here,
-  // before a kernel could fault on it.
-  auto check_buffer = [&](const void *p, size_t bytes, const std::string &what) -> bool {
-    hipPointerAttribute_t a;
-    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-      (void)hipGetLastError();  // do not leave the failed query to the next call
-      set_err(what + " is not device memory");
-      return false;
-    }
-    const bool managed = a.isManaged || a.type == hipMemoryTypeManaged;
-    if (!managed && (a.type != hipMemoryTypeDevice || a.device != f->device)) {
-      set_err(what + " is not device memory of the fusion's device");
-      return false;
-    }
-    if (!managed) {
-      hipDeviceptr_t base = nullptr;
-      size_t size = 0;
-      if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
-        (void)hipGetLastError();
-        set_err(what + ": hipMemGetAddressRange failed");
-        return false;
-      }
-      if ((uintptr_t)p + bytes > (uintptr_t)base + size) {
-        set_err(what + " extends past the end of its allocation");
-        return false;
-      }
-    }
-    return true;
-  };
-  const hf::Type &rt = f->g.nodes[f->g.root].t;
-  const size_t rbytes = (size_t)hf::storage_bytes(rt.dt, rt.numel());
-  const uintptr_t r0 = (uintptr_t)result;
-  const uintptr_t r1 = r0 + (uintptr_t)rbytes;
-  if (rt.numel() > 0 && (!result || (r0 & 15))) {
-    set_err("result must be a non-NULL, 16-byte aligned device pointer");
-    return HF_ERR_INVALID;
-  }
-  if (rt.numel() > 0 && !check_buffer(result, rbytes, "the result")) return HF_ERR_INVALID;
-  for (int k = 0; k < n_params; ++k) {
-    int pn = f->g.param_node[k];
-    if (pn < 0) continue;
-    const hf::Type &pt = f->g.nodes[pn].t;
-    if (pt.numel() == 0) continue;
-    uintptr_t p0 = (uintptr_t)params[k], p1 = p0 + (uintptr_t)hf::storage_bytes(pt.dt, pt.numel());
-    if (!params[k] || (p0 & 15)) {
-      set_err("parameter " + std::to_string(k) + " must be a non-NULL, 16-byte aligned device pointer");
-      return HF_ERR_INVALID;
-    }
-    if (!check_buffer(params[k], (size_t)(p1 - p0), "parameter " + std::to_string(k))) return HF_ERR_INVALID;
-    if (rt.numel() > 0 && p0 < r1 && r0 < p1) {
-      set_err("the result buffer overlaps parameter " + std::to_string(k));
-      return HF_ERR_INVALID;
-    }
-  }
-  if (f->P.empty) return HF_OK;
-  // Kernel arguments, in the generated kernel's order: parameters, result,
-  // the per-axis quantization arrays, the workspace.  On the stack: a launch
-  // allocates nothing.
-  constexpr int kMaxArgs = HF_MAX_NODES + 1 + 3 * HF_MAX_NODES + 1;
-  void *vals[kMaxArgs];
-  void *ptrs[kMaxArgs];
-  int na = 0;
-  for (int k = 0; k < n_params; ++k) vals[na++] = const_cast<void *>(params[k]);
-  vals[na++] = result;
-  for (void *q : f->qdev) vals[na++] = q;
-  vals[na++] = f->ws;
-  for (int k = 0; k < na; ++k) ptrs[k] = &vals[k];
-  e = hipModuleLaunchKernel(f->fn, (unsigned)f->P.grid, 1, 1, (unsigned)f->P.block, 1, 1, 0, (hipStream_t)stream,
-                            ptrs, nullptr);
-  if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel");
-  if (f->fold) {
-    e = hipModuleLaunchKernel(f->fold, (unsigned)f->P.fold_grid, 1, 1, 256, 1, 1, 0, (hipStream_t)stream, ptrs,
-                              nullptr);
-    if (e != hipSuccess) return hip_fail(e, "hipModuleLaunchKernel(fold)");
-  }
-  return HF_OK;
+hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params, void *result, void *workspace,
+                           void *stream) {
+  return launch(f, params, n_params, result, workspace, true, stream);
 }
 
-void hf_fusion_destroy(hf_fusion *f) { release(f); }
+hf_status hf_fusion_destroy(hf_fusion *f) {
+  if (!f) return HF_OK;
+  if (f->mod) {
+    // Launches of the handle may still be running: wait for the device
+    // before the code object and the quantization arrays go away.
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != f->device && (e = hipSetDevice(f->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    e = hipDeviceSynchronize();
+    if (cur != f->device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before releasing the fusion (nothing released)");
+  }
+  release(f);
+  return HF_OK;
+}
 
 }  // extern "C"

@@ -13,9 +13,11 @@
  *                      generate HIP source for it, compile it for gfx950 and
  *                      load it on the current device.  All validation happens
  *                      here, on the host, before any GPU call.
- *   hf_fusion_launch   run it on a caller-supplied stream; asynchronous; no
- *                      allocation, no synchronisation.
- *   hf_fusion_destroy  release what create allocated.
+ *   hf_fusion_launch   run it on a caller-supplied stream with caller-owned
+ *                      buffers; asynchronous; no allocation, no
+ *                      synchronisation.
+ *   hf_fusion_destroy  wait for the device, then release what create
+ *                      allocated.
  *
  * Conventions:
  *   - Every function has C linkage and takes plain pointers and sizes only.
@@ -24,9 +26,13 @@
  *   - Errors: every call returns an hf_status; hf_last_error() gives a
  *     message for the last failing call on the calling thread.
  *   - A fusion handle is immutable after create and bound to the device that
- *     was current at create.  Launches of ONE handle must not overlap in time
- *     (same stream, or synchronised), because a column-reduce plan keeps its
- *     cross-workgroup partials and counters in the handle's workspace.
+ *     was current at create.  Launches hold no state in the handle: one handle
+ *     may be launched from several threads and on several streams at once, as
+ *     long as the buffers each launch writes (its result and its workspace)
+ *     are not in use by another launch in flight.  The fusion computation
+ *     writes only into the buffers it is given (XLA:GPU Emitters, "Loop
+ *     emitter": the entry function inserts its results into the result
+ *     buffers it receives).
  */
 #ifndef HLOFUSION_H
 #define HLOFUSION_H
@@ -256,8 +262,13 @@ typedef struct {
 #define HF_CREATE_PLAN_ONLY 1u     /* validate and plan; no code, no GPU */
 #define HF_CREATE_COMPILE_ONLY 2u  /* also generate and compile; no GPU */
 
-/* Validate, plan, generate, compile and load.  On success *out owns a handle
- * to free with hf_fusion_destroy.  Errors: HF_ERR_INVALID for a descriptor
+/* Validate, plan, generate, compile and load.  The descriptor is the fusion
+ * instruction's called computation: its parameters, the op DAG in topological
+ * order and its root (XLA:GPU Emitters: a fusion is an instruction with
+ * operands and a called computation, "kind=kLoop, calls=..."; "Hero-based
+ * codegen" picks the emitter from it).  The library copies what it needs;
+ * the descriptor and every host array it points to may be freed on return.
+ * On success *out owns a handle to free with hf_fusion_destroy.  Errors: HF_ERR_INVALID for a descriptor
  * that breaks an op's constraints (message names the node), HF_ERR_UNSUPPORTED
  * for a valid fusion this library does not implement (among them a parameter
  * or result of 2 GiB or more, or any value of 2^31 elements or more: the
@@ -273,25 +284,43 @@ hf_status hf_fusion_plan(const hf_fusion *f, hf_plan_info *info);
  * was created with HF_CREATE_PLAN_ONLY. */
 hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *len);
 
-/* Run the fusion.  params[i] is the DEVICE pointer of parameter i (dense, in
- * its declared layout, 16-byte aligned; numel * element size bytes, 4-bit
- * types packed as described at hf_dtype); result is the device pointer of the
- * root buffer (dense, root layout, 16-byte aligned, not overlapping any
- * parameter).  The same parameter pointer may be passed twice.  stream is a
- * hipStream_t (NULL = the null stream).  The launch is asynchronous and
- * allocates nothing; a fault inside the kernel surfaces at the caller's next
- * synchronisation.  Each buffer must be device memory of the fusion's
- * device (or managed memory) whose whole extent lies in one allocation; host
- * memory, pinned or not, is rejected.  Errors: HF_ERR_INVALID (count, NULL,
- * alignment, overlap, not device memory, extent past its allocation,
- * plan-only handle, wrong current device), HF_ERR_HIP.  Launches of one
- * handle must not overlap in time (a column reduce's workspace belongs to the
- * handle). */
+/* Run the fusion (XLA:GPU Emitters, "Loop emitter": the entry function takes
+ * the parameters and the result buffers and writes its results only into
+ * those).  params[i] is the DEVICE pointer of parameter i (dense, in its
+ * declared layout, 16-byte aligned; numel * element size bytes, 4-bit types
+ * packed as described at hf_dtype); result is the device pointer of the root
+ * buffer (dense, root layout, 16-byte aligned, not overlapping any
+ * parameter).  The same parameter pointer may be passed twice, as the pages'
+ * ABI passes two tensors that share a buffer slice once (XLA:GPU Emitters,
+ * the passes that merge pointers to the same slice).
+ *
+ * workspace is scratch memory for this launch only, owned by the caller: a
+ * device buffer of at least hf_plan_info.workspace_bytes bytes, 16-byte
+ * aligned, overlapping neither the result nor a parameter.  Its contents on
+ * entry do not matter and are undefined afterwards.  It may be NULL when
+ * workspace_bytes is 0 (every plan except a column reduce whose reduced
+ * extent is split into several segments).  Two launches in flight at the same
+ * time need two workspaces.
+ *
+ * stream is a hipStream_t (NULL = the null stream).  The launch is
+ * asynchronous and allocates nothing; a fault inside the kernel surfaces at
+ * the caller's next synchronisation.  Each buffer must be device memory of
+ * the fusion's device (or managed memory) whose whole extent lies in one
+ * allocation; host memory, pinned or not, is rejected.  Errors:
+ * HF_ERR_INVALID (count, NULL, alignment, overlap, not device memory, extent
+ * past its allocation, workspace missing or too small, plan-only handle,
+ * wrong current device), HF_ERR_HIP. */
 hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params,
-                           void *result, void *stream);
+                           void *result, void *workspace, void *stream);
 
-/* Release the handle (NULL is allowed). */
-void hf_fusion_destroy(hf_fusion *f);
+/* Release the handle (NULL is allowed).  It first waits for all work on the
+ * fusion's device (hipDeviceSynchronize), so launches still in flight finish
+ * before their code object is unloaded.  A HIP graph that captured a launch
+ * of the handle must not be replayed after it is destroyed.  If the wait
+ * fails (for example while a stream capture forbids it), nothing is released
+ * and HF_ERR_HIP is returned: the handle stays valid and may be destroyed
+ * again later. */
+hf_status hf_fusion_destroy(hf_fusion *f);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *hf_last_error(void);

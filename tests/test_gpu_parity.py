@@ -975,24 +975,30 @@ def test_reduce_special_values(hero):
 # --------------------------------------------------------------------------
 # launches recorded into a HIP graph
 # --------------------------------------------------------------------------
-def test_concurrent_launches_from_threads_on_streams():
-    """Four host threads, each with its own stream (default priority) and
-    its own handles of a loop, a transpose, a row reduce and a column reduce
-    (the column reduce's workspace belongs to its handle), launch 20 rounds
-    at once.  Every output equals the single-threaded result bitwise, and the
-    oracle where exact."""
-    import threading
-    import torch
-    import compiler_hlo_amd as H
-    from harness import from_device, to_device
+def _concurrency_cases():
     makers = [lambda: W.transpose_exp_f32(512, 768, seed=71),
               lambda: W.row_reduce_exp_add_bf16(2, 16, 4096, seed=72),
               lambda: W.column_reduce_max_f32(2048, 1024, seed=73),
               lambda: W.quant_dequant_bias_requant(300, 4096, seed=74)]
-    cases = [mk() for mk in makers]
+    return [mk() for mk in makers]
+
+
+def test_concurrent_launches_of_one_handle_from_threads_on_streams():
+    """ONE handle per hero (a loop, a transpose, a row reduce and a column
+    reduce whose launch needs a workspace), shared by four host threads, each
+    with its own stream (default priority), its own result buffers and its own
+    workspace, launching 20 rounds at once.  Every output equals the
+    single-stream result bitwise, and the oracle where exact."""
+    import threading
+    import torch
+    import compiler_hlo_amd as H
+    from harness import from_device, to_device
+    cases = _concurrency_cases()
+    fs = [H.Fusion(spec.nodes) for spec, _, _ in cases]
+    assert fs[2].plan()["hero"] == "column_reduce" and fs[2].workspace_bytes > 0
     ref = []
-    for spec, params, _ in cases:
-        got, f = run_gpu(spec.nodes, params)
+    for (spec, params, _), f in zip(cases, fs):
+        got, _ = run_gpu(spec.nodes, params, fusion=f)
         ref.append(got)
     assert_bitexact(ref[2], oracle.evaluate(cases[2][0].nodes, cases[2][1]), "f32")
     assert_bitexact(ref[3], oracle.evaluate(cases[3][0].nodes, cases[3][1]), "s8")
@@ -1001,13 +1007,13 @@ def test_concurrent_launches_from_threads_on_streams():
     def worker(t):
         try:
             stream = torch.cuda.Stream()
-            fs = [H.Fusion(spec.nodes) for spec, _, _ in cases]
-            devs = [[to_device(p) for p in params] for _, params, _ in cases]
             with torch.cuda.stream(stream):
-                res = [f(*d, stream=stream) for f, d in zip(fs, devs)]
+                devs = [[to_device(p) for p in params] for _, params, _ in cases]
+                wss = [torch.empty(max(1, f.workspace_bytes), dtype=torch.uint8, device="cuda") for f in fs]
+                res = [f(*d, stream=stream, workspace=w) for f, d, w in zip(fs, devs, wss)]
                 for _ in range(19):
-                    for f, d, r in zip(fs, devs, res):
-                        f(*d, out=r, stream=stream)
+                    for f, d, r, w in zip(fs, devs, res, wss):
+                        f(*d, out=r, stream=stream, workspace=w)
             stream.synchronize()
             outs[t] = [from_device(r, spec.nodes[-1]["dtype"]) for r, (spec, _, _) in zip(res, cases)]
         except Exception as e:  # reported by the main thread
@@ -1025,12 +1031,58 @@ def test_concurrent_launches_from_threads_on_streams():
             assert np.array_equal(outs[t][k].view(np.uint8), ref[k].view(np.uint8)), (t, k)
 
 
+def test_one_handle_on_four_streams_from_one_thread():
+    """One column-reduce handle launched round-robin on four streams from one
+    thread, so that its launches overlap on the device: each stream has its
+    own input, result and workspace.  Every result equals the oracle's."""
+    import torch
+    import compiler_hlo_amd as H
+    from harness import from_device, to_device
+    seeds = [301, 302, 303, 304]
+    specs = [W.column_reduce_max_f32(4096, 2048, seed=s) for s in seeds]
+    f = H.Fusion(specs[0][0].nodes)
+    assert f.plan()["hero"] == "column_reduce" and f.workspace_bytes > 0
+    streams = [torch.cuda.Stream() for _ in seeds]
+    ins, outs, wss = [], [], []
+    for (spec, params, _), st in zip(specs, streams):
+        with torch.cuda.stream(st):
+            ins.append([to_device(p) for p in params])
+            outs.append(torch.empty(2048, dtype=torch.float32, device="cuda"))
+            wss.append(torch.empty(f.workspace_bytes, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    for _ in range(25):
+        for st, i, o, w in zip(streams, ins, outs, wss):
+            f(*i, out=o, stream=st, workspace=w)
+    torch.cuda.synchronize()
+    for (spec, params, _), o in zip(specs, outs):
+        assert_bitexact(from_device(o, "f32"), oracle.evaluate(spec.nodes, params), "f32")
+
+
+def test_destroy_right_after_an_async_launch():
+    """Destroying a handle while its launch may still run waits for the
+    device first: the output is complete and correct afterwards."""
+    import torch
+    import compiler_hlo_amd as H
+    from harness import from_device, to_device
+    spec, params, _ = W.column_reduce_max_f32(8192, 4096, seed=305)
+    x = to_device(params[0])
+    torch.cuda.synchronize()
+    f = H.Fusion(spec.nodes)
+    out = f(x)
+    f.close()
+    torch.cuda.synchronize()
+    assert_bitexact(from_device(out, "f32"), oracle.evaluate(spec.nodes, params), "f32")
+    out2 = H.Fusion(spec.nodes)(x)  # the temporary handle is destroyed at once
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device(out2, "f32").view(np.uint32), from_device(out, "f32").view(np.uint32))
+
+
 @pytest.mark.parametrize("k", range(3))
 def test_launch_in_hip_graph(k):
     """A launch recorded into a HIP graph (torch.cuda.graph) and replayed with
     new inputs copied in, with an eager launch of the same handle between
     replays: every replay equals the eager result bitwise.  The column
-    reduce's launch holds two kernels and the handle's workspace."""
+    reduce's launch holds two kernels and a workspace."""
     import torch
     import compiler_hlo_amd as H
     make = [lambda seed: W.transpose_bf16_021(4, 64, 128, seed=seed),
@@ -1247,6 +1299,28 @@ def test_launch_argument_errors():
     with pytest.raises(H.FusionError) as e:
         f.launch_ptrs([x.data_ptr()], x.data_ptr())
     assert e.value.status == "HF_ERR_INVALID" and "overlaps" in e.value.message
+    # a plan that needs a workspace: missing, misaligned or overlapping
+    cspec, cparams, _ = W.column_reduce_max_f32(4096, 512, seed=7)
+    cf = H.Fusion(cspec.nodes)
+    nws = cf.workspace_bytes
+    assert nws > 0
+    cx = to_device(cparams[0])
+    cout = torch.empty(512, dtype=torch.float32, device="cuda")
+    ws = torch.empty(nws + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(H.FusionError) as e:
+        cf.launch_ptrs([cx.data_ptr()], cout.data_ptr(), 0, 0)
+    assert e.value.status == "HF_ERR_INVALID" and "workspace" in e.value.message
+    with pytest.raises(H.FusionError) as e:
+        cf.launch_ptrs([cx.data_ptr()], cout.data_ptr(), 0, ws.data_ptr() + 4)
+    assert e.value.status == "HF_ERR_INVALID" and "workspace" in e.value.message
+    with pytest.raises(H.FusionError) as e:
+        cf.launch_ptrs([cx.data_ptr()], cout.data_ptr(), 0, cx.data_ptr())
+    assert e.value.status == "HF_ERR_INVALID" and "overlaps" in e.value.message
+    with pytest.raises(ValueError):
+        cf(cx, workspace=torch.empty(nws - 16, dtype=torch.uint8, device="cuda"))
+    cf.launch_ptrs([cx.data_ptr()], cout.data_ptr(), torch.cuda.current_stream().cuda_stream, ws.data_ptr())
+    torch.cuda.synchronize()
+    assert_bitexact(from_device(cout, "f32"), oracle.evaluate(cspec.nodes, cparams), "f32")
     # pinned host memory is not device memory (the GPU could read it, so the
     # launch would not fault even if it were let through)
     h = torch.empty(64 * 64, dtype=torch.float32).pin_memory()
