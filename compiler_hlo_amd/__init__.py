@@ -113,7 +113,9 @@ def node_attr(nd: dict) -> list:
 
 
 EXPORTS = ["hf_fusion_create", "hf_fusion_plan", "hf_fusion_source", "hf_fusion_launch",
-           "hf_fusion_destroy", "hf_last_error", "hf_abi_version", "hf_linear_index"]
+           "hf_fusion_launch_noalloc", "hf_fusion_destroy", "hf_last_error", "hf_abi_version",
+           "hf_linear_index"]
+SCRATCH_BYTES = 16 << 20  # HF_SCRATCH_BYTES: the no-allocation launch's scratch memory per GPU
 
 
 def _load():
@@ -139,6 +141,9 @@ def _load():
     lib.hf_fusion_launch.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p]
+    lib.hf_fusion_launch_noalloc.restype = ctypes.c_int
+    lib.hf_fusion_launch_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.hf_fusion_destroy.restype = ctypes.c_int
     lib.hf_fusion_destroy.argtypes = [ctypes.c_void_p]
     lib.hf_last_error.restype = ctypes.c_char_p
@@ -273,6 +278,14 @@ class Fusion:
         arr = (ctypes.c_void_p * max(1, len(param_ptrs)))(*param_ptrs)
         _check(_lib.hf_fusion_launch(self._h, arr, len(param_ptrs), ctypes.c_void_p(out_ptr),
                                      ctypes.c_void_p(workspace), ctypes.c_void_p(stream)))
+
+    def launch_noalloc_ptrs(self, param_ptrs, out_ptr: int, stream: int = 0):
+        """hf_fusion_launch_noalloc: launch with raw device pointers, the
+        library's per-GPU scratch memory standing in for the workspace (no
+        allocation anywhere; overlapping calls on one GPU race on it)."""
+        arr = (ctypes.c_void_p * max(1, len(param_ptrs)))(*param_ptrs)
+        _check(_lib.hf_fusion_launch_noalloc(self._h, arr, len(param_ptrs), ctypes.c_void_p(out_ptr),
+                                             ctypes.c_void_p(stream)))
 
     def __call__(self, *params, out=None, stream=None, workspace=None):
         """Run on torch tensors (flat, physical order, on the GPU); returns the

@@ -20,6 +20,7 @@
 
 #include "ir.h"
 #include "plan.h"
+#include "scratch.h"
 
 // Device templates, embedded at build time: k_src_common, k_src_loop,
 // k_src_transpose, k_src_reduce_row, k_src_reduce_col.
@@ -201,6 +202,15 @@ hf_status load_on_device(hf_fusion *f) {
     set_err(std::string("this library targets gfx950 (MI355X); current device is ") + prop.gcnArchName);
     return HF_ERR_UNSUPPORTED;
   }
+  {
+    // set-up of the no-allocation launch: this device's scratch address
+    std::string err;
+    const hf_status st = hf::scratch_prepare(f->device, &err);
+    if (st != HF_OK) {
+      set_err(err);
+      return st;
+    }
+  }
   e = hipModuleLoadData(&f->mod, f->code.data());
   if (e != hipSuccess) return hip_fail(e, "hipModuleLoadData");
   e = hipModuleGetFunction(&f->fn, f->mod, f->P.kernel_name.c_str());
@@ -369,6 +379,30 @@ hf_status launch(hf_fusion *f, const void *const *params, int32_t n_params, void
 }
 
 }  // namespace
+
+namespace hf {
+
+hf_status launch_in_scratch(hf_fusion *f, const void *const *params, int32_t n_params, void *result, void *stream) {
+  if (!f) {
+    set_err("NULL handle");
+    return HF_ERR_INVALID;
+  }
+  const long long need = f->P.ws_bytes;
+  if (need > (long long)HF_SCRATCH_BYTES) {
+    set_err("this fusion needs " + std::to_string(need) + " bytes of workspace, more than the " +
+            std::to_string((long long)HF_SCRATCH_BYTES) +
+            " bytes of the library's scratch memory: launch it with hf_fusion_launch and a workspace");
+    return HF_ERR_UNSUPPORTED;
+  }
+  void *ws = nullptr;
+  if (need > 0 && !(ws = scratch_address(f->device))) {
+    set_err("no scratch memory was set up on the fusion's device (the handle was not loaded on a device)");
+    return HF_ERR_INVALID;
+  }
+  return launch(f, params, n_params, result, ws, false, stream);
+}
+
+}  // namespace hf
 
 extern "C" {
 

@@ -313,6 +313,21 @@ hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *le
 hf_status hf_fusion_launch(hf_fusion *f, const void *const *params, int32_t n_params,
                            void *result, void *workspace, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * launch as hf_fusion_launch, with the library's own scratch memory in place
+ * of the caller's workspace.  It allocates nothing.  The scratch memory is a
+ * device array of HF_SCRATCH_BYTES per GPU, set up by hf_fusion_create and
+ * held until the process ends.  A fusion whose workspace_bytes exceeds
+ * HF_SCRATCH_BYTES is rejected with HF_ERR_UNSUPPORTED.  Every call on one GPU
+ * shares that GPU's scratch memory: calls whose launches overlap in time on
+ * one GPU (other streams, other threads) race on it and give wrong results;
+ * run them on one stream or use hf_fusion_launch with separate workspaces.
+ * Other arguments and errors as for hf_fusion_launch. */
+#define HF_SCRATCH_BYTES (16u << 20)
+hf_status hf_fusion_launch_noalloc(hf_fusion *f, const void *const *params, int32_t n_params,
+                                   void *result, void *stream);
+
 /* Release the handle (NULL is allowed).  It first waits for all work on the
  * fusion's device (hipDeviceSynchronize), so launches still in flight finish
  * before their code object is unloaded.  A HIP graph that captured a launch
