@@ -681,8 +681,9 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
                   f, ix.str(), call_args(it), "", "", "float (&hf_res)[HF_V]");
       }
       if (R.reducer == HF_REDUCER_ARGMAX) {
-        // max/argmax: the folds start from (init_value, index init); the
-        // result is the index
+        // max/argmax: the folds start from (init_value, HF_ARG_NONE); the
+        // result is the index, or the index init where no element replaced
+        // the initial pair
         glue << "#define HF_ARG_V0 " << flit(round_to_dtype(R.init, g.nodes[P.rin].t.dt)) << "\n#define HF_ARG_K0 ("
              << (long long)R.cst << ")\n";
         glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store_arg" : "hf_cr_store_arg")
@@ -693,7 +694,7 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
         for (int d : kept) kset[d] = 1;
         for (int d : kept_inc)
           if (!kset[d]) glue << "  const int i" << d << " = 0;\n";
-        glue << "  A.out[" << outoff << "] = k;\n}\n";
+        glue << "  A.out[" << outoff << "] = k == HF_ARG_NONE ? HF_ARG_K0 : k;\n}\n";
         break;
       }
       glue << "__device__ __forceinline__ void " << (is_row ? "hf_rr_store" : "hf_cr_store") << "(const HfArgs &A, int "

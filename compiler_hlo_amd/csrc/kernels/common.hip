@@ -120,7 +120,14 @@ __device__ __forceinline__ float hf_group_reduce(float v) {
 // value replaces the running maximum when value >= max (so NaN never does,
 // and later equal values win).  Partial results then combine by larger
 // value, then larger index -- a commutative, associative choice that gives
-// the sequential fold's answer.
+// the sequential fold's answer.  Every partial starts from (value init,
+// HF_ARG_NONE): HF_ARG_NONE means "no element has replaced the init yet" and
+// loses every index tie, so the final pair holds the last index of the
+// maximum whenever an element reached it.  The index init of the fold is
+// written only where HF_ARG_NONE survives to the end (the store), which is
+// exactly where the sequential fold never replaced its initial pair -- for
+// any index init, also one inside the row.
+#define HF_ARG_NONE (-2147483647 - 1)
 __device__ __forceinline__ void hf_arg_step(float &m, int &k, float v, int j) {
   if (v >= m) {
     m = v;

@@ -18,7 +18,8 @@
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_C, HF_R, HF_CL,
 // HF_RL, HF_CB, HF_NCB, HF_S, HF_RS, hf_regs_t, hf_cr_eval_fetch(A, r, c, R),
 // hf_cr_eval(A, r, c, R, x), hf_cr_store(A, c, acc); for max/argmax (HF_OP 3)
-// HF_ARG_V0, HF_ARG_K0 and hf_cr_store_arg(A, c, index).
+// HF_ARG_V0 and hf_cr_store_arg(A, c, index) (which writes the index init
+// where the index is still HF_ARG_NONE).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
 #if HF_OP == 3
@@ -36,7 +37,7 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
 #pragma unroll
     for (int v = 0; v < HF_V; ++v) {
       m[v] = HF_ARG_V0;
-      k[v] = HF_ARG_K0;
+      k[v] = HF_ARG_NONE;
     }
     const int r_begin = seg * HF_RS;
     const int r_end = r_begin + HF_RS < HF_R ? r_begin + HF_RS : HF_R;
@@ -136,7 +137,7 @@ extern "C" __global__ __launch_bounds__(256) void HF_FOLD_NAME(HF_KERNEL_PARAMS)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = blockIdx.x * 64 + lane;
     float m = HF_ARG_V0;
-    int k = HF_ARG_K0;
+    int k = HF_ARG_NONE;
     if (col < HF_C)
       for (int q = wave; q < HF_S; q += 4)
         hf_arg_combine(m, k, ((const float *)A.ws)[(long)q * HF_C + col],

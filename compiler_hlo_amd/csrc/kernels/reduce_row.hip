@@ -15,7 +15,8 @@
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
 // (vectors per row), HF_TPR, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
 // hf_rr_eval(A, row, kv, R, x) (HF_V floats), hf_rr_store(A, row, acc); for max/argmax
-// (HF_OP 3) HF_ARG_V0, HF_ARG_K0 and hf_rr_store_arg(A, row, index).
+// (HF_OP 3) HF_ARG_V0 and hf_rr_store_arg(A, row, index) (which writes the
+// index init where the index is still HF_ARG_NONE).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
 #if HF_OP == 3
@@ -29,7 +30,7 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
   for (int row0 = blockIdx.x * RPB; row0 < HF_ROWS; row0 += gridDim.x * RPB) {
     const int row = row0 + rloc;
     float m = HF_ARG_V0;
-    int k = HF_ARG_K0;
+    int k = HF_ARG_NONE;
     if (row < HF_ROWS) {
       // the row's chunks in batches of up to 8 per thread, loads first
       constexpr int IT = (HF_KV + HF_TPR - 1) / HF_TPR;

@@ -168,7 +168,9 @@ typedef enum {
  * (value, index) : (max, argmax), started from (init_value, constant).  The
  * library folds in parallel and combines partial results by larger value,
  * then larger index: ties go to the last index, as in the sequential fold, and
- * NaN values are never selected. */
+ * NaN values are never selected.  The index init (`constant`, any s32 value)
+ * is the result exactly where no element is >= init_value, as in the
+ * sequential fold. */
 typedef enum {
   HF_REDUCER_ADD = 0,
   HF_REDUCER_MAX = 1,

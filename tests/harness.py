@@ -101,3 +101,23 @@ def assert_ulp(got, want, dtype: str, max_ulp: int):
     assert worst <= max_ulp, "max distance %d ulp > %d (%d elements over)" % (
         worst, max_ulp, int((d > max_ulp).sum()))
     return d
+
+
+def oracle_points_threaded(nodes, params, points, workers: int | None = None):
+    """oracle.evaluate_points over row chunks in a thread pool.  The oracle
+    is single-threaded C called through ctypes, which releases the GIL, and it
+    keeps no shared state while evaluating, so the chunks run in parallel on
+    the host's cores (at most 16, the host share of one GPU)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    pts = np.ascontiguousarray(np.asarray(points, dtype=np.int64))
+    oracle.lib()  # load once, before the threads
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    chunks = np.array_split(np.arange(pts.shape[0]), workers * 4)
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(lambda ix: oracle.evaluate_points(nodes, params, pts[ix]), [c for c in chunks if c.size]))
+    vals = np.concatenate([v for v, _ in parts])
+    aux = np.concatenate([a for _, a in parts])
+    return vals, aux
+

@@ -278,25 +278,25 @@ def test_transpose_bf16_small(b, m, n):
 
 
 def test_transpose_bf16_full():
+    """C2b at full size: all 33,554,432 outputs against the oracle's whole
+    evaluation, bit-exact."""
     spec, params, _ = W.transpose_bf16_021()
     say("transpose bf16 full")
     got, f = run_gpu(spec.nodes, params, reps=2)
     assert f.plan()["hero"] == "transpose"
-    want = np.transpose(params[0].reshape(64, 512, 1024), (0, 2, 1)).ravel()
-    assert_bitexact(got, want, "bf16")
-    pts = np.stack([np.random.default_rng(1).integers(0, d, 4000) for d in (64, 1024, 512)], axis=1)
-    vals, _ = oracle.evaluate_points(spec.nodes, params, pts)
-    lin = (pts[:, 0] * 1024 + pts[:, 1]) * 512 + pts[:, 2]
-    gv = oracle.bf16_bits_to_f32(got[lin]).astype(np.float64)
-    assert np.array_equal(gv, vals)
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "bf16")
 
 
 # --------------------------------------------------------------------------
 # row reduce: sum over the minor dim of convert(add(exp x, broadcast b)) in bf16
 # --------------------------------------------------------------------------
-def _check_sum(got, spec, params, rows_idx):
+def _check_sum(got, spec, params, rows_idx, threaded=False):
     pts = np.asarray(rows_idx, dtype=np.int64)
-    vals, aux = oracle.evaluate_points(spec.nodes, params, pts)
+    if threaded:
+        from harness import oracle_points_threaded
+        vals, aux = oracle_points_threaded(spec.nodes, params, pts)
+    else:
+        vals, aux = oracle.evaluate_points(spec.nodes, params, pts)
     rn = spec.nodes[-1]
     lin = np.array([oracle.linear_index(rn["dims"], rn["m2m"] or oracle.default_m2m(len(rn["dims"])), p)
                     for p in pts])
@@ -314,14 +314,18 @@ def test_row_reduce_small(d0, d2, d3):
     _check_sum(got, spec, params, [[a, 0, c] for a in range(d0) for c in range(d2)])
 
 
-def test_row_reduce_full_sampled_and_layout_invariant():
+def test_row_reduce_full_every_row_and_layout_invariant():
+    """C3 at full size: every one of the 10,240 sums within 1e-5 * sum|y| of
+    the oracle's long-double sum (the oracle runs on the host's cores in
+    parallel, a chunk of rows per thread)."""
+    import time
     spec, params, _ = W.row_reduce_exp_add_bf16()
     say("row reduce full")
     got, f = run_gpu(spec.nodes, params, reps=2)
-    rng = np.random.default_rng(4)
-    rows = [[int(a), 0, int(c)] for a, c in zip(rng.integers(0, 8, 40), rng.integers(0, 1280, 40))]
-    rows += [[0, 0, 0], [7, 0, 1279]]
-    _check_sum(got, spec, params, rows)
+    rows = [[a, 0, c] for a in range(8) for c in range(1280)]
+    t0 = time.time()
+    _check_sum(got, spec, params, rows, threaded=True)
+    say("  all %d rows checked against the oracle in %.1f s" % (len(rows), time.time() - t0))
     # {3,2,0,1} stores the same bytes (dim 1 has size 1): bitwise equal results
     spec2, params2, _ = W.row_reduce_exp_add_bf16(m2m=(3, 2, 0, 1))
     got2, _ = run_gpu(spec2.nodes, params2)
@@ -624,6 +628,38 @@ def test_argmax_nan_and_init_ties():
         s.argmax(p, rdim, list(arr.shape))
         got, _ = run_gpu(s.nodes, [arr.ravel()])
         assert_bitexact(got, oracle.evaluate(s.nodes, [arr.ravel()]), "s32")
+
+
+@pytest.mark.parametrize("index_init", [0, "n+5", -1])
+@pytest.mark.parametrize("n", [5, 3, 1000, 6000])
+def test_argmax_index_init_inside_and_past_the_row(n, index_init):
+    """Any s32 index init (Operation semantics, "Variadic Reduce": the fold
+    starts from (init_value, index init)): all-NaN rows, rows of -inf, rows
+    whose maximum equals the value init (2) at several positions, rows that
+    never reach it, and ordinary rows, through the row hero (short rows in
+    sub-wave mode, rows of 1000) and the column hero (6000 rows: split into
+    segments, so the workspace and the fold kernel carry the partials).
+    Bit-exact against the oracle."""
+    nan, ninf = np.float32("nan"), np.float32("-inf")
+    k0 = n + 5 if index_init == "n+5" else index_init
+    g = W.rng(120 + n)
+    rows = [np.full(n, nan), np.full(n, ninf), np.zeros(n), g.integers(-3, 3, n, endpoint=True)]
+    r = g.integers(-3, 2, n, endpoint=True).astype(np.float32)   # max 2 = the value init, ties
+    rows.append(r)
+    r = np.where(g.random(n) < 0.5, nan, 2.0)                    # init-valued among NaNs
+    rows.append(r)
+    x = np.stack([np.asarray(v, np.float32) for v in rows] * 11)  # 66 rows
+    for value_init in (2.0, float("-inf")):
+        for rdim, arr in ((1, x), (0, np.ascontiguousarray(x.T))):
+            s = W.Spec()
+            p = s.parameter(0, "f32", list(arr.shape))
+            s.argmax(p, rdim, list(arr.shape), index_init=k0, init=value_init)
+            got, f = run_gpu(s.nodes, [arr.ravel()])
+            want = oracle.evaluate(s.nodes, [arr.ravel()])
+            assert_bitexact(got, want, "s32")
+            if rdim == 0 and n == 6000:
+                assert f.plan()["hero"] == "column_reduce" and f.plan()["workspace_bytes"] > 0
+    say("argmax index init", k0, "rows of", n, "ok")
 
 
 # --------------------------------------------------------------------------
@@ -1150,7 +1186,10 @@ def test_exp_bf16_exhaustive():
     s.unary("exponential", p, "bf16", [65536])
     got, _ = run_gpu(s.nodes, [allbits])
     d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), "bf16", 1)
-    say("bf16 exp: %d of 65536 inputs 1 ulp off" % int((d > 0).sum()))
+    off = int((d > 0).sum())
+    say("bf16 exp: %d of 65536 inputs 1 ulp off" % off)
+    # measured: 2 inputs; more would move C3's sums and the bf16 exp fusions
+    assert off <= 2, off
 
 
 def test_tanh_bf16_exhaustive():
@@ -1159,8 +1198,8 @@ def test_tanh_bf16_exhaustive():
     p = s.parameter(0, "bf16", [65536])
     s.unary("tanh", p, "bf16", [65536])
     got, _ = run_gpu(s.nodes, [allbits])
-    d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), "bf16", 1)
-    say("bf16 tanh: %d of 65536 inputs 1 ulp off" % int((d > 0).sum()))
+    # correctly rounded on every input: the bit-exact GELU rests on it
+    assert_bitexact(got, oracle.evaluate(s.nodes, [allbits]), "bf16")
 
 
 def test_exp_log_f32_sample():

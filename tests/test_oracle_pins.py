@@ -940,6 +940,21 @@ def test_argmax_skips_nan_and_takes_values_equal_to_init():
     assert got == [4, -1, 2, 4]
 
 
+def test_argmax_with_an_index_init_inside_the_row():
+    """Operation semantics, "Variadic Reduce": the fold starts from
+    (init_value, index init) and an element replaces the running pair when
+    value >= max.  With value init 2 and index init 7 (worked by hand): a
+    row whose maximum equals the value init returns the last index holding
+    it; a row that never reaches the init, or holds only NaN, returns 7."""
+    nan = float("nan")
+    rows = np.array([[1, 2, 0, 2, 1], [1, 0, 1, 0, 1], [nan] * 5, [3, 2, 3, 1, 2], [2, nan, 2, nan, nan]],
+                    np.float32)
+    got = ev(_argmax_spec(rows.shape, 1, init=2.0, index_init=7), [rows]).astype(np.int64).tolist()
+    assert got == [3, 7, 7, 2, 2]
+    got = ev(_argmax_spec(rows.shape, 1, init=2.0, index_init=0), [rows]).astype(np.int64).tolist()
+    assert got == [3, 0, 0, 2, 2]
+
+
 # --------------------------------------------------------------------------
 # Elementwise ops on quantized tensors (StableHLO Specification, each op's
 # semantics for quantized types: dequantize, op, quantize)
