@@ -935,7 +935,7 @@ def test_column_reduce_small(r, c):
 def test_column_reduce_full_both_layouts():
     spec, params, _ = W.column_reduce_max_f32()
     say("column reduce full")
-    got, f = run_gpu(spec.nodes, params, reps=3)  # repeated launches reuse the counters
+    got, f = run_gpu(spec.nodes, params, reps=3)  # repeated launches, each with its own workspace
     assert f.plan()["hero"] == "column_reduce"
     want = params[0].reshape(16384, 4096).max(axis=0)
     assert_bitexact(got, want, "f32")
@@ -945,6 +945,7 @@ def test_column_reduce_full_both_layouts():
     got_c, fc = run_gpu(spec_c.nodes, [colmajor])
     assert fc.plan()["hero"] == "row_reduce"
     assert np.array_equal(got.view(np.uint32), got_c.view(np.uint32))
+    assert_bitexact(got_c, oracle.evaluate(spec_c.nodes, [colmajor]), "f32")
 
 
 @pytest.mark.parametrize("dims,red,m2m", [([3, 50, 40], [1], None), ([2, 3, 1000, 64], [2], None),
