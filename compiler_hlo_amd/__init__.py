@@ -181,6 +181,24 @@ def linear_index(dims, m2m, index) -> int:
                                 (ctypes.c_int64 * MAX_RANK)(*index))
 
 
+class PreparedLaunch:
+    """hf_fusion_launch with its argument array built once (see
+    Fusion.prepare); it keeps the fusion alive."""
+
+    def __init__(self, fusion, param_ptrs, out_ptr: int, workspace: int = 0):
+        self._fusion = fusion
+        self._n = len(param_ptrs)
+        self._arr = (ctypes.c_void_p * max(1, self._n))(*param_ptrs)
+        self._out = ctypes.c_void_p(out_ptr)
+        self._ws = ctypes.c_void_p(workspace)
+        self._launch = _lib.hf_fusion_launch
+
+    def __call__(self, stream: int = 0):
+        rc = self._launch(self._fusion._h, self._arr, self._n, self._out, self._ws, stream)
+        if rc:
+            _check(rc)
+
+
 class Fusion:
     """One compiled fusion.  ``mode`` is "load" (default: compile and load on
     the current GPU), "compile" (generate and compile only; no GPU) or "plan"
@@ -278,6 +296,12 @@ class Fusion:
         arr = (ctypes.c_void_p * max(1, len(param_ptrs)))(*param_ptrs)
         _check(_lib.hf_fusion_launch(self._h, arr, len(param_ptrs), ctypes.c_void_p(out_ptr),
                                      ctypes.c_void_p(workspace), ctypes.c_void_p(stream)))
+
+    def prepare(self, param_ptrs, out_ptr: int, workspace: int = 0):
+        """A launch with fixed buffers, marshalled once: calling the returned
+        object with a raw hipStream_t launches it (hf_fusion_launch) without
+        rebuilding the ctypes argument array each time."""
+        return PreparedLaunch(self, param_ptrs, out_ptr, workspace)
 
     def launch_noalloc_ptrs(self, param_ptrs, out_ptr: int, stream: int = 0):
         """hf_fusion_launch_noalloc: launch with raw device pointers, the
