@@ -165,16 +165,33 @@ def read_pmc_csv(run_dir, counter):
     return {k: sum(v) / len(v) for k, v in per.items()}
 
 
-def write_traffic(pmc_root, names):
-    """Turn rocprofv3 --pmc runs into profiles/traffic.json.
+def read_kernel_stats(path):
+    """{kernel name: average ns} from a rocprofv3 --kernel-trace --stats
+    *_kernel_stats.csv."""
+    import csv
+    return {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(path))}
+
+
+def kernel_name_of(source: str) -> str:
+    for line in source.splitlines():
+        if line.startswith("#define HF_KERNEL_NAME "):
+            return line.split()[2]
+    raise ValueError("no kernel name in the generated source")
+
+
+def write_traffic(pmc_root, names, stats_csv=None):
+    """Turn rocprofv3 runs into profiles/traffic.json.
 
     Expects <pmc_root>/<workload>/<COUNTER>/ for COUNTER in FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), including the f32 copy.  Each counter is
     scaled by the ratio that makes the copy's reading equal its known bytes
     (read 4n, write 4n); a launch's traffic sums its kernels (a column reduce
-    with segments has a fold kernel too)."""
+    with segments has a fold kernel too).  With stats_csv (the
+    *_kernel_stats.csv of a --kernel-trace --stats run of this bench), each
+    record also gets the kernel-trace average of its kernels per launch."""
     import compiler_hlo_amd as H
     makers = workload_makers()
+    stats = read_kernel_stats(stats_csv) if stats_csv else {}
     cal = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         got = read_pmc_csv(os.path.join(pmc_root, "copy_f32_4096x4096", ctr), ctr)
@@ -198,6 +215,11 @@ def write_traffic(pmc_root, names):
             total += b
         rec["bytes_per_launch"] = round(total)
         rec["traffic_over_algorithmic"] = round(total / rec["algorithmic_bytes"], 4)
+        kname = kernel_name_of(f.source())
+        mine = [v for k, v in stats.items() if k == kname or k == kname + "_fold"]
+        if mine:
+            rec["kernel"] = kname
+            rec["trace_avg_us"] = round(sum(mine) / 1e3, 3)
         out[name] = rec
         log("%-32s fetch %.1f MB write %.1f MB  x%.3f of algorithmic" % (
             name, rec["fetch_bytes"] / 1e6, rec["write_bytes"] / 1e6, rec["traffic_over_algorithmic"]))
@@ -253,38 +275,79 @@ def time_cases(cases, steps, warmup):
     return wall, per
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(makers, min_seconds=10.0):
     """The oracle, as it stands, single-threaded, on the full workload of one
     step, repeated until at least `min_seconds` of CPU work (a few steps).
-    Only evaluation is timed."""
+    Only evaluation is timed.  The calling thread is pinned to one core (the
+    first this process may use) for the measurement and unpinned after."""
     import oracle
     cases = [make() for make in makers]
-    total_bytes, total_t, reps = 0, 0.0, 0
-    while total_t < min_seconds or reps == 0:
-        for spec, params, meta in cases:
-            t0 = time.perf_counter()
-            oracle.evaluate(spec.nodes, params)
-            total_t += time.perf_counter() - t0
-            total_bytes += meta["bytes"]
-        reps += 1
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        total_bytes, total_t, reps = 0, 0.0, 0
+        while total_t < min_seconds or reps == 0:
+            for spec, params, meta in cases:
+                t0 = time.perf_counter()
+                oracle.evaluate(spec.nodes, params)
+                total_t += time.perf_counter() - t0
+                total_bytes += meta["bytes"]
+            reps += 1
+    finally:
+        os.sched_setaffinity(0, allowed)
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cores": os.cpu_count(),
+            "pinned_core": core,
             "sample": "%d full steps (exp-transpose f32[4096,4096] + transpose bf16[64,512,1024]); "
-                      "%.1f s single-threaded on the host" % (reps, total_t)}
+                      "%.1f s on 1 thread pinned to core %d of %d" % (reps, total_t, core, os.cpu_count())}
 
 
-def load_traffic(name, source_hash):
-    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE,
-    WRITE_SIZE), kept in profiles/traffic.json with the hash of the kernel
-    source it was taken on; None once the kernel has changed."""
+def load_profile(name, source_hash):
+    """The rocprofv3 record of a workload in profiles/traffic.json (HBM
+    traffic per launch from FETCH_SIZE and WRITE_SIZE, the kernel-trace
+    average), kept with the hash of the kernel source it was taken on; {}
+    once the kernel has changed."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         t = json.load(open(path))[name]
     except Exception:
-        return None
-    if t.get("source_fnv1a") != source_hash:
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    return t if t.get("source_fnv1a") == source_hash else {}
+
+
+def load_traffic(name, source_hash):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated), or None."""
+    return load_profile(name, source_hash).get("bytes_per_launch")
+
+
+# The configurations the 70% gate applies to, by workload.
+GATED = {"C2a": "transpose_exp_f32", "C2b": "transpose_bf16_021", "C3": "row_reduce_exp_add_bf16",
+         "C4r": "column_reduce_max_f32", "C5": "quant_dequant_bias_requant"}
+
+
+def roofline_entry(case_name, hero, nbytes, seconds, source_hash):
+    """The HBM roofline of one workload's launch: algorithmic bytes over the
+    events time per launch, against 8 TB/s, with the rocprofv3 kernel time and
+    traffic of the same kernel source when profiles/traffic.json has them."""
+    prof = load_profile(case_name, source_hash)
+    achieved = nbytes / seconds / 1e9
+    traffic = prof.get("bytes_per_launch")
+    return {"workload": case_name, "hero": hero, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes, "avg_launch_us": round(seconds * 1e6, 3),
+            "trace_avg_us": prof.get("trace_avg_us"), "traffic": traffic,
+            "traffic_ratio": round(traffic / nbytes, 4) if traffic else None}
 
 
 def fnv1a(s: str) -> str:
@@ -305,13 +368,15 @@ def main():
     ap.add_argument("--only", default=None, help="time one named workload alone (profiling)")
     ap.add_argument("--traffic", default=None, metavar="PMC_DIR",
                     help="write profiles/traffic.json from rocprofv3 --pmc runs under PMC_DIR (no GPU)")
+    ap.add_argument("--stats", default=None, metavar="CSV",
+                    help="with --traffic: the *_kernel_stats.csv of a --kernel-trace --stats run of this bench")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the fusion is a single-device hot path); "
               "--gpus %d is not supported" % a.gpus, file=sys.stderr)
         sys.exit(2)
     if a.traffic:
-        write_traffic(a.traffic, [n for n in workload_makers() if not n.startswith(("copy_", "iota_"))])
+        write_traffic(a.traffic, [n for n in workload_makers() if not n.startswith(("copy_", "iota_"))], a.stats)
         return
 
     import torch
@@ -341,7 +406,13 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": name, "algorithmic_bytes": dc.bytes,
-            "avg_launch_us": round(per[dom] * 1e6, 3)}
+            "avg_launch_us": round(per[dom] * 1e6, 3),
+            "trace_avg_us": load_profile(name, fnv1a(dc.fusion.source())).get("trace_avg_us")}
+    rooflines = {}
+    for i, c in enumerate(cases):
+        for cfg, wl in GATED.items():
+            if wl == c.meta["name"]:
+                rooflines[cfg] = roofline_entry(wl, c.plan["hero"], c.bytes, per[i], fnv1a(c.fusion.source()))
     log("step: %.2f us wall; %s %.2f us (%.1f GB/s), %s %.2f us (%.1f GB/s)" % (
         wall * 1e6, c2a.meta["name"], per[0] * 1e6, c2a.bytes / per[0] / 1e9,
         c2b.meta["name"], per[1] * 1e6, c2b.bytes / per[1] / 1e9))
@@ -367,6 +438,9 @@ def main():
             mk, kw, tr = makers[key]
             c = Case(mk, kwargs=kw, transform=tr)
             _, p = time_cases([c], 100, 10)
+            for cfg, wl in GATED.items():
+                if wl == key:
+                    rooflines[cfg] = roofline_entry(wl, c.plan["hero"], c.bytes, p[0], fnv1a(c.fusion.source()))
             heroes[key] = {"hero": c.plan["hero"], "us": round(p[0] * 1e6, 3),
                            "GBps": round(c.bytes / p[0] / 1e9, 1),
                            "frac": round(c.bytes / p[0] / 1e9 / PEAK_HBM_GBS, 4),
@@ -390,6 +464,7 @@ def main():
                                "transpose(x,{0,2,1}) bf16[64,512,1024], row-major in and out",
                    "step_bytes": step_bytes, "buffer_sets": sets_used},
         "roofline": roof,
+        "rooflines": {k: rooflines[k] for k in GATED if k in rooflines},
         "cpu_baseline": cpu,
         "heroes": heroes,
     }

@@ -329,11 +329,15 @@ class Gen {
       v = fresh(b, n);
       lanes(b, v, "float", "hf_rv");
     } else if (n == c.leaf) {
-      // staged value from the LDS tile: [w][u] with u along the lane
+      // staged value from the LDS tile: [w][u] with u along the lane; u is
+      // the tile's flattened U index over the merged dims (minor first)
       v = fresh(b, n);
-      const Term &tw = E[P_.lane_in], &tu = E[P_.lane_out];
+      const Term &tw = E[P_.lane_in];
+      std::string tu = term_str(E[P_.u_dims.back()]);
+      for (int k = (int)P_.u_dims.size() - 2; k >= 0; --k)
+        tu = "(" + tu + ") * " + std::to_string(t.dims[P_.u_dims[k]]) + " + " + term_str(E[P_.u_dims[k]]);
       b.os << "  " << rtype(t) << " " << v << "[" << b.V << "];\n";
-      b.os << "  { const int o = (" << term_str(tw) << " - hf_w0) * HF_PITCH + (" << term_str(tu) << " - hf_u0);\n";
+      b.os << "  { const int o = (" << term_str(tw) << " - hf_w0) * HF_PITCH + (" << tu << " - hf_u0);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << b.V << "; ++l) " << v << "[l] = hf_tile[o + l]; }\n";
     } else if (nd.op == HF_PARAMETER) {
       v = load(b, n, rtype(t), t.dt, t, "A.p" + std::to_string(nd.param), E, is_streaming(g_, n));
@@ -583,19 +587,23 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
       std::string fl = gen.fn(0, ld.root, ld.lane);
       std::string fs = P.staged == g.root ? "" : gen.fn(1, st.root, st.lane);
       std::vector<int> batch;
-      std::vector<char> set(rt.rank, 0);
+      std::vector<char> set(rt.rank, 0), in_u(rt.rank, 0);
+      for (int d : P.u_dims) in_u[d] = 1;
       for (int k = 0; k < rt.rank; ++k) {
         int d = rt.m2m[k];
-        if (rt.dims[d] > 1 && d != P.lane_in && d != P.lane_out) {
+        if (rt.dims[d] > 1 && d != P.lane_in && !in_u[d]) {
           batch.push_back(d);
           set[d] = 1;
         }
       }
-      set[P.lane_in] = set[P.lane_out] = 1;
+      set[P.lane_in] = 1;
+      for (int d : P.u_dims) set[d] = 1;
       std::ostringstream ix;
       if (!batch.empty()) delinearize(ix, rt, batch, "b", "hf_t");
       else ix << "  (void)b;\n";
-      ix << "  const int i" << P.lane_in << " = w;\n  const int i" << P.lane_out << " = u;\n";
+      ix << "  const int i" << P.lane_in << " = w;\n";
+      if (P.u_dims.size() == 1) ix << "  const int i" << P.lane_out << " = u;\n";
+      else delinearize(ix, rt, P.u_dims, "u", "hf_u");  // the tile's U index over the merged dims
       zero_dims(ix, rt, set);
       types << "typedef hf_R_" << fl << " hf_ldregs_t;\n";
       glue_pair(glue, "hf_tr_load", "int b, int w, int u", "hf_ldregs_t", fl, ix.str(), call_args(rt), "", "",

@@ -20,12 +20,22 @@
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
   __shared__ hf_tile_t tile[HF_TW * HF_PITCH];
+#if HF_ORDER == 3
+  // XCD-contiguous: workgroup i runs on XCD i % 8, so XCD x takes the x-th
+  // contiguous range of tiles in (batch, U-tile, W-tile) order, W fastest.
+  // Tiles that share input lines (the W-neighbours of one U range, when the
+  // input rows are not whole 128-byte lines) then read them through one L2.
+  constexpr int NX = 8;
+  const int n = (int)gridDim.x, x = (int)blockIdx.x % NX, q = n / NX, r = n % NX;
+  const int bid = x * q + (x < r ? x : r) + (int)blockIdx.x / NX;
+#else
   const int bid = blockIdx.x;
+#endif
   const int b = bid / (HF_NTU * HF_NTW);
   const int t = bid % (HF_NTU * HF_NTW);
 #if HF_ORDER == 0  // U-tiles fastest
   const int tu = t % HF_NTU, tw = t / HF_NTU;
-#elif HF_ORDER == 1  // W-tiles fastest
+#elif HF_ORDER == 1 || HF_ORDER == 3  // W-tiles fastest
   const int tw = t % HF_NTW, tu = t / HF_NTW;
 #else  // diagonal: W-tiles fastest, U-tile shifted by the W-tile
   const int tw = t % HF_NTW, tu = (t / HF_NTW + tw) % HF_NTU;

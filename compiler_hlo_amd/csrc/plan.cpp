@@ -573,8 +573,27 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     P.staged = s;
     P.lane_in = lin;
     P.lane_out = lout;
-    long long DU = rt.dims[lout], DW = rt.dims[lin];
-    int vout = align_lanes(st, vec_width(DU, std::max(1, 16 / dtype_bytes(rt.dt))));
+    // The tile's U dim is the output's physically minor dim together with
+    // the output dims that lie physically between it and W: for fixed W and
+    // batch those are one contiguous run of the output, so a tile over their
+    // flattened index writes whole lines (abs(transpose(exp x, {2,1,0})) on
+    // f32[20,160,170]: the output's rows of 20 floats then are stored 3200 at
+    // a time instead of 80 bytes per workgroup).  Vectors run along the minor
+    // dim alone, so they never cross into the next index of a merged dim.
+    std::vector<int> udims{lout};
+    {
+      int kin = 0, kout = 0;
+      for (int k = 0; k < rt.rank; ++k) {
+        if (rt.m2m[k] == lin) kin = k;
+        if (rt.m2m[k] == lout) kout = k;
+      }
+      for (int k = kout + 1; k < kin; ++k)
+        if (rt.dims[rt.m2m[k]] > 1) udims.push_back(rt.m2m[k]);
+    }
+    P.u_dims = udims;
+    long long DU = 1, DW = rt.dims[lin];
+    for (int d : udims) DU *= rt.dims[d];
+    int vout = align_lanes(st, vec_width(rt.dims[lout], std::max(1, 16 / dtype_bytes(rt.dt))));
     int vin = align_lanes(ld, vec_width(DW, std::max(1, 16 / stream_elem_bytes(g, ld, dtype_bytes(g.nodes[s].t.dt)))));
     ld.V = vin;
     st.V = vout;
@@ -591,16 +610,29 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     const bool narrow = pow2_rows && vin == 4 && vout == 4;
     int tu = (int)std::min<long long>(env_ll("HF_TR_TU", narrow ? 32 : 64), pow2_ceil(DU));
     int tw = (int)std::min<long long>(env_ll("HF_TR_TW", narrow ? 128 : 64), pow2_ceil(DW));
+    long long nb = rt.numel() / (DU * DW);
+    // A tiling that would leave fewer than two workgroups per CU (256 CUs)
+    // takes the pages' 32x32 tile instead: abs(transpose(exp x, {2,1,0})) on
+    // f32[20,160,170] ran 4.70 us with 64x64 tiles (150 workgroups) and
+    // 3.67 us with 32x32 (600).
+    // (The narrow tiles above keep their shape: they are for row strides of
+    // a power of two.)
+    if (!narrow && !std::getenv("HF_TR_TU") && !std::getenv("HF_TR_TW") &&
+        nb * ceil_div(DU, tu) * ceil_div(DW, tw) < 512) {
+      tu = std::min(tu, 32);
+      tw = std::min(tw, 32);
+    }
     tu = std::max(tu, vout);
     tw = std::max(tw, vin);
     long long ntu = ceil_div(DU, tu), ntw = ceil_div(DW, tw);
-    long long nb = rt.numel() / (DU * DW);
     int pitch = tu + 1;
     // Tile order.  U-tiles fastest keeps the writes of concurrent workgroups
     // spread over the output.  When the input rows of a tile lie 8 KiB or
     // more apart, the reads of U-consecutive tiles share their low address
     // bits (and so their HBM channels); a diagonal order then spreads both.
-    const long long order = env_ll("HF_TR_ORDER", in_row_bytes >= 8192 ? 2 : 0);
+    // Input rows that are not whole 128-byte lines share their edge lines
+    // between W-neighbouring tiles: those go to one XCD (order 3).
+    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0 ? 3 : in_row_bytes >= 8192 ? 2 : 0);
     // Threads per tile: one 128-bit vector per thread and phase for the
     // narrow tiles above; otherwise 512 (one or two vectors each) when both
     // phases of a full tile divide evenly among them, else 256.

@@ -66,6 +66,7 @@ struct Plan {
   std::vector<Ctx> ctx;       // loop/reduce: 1; transpose: [0] load, [1] store
   int staged = -1;            // transpose: staged node
   int lane_in = -1, lane_out = -1;
+  std::vector<int> u_dims;    // transpose: dims of the tile's U index, minor -> major (lane_out first)
   // reduce
   int rin = -1;               // reduce operand node
   std::vector<int> order;     // input dims with extent > 1, physical minor -> major

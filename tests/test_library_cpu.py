@@ -589,20 +589,21 @@ def test_algorithmic_bytes_of_the_workloads():
 
 def test_transpose_tile_arithmetic_of_the_pages_example():
     """The pages' transpose example (20x160x170 -> 170x160x20 with 32-wide tiles
-    over the two swapped dims) has 960 blocks; the same tile count follows
-    from our tiling rule with 32x32 tiles."""
+    over the two swapped dims, one batch index per block) has 960 blocks.  Our
+    tiling merges the output's middle dim (160, physically between the
+    output's minor dim and the transposed one) into the tile's U index, which
+    runs over 160 x 20 = 3200 contiguous outputs: with the same 32x32 tiles
+    (chosen by itself for a grid this small) that is 100 x 6 = 600 blocks,
+    with no padding of the 20-long rows up to 32."""
     ntiles = -(-20 // 32) * 160 * -(-170 // 32)
     assert ntiles == 960
     s = W.Spec()
     x = s.parameter(0, "f32", [20, 160, 170])
     e = s.unary("exponential", x, "f32", [20, 160, 170])
     s.transpose(e, [2, 1, 0], "f32", [170, 160, 20])
-    os.environ["HF_TR_TU"], os.environ["HF_TR_TW"] = "32", "32"
-    try:
-        p = plan_of(s)
-    finally:
-        del os.environ["HF_TR_TU"], os.environ["HF_TR_TW"]
-    assert p["hero"] == "transpose" and p["grid_blocks"] == 960
+    p = plan_of(s)
+    assert p["hero"] == "transpose" and (p["tile_rows"], p["tile_cols"]) == (32, 32)
+    assert p["cols"] == 3200 and p["grid_blocks"] == -(-3200 // 32) * -(-170 // 32) == 600
 
 
 # --------------------------------------------------------------------------
