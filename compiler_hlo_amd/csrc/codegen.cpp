@@ -14,6 +14,12 @@
 // hero templates call the fetch functions of a whole step (several rows,
 // tile rows or row chunks) before any compute, so all of the step's loads
 // are in flight together; the compute function F only unpacks registers.
+//
+// The pipelined loop hero (HF_PIPE) splits the loads once more: those whose
+// index does not move with the row (per-axis quantization arrays, a bias
+// broadcast along the rows, scalars) go to a second struct hf_I_F, loaded
+// once per thread by F_inv before any row is fetched, so that the compute of
+// the first row waits for its own row only and not for rows fetched ahead.
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -74,12 +80,16 @@ struct Body {
   std::ostringstream os;     // compute
   std::ostringstream fetch;  // loads into R
   std::ostringstream members;
+  std::ostringstream inv_fetch;    // row-invariant loads into I (pipelined loop)
+  std::ostringstream inv_members;
+  std::ostringstream inv_pin;
   std::map<std::string, std::string> memo;
   int root = -1;
   int lane = -1;
   int V = 1;
   int tmp = 0;
   int nmem = 0;
+  int ninv = 0;
   bool tile = false;
   bool rleaf = false;     // the context's leaf is a reduced value passed in (hf_rv)
 };
@@ -91,8 +101,12 @@ class Gen {
     nt_loads_ = nt ? (std::atoi(nt) & 1) : true;
     // A hero that keeps the next step's loads in flight while it computes
     // needs every load of a step in its fetch phase, small arrays included.
-    for (auto &m : P.macros)
+    for (auto &m : P.macros) {
       if (m.first == "HF_RR_PIPE" && m.second) fetch_all_ = true;
+      // The pipelined loop fetches every row-dependent load of a row ahead
+      // of its compute and loads the row-invariant ones once (hf_I_F).
+      if (m.first == "HF_PIPE" && m.second) inv_split_ = true;
+    }
   }
 
   // Emits (once) the struct, fetch and compute functions of the partition
@@ -120,10 +134,23 @@ class Gen {
     f << "struct hf_R_" << name << " {\n" << b.members.str() << "  char hf_pad;\n};\n";
     f << "__device__ __forceinline__ void " << name << "_fetch(const HfArgs &A" << idx << ", hf_R_" << name
       << " &R) {\n" << b.fetch.str() << "  (void)A; (void)R;\n}\n";
+    std::string inv;
+    if (inv_split_) {
+      // row-invariant loads, and a pin that keeps them in registers: after
+      // it the compiler cannot re-issue them (as rematerialized loads) behind
+      // rows already in flight
+      f << "struct hf_I_" << name << " {\n" << b.inv_members.str() << "  char hf_pad;\n};\n";
+      f << "__device__ __forceinline__ void " << name << "_inv(const HfArgs &A" << idx << ", hf_I_" << name
+        << " &I) {\n" << b.inv_fetch.str() << "  (void)A; (void)I;\n}\n";
+      f << "__device__ __forceinline__ void " << name << "_pin(hf_I_" << name << " &I) {\n" << b.inv_pin.str()
+        << "  (void)I;\n}\n";
+      inv = ", const hf_I_" + name + " &I";
+    }
     f << "__device__ __forceinline__ void " << name << "(const HfArgs &A" << tile << idx << ", const hf_R_" << name
-      << " &R, " << rtype(t) << " (&hf_out)[" << c.V << "]) {\n";
+      << " &R" << inv << ", " << rtype(t) << " (&hf_out)[" << c.V << "]) {\n";
     f << b.os.str();
-    f << "#pragma unroll\n  for (int l = 0; l < " << c.V << "; ++l) hf_out[l] = " << v << "[l];\n  (void)A; (void)R;\n}\n\n";
+    f << "#pragma unroll\n  for (int l = 0; l < " << c.V << "; ++l) hf_out[l] = " << v << "[l];\n  (void)A; (void)R;"
+      << (inv_split_ ? " (void)I;" : "") << "\n}\n\n";
     defs_ << f.str();
     return name;
   }
@@ -152,6 +179,44 @@ class Gen {
   }
 
   // dim of E that is the lane variable (or -1)
+  // Where a load goes: the fetch struct R (streaming operands; every load of
+  // a hero that fetches whole steps ahead), the row-invariant struct I
+  // (pipelined loop), or the compute function itself (small arrays, hoisted
+  // out of the hero's row loop by the compiler).
+  struct Dest {
+    int kind;  // 0 compute, 1 R, 2 I
+    std::string name;
+    std::ostringstream &os;
+  };
+  Dest dest(Body &b, const Index &E, bool stream) {
+    if (inv_split_ && !stream && row_invariant(E, b.lane)) return {2, "I.i" + std::to_string(b.ninv++), b.inv_fetch};
+    if (stream || fetch_all_ || inv_split_) return {1, "R." + member(b), b.fetch};
+    return {0, "w" + std::to_string(b.tmp++), b.os};
+  }
+  void declare(Body &b, const Dest &d, const std::string &type, int count) {
+    const std::string dims = count ? "[" + std::to_string(count) + "]" : "";
+    if (d.kind == 0) {
+      b.os << "  " << type << " " << d.name << dims << ";\n";
+      return;
+    }
+    (d.kind == 1 ? b.members : b.inv_members) << "  " << type << " " << d.name.substr(2) << dims << ";\n";
+    // 32- and 64-bit values are pinned in registers (narrower ones are left)
+    if (d.kind == 2 && (type == "hf_u32" || type == "float" || type == "int" || type == "double")) {
+      if (count)
+        b.inv_pin << "#pragma unroll\n  for (int k = 0; k < " << count << "; ++k) asm volatile(\"\" : \"+v\"(" << d.name
+                  << "[k]));\n";
+      else
+        b.inv_pin << "  asm volatile(\"\" : \"+v\"(" << d.name << "));\n";
+    }
+  }
+  // An index whose every term is a constant or the lane variable: the same
+  // for every row of the loop hero (the row index feeds the other dims).
+  static bool row_invariant(const Index &E, int lane) {
+    for (const Term &t : E)
+      if (t.k == Term::EXPR || (t.k == Term::VAR && t.var != lane)) return false;
+    return true;
+  }
+
   static int lane_dim(const Index &E, int lane) {
     if (lane < 0) return -1;
     for (size_t d = 0; d < E.size(); ++d)
@@ -174,13 +239,10 @@ class Gen {
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     std::vector<long long> st = phys_strides(t);
     b.os << "  " << reg << " " << v << "[" << V << "];\n";
-    const bool in_fetch = stream || fetch_all_;
-    std::string m = in_fetch ? "R." + member(b) : "w" + std::to_string(b.tmp++);
-    std::ostringstream &ld_os = in_fetch ? b.fetch : b.os;
-    auto decl = [&](const std::string &type, int count) {
-      if (in_fetch) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
-      else b.os << "  " << type << " " << m << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
-    };
+    const Dest dst = dest(b, E, stream);
+    std::string m = dst.name;
+    std::ostringstream &ld_os = dst.os;
+    auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
       decl(ctype(dt), 0);
       ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
@@ -226,13 +288,10 @@ class Gen {
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     std::vector<long long> st = phys_strides(t);
     b.os << "  " << reg << " " << v << "[" << V << "];\n";
-    const bool in_fetch = stream || fetch_all_;
-    std::string m = in_fetch ? "R." + member(b) : "w" + std::to_string(b.tmp++);
-    std::ostringstream &ld_os = in_fetch ? b.fetch : b.os;
-    auto decl = [&](const std::string &type, int count) {
-      if (in_fetch) b.members << "  " << type << " " << m.substr(2) << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
-      else b.os << "  " << type << " " << m << (count ? "[" + std::to_string(count) + "]" : "") << ";\n";
-    };
+    const Dest dst = dest(b, E, stream);
+    std::string m = dst.name;
+    std::ostringstream &ld_os = dst.os;
+    auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
     const std::string bytes = "((const unsigned char *)" + ptr + ")";
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
       decl("unsigned char", 0);
@@ -269,6 +328,20 @@ class Gen {
     const int V = b.V;
     int ld = V > 1 ? lane_dim(E, b.lane) : -1;
     b.os << "  double " << v << "[" << V << "];\n";
+    if (inv_split_ && row_invariant(E, b.lane)) {  // loaded once, into I
+      const Dest dst = dest(b, E, false);
+      const bool scalar = ld < 0 || t.dims[ld] <= 1;
+      declare(b, dst, "double", scalar ? 0 : V);
+      if (scalar) {
+        b.inv_fetch << "  " << dst.name << " = " << ptr << "[" << off << "];\n";
+        b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = " << dst.name << ";\n";
+      } else {
+        b.inv_fetch << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) "
+                    << dst.name << "[l] = " << ptr << "[o + l]; }\n";
+        b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = " << dst.name << "[l];\n";
+      }
+      return v;
+    }
     if (ld < 0 || t.dims[ld] <= 1) {
       b.os << "  { const double s = " << ptr << "[" << off << "];\n#pragma unroll\n    for (int l = 0; l < " << V
            << "; ++l) " << v << "[l] = s; }\n";
@@ -345,6 +418,7 @@ class Gen {
       v = fresh(b, n);
       lanes(b, v, "float", flit(round_to_dtype(nd.cst, t.dt)));
     } else if (other_partition) {
+      if (inv_split_) fail(HF_ERR_UNSUPPORTED, "codegen: the pipelined loop takes one partition");
       int ld = lane_dim(E, b.lane);
       std::string f = fn(ci, n, ld);
       std::string m = member(b);
@@ -475,6 +549,7 @@ class Gen {
   const Graph &g_;
   Plan &P_;
   bool nt_loads_ = true;
+  bool inv_split_ = false;
   bool fetch_all_ = false;
   std::ostringstream defs_;
   std::map<std::string, bool> done_;
@@ -576,8 +651,26 @@ std::string generate_source(const Graph &g, Plan &P, const std::string &prelude,
       }
       zero_dims(ix, rt, set);
       types << "typedef hf_R_" << f << " hf_regs_t;\n";
-      glue_pair(glue, "hf_loop_eval", "int row, int colv", "hf_regs_t", f, ix.str(), call_args(rt), "", "",
-                "hf_val_t (&hf_res)[HF_V]");
+      bool pipe = false;
+      for (auto &m : P.macros)
+        if (m.first == "HF_PIPE" && m.second) pipe = true;
+      if (pipe) {
+        // the pipelined loop: row-invariant loads once (hf_loop_inv, at any
+        // row of the thread), then pinned; the compute takes both structs
+        types << "typedef hf_I_" << f << " hf_inv_t;\n";
+        const std::string args = call_args(rt);
+        glue << "__device__ __forceinline__ void hf_loop_eval_fetch(const HfArgs &A, int row, int colv, hf_regs_t &R) {\n"
+             << ix.str() << "  " << f << "_fetch(A" << args << ", R);\n}\n";
+        glue << "__device__ __forceinline__ void hf_loop_inv(const HfArgs &A, int row, int colv, hf_inv_t &I) {\n"
+             << ix.str() << "  " << f << "_inv(A" << args << ", I);\n}\n";
+        glue << "__device__ __forceinline__ void hf_loop_inv_pin(hf_inv_t &I) { " << f << "_pin(I); }\n";
+        glue << "__device__ __forceinline__ void hf_loop_eval(const HfArgs &A, int row, int colv, const hf_regs_t &R, "
+                "const hf_inv_t &I, hf_val_t (&hf_res)[HF_V]) {\n"
+             << ix.str() << "  " << f << "(A" << args << ", R, I, hf_res);\n}\n";
+      } else {
+        glue_pair(glue, "hf_loop_eval", "int row, int colv", "hf_regs_t", f, ix.str(), call_args(rt), "", "",
+                  "hf_val_t (&hf_res)[HF_V]");
+      }
       glue << "__device__ __forceinline__ void hf_loop_store(const HfArgs &A, int row, int colv, const hf_val_t (&r)[HF_V]) {\n";
       glue << "  " << store_call(rt.dt, c.V, "row * " + std::to_string(DL) + " + colv * HF_V", "r") << "\n}\n";
       break;

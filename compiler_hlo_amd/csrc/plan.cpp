@@ -462,6 +462,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
   for (const Quant &q : g.quants)
     if (q.qdim >= 0) small = true;
   int V = 1;
+  int wbits_all = 0;  // widest of the result and the streaming inputs, in bits
   if (c.lane >= 0 && !c.general) {
     // 128-bit lanes for the widest of the result and the streaming inputs,
     // except where every stream is 4-bit and column data is read: 32 elements
@@ -470,6 +471,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
     // 16, 8.6 at 8 and 8.3 at 4 elements a lane; a per-tensor s4 requantize
     // keeps 32: 6.7 us against 8.1 at 16).
     const int wbits = std::max(dtype_bits(rt.dt), stream_elem_bits(g, c));
+    wbits_all = wbits;
     const int vdef = small && wbits <= 4 ? 4 : 128 / wbits;
     V = vec_width(DL, std::max(1, (int)std::min<long long>(env_ll("HF_LOOP_VMAX", vdef), 128 / wbits)));
     V = align_lanes(c, V);
@@ -503,16 +505,38 @@ Plan plan_loop(const Graph &g, Ctx c) {
     rpb = block / tpr;
     nch = 1;
   }
+  //
+  // Fusions of 8-bit streams with one partition (quantized arithmetic, and
+  // the per-axis requantize with its column data) run software-pipelined:
+  // each thread loads its column data once, then keeps the loads of the next
+  // HF_PIPE rows in flight while it computes and stores the current one,
+  // over HF_NR rows (a compile-time count, up to 16), in at least 256
+  // workgroups (one wave per SIMD).  Loading every row up front left the
+  // VALU idle until most of the data had arrived.  Measured at sustained
+  // clocks: the per-axis requantize of i8[4096,4096] took 8.88 us with four
+  // rows a thread loaded up front, and 7.47-7.52 us pipelined six rows deep
+  // over 16 rows (7.69 four deep, 8.1 with eight rows a thread); the
+  // quantized add of i8[4096,4096] went from 10.69 to 9.94 us (four deep,
+  // 16 rows).  GELU in bf16 (VALU-bound), the f32 pad/reverse/concatenate
+  // and si4 streams (2 bytes a lane) ran 8-12% slower pipelined and keep
+  // the loop above.
+  const bool pipe = c.part_root.size() == 1 && wbits_all == 8 && V * 8 == 128 && env_ll("HF_LOOP_PIPE", 1) > 0;
   long long per = small ? 4 : 1;
   long long target = env_ll("HF_LOOP_WGS", nch * ceil_div(ceil_div(rows, rpb), per));
+  if (pipe && !std::getenv("HF_LOOP_WGS"))
+    target = nch * std::max(ceil_div(256, nch), ceil_div(ceil_div(rows, rpb), 16));
   long long ngroups = std::max<long long>(1, std::min(ceil_div(rows, rpb), std::max<long long>(1, target / nch)));
+  const long long rstep = ngroups * rpb;
+  const long long nr = ceil_div(rows, rstep);
+  const long long pd = pipe && nr <= 16 ? std::min(env_ll("HF_LOOP_PIPE", small ? 6 : 4), nr) : 0;
   P.ctx.push_back(c);
   P.block = block;
   P.grid = nch * ngroups;
   P.empty = rt.numel() == 0;
   P.macros = {{"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", rows}, {"HF_COLS_V", cols_v},
               {"HF_TPR", tpr}, {"HF_RPB", rpb}, {"HF_NCH", nch},
-              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", small ? 4 : 2)}};
+              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", small ? 4 : 2)},
+              {"HF_PIPE", pd}, {"HF_RSTEP", rstep}, {"HF_NR", nr}};
   P.info.vector_elems = V;
   P.info.elements = rt.numel();
   P.info.rows = rows;

@@ -58,6 +58,60 @@ def test_quant_full():
     say("clamped fraction", clamped)
 
 
+@pytest.mark.parametrize("r,c", [(1030, 4096), (4091, 4096), (4096, 4096), (257, 8192), (64, 1024)])
+def test_quant_pipelined_rows(r, c):
+    """The per-axis requantize on the pipelined loop (8-bit streams): row
+    counts that leave the last row of some threads past the end, and grids
+    of one to sixteen rows a thread; bit-exact."""
+    spec, params, _ = W.quant_dequant_bias_requant(r, c, seed=90 + r % 7)
+    got, f = run_gpu(spec.nodes, params)
+    src = f.source()
+    say("quant pipelined", r, c, f.plan()["grid_blocks"],
+        [l for l in src.splitlines() if l.startswith(("#define HF_PIPE", "#define HF_NR"))])
+    assert "#define HF_PIPE 0" not in src
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "s8")
+
+
+def test_pipelined_loop_row_and_column_data():
+    """Pipelined 8-bit loops whose small arrays move with the row (per-axis
+    dequantize along dim 0, a bias broadcast along dim 0) and with the column
+    (a per-axis quantize of the result along dim 1, with its reciprocal
+    scales), plus a rank-0 parameter: the row-dependent ones are fetched
+    with each row, the others once.  Bit-exact against the oracle."""
+    g = W.rng(93)
+    r, c = 2053, 2048
+    q = W.integers(g, r * c, -128, 127, np.int8)
+    s_in = W.uniform_f32(g, r, 0.001, 0.05)
+    z_in = W.integers(g, r, -20, 20, np.int64)
+    s_out = W.uniform_f32(g, c, 0.01, 0.04)
+    z_out = W.integers(g, c, -10, 10, np.int64)
+    brow = W.normal_f32(g, r, 0.1)
+    k = np.array(0.03125, np.float32)
+    s = W.Spec()
+    p = s.parameter(0, "s8", [r, c], quant=W.quant_type("s8", s_in, z_in, qdim=0))
+    b = s.parameter(1, "f32", [r])
+    kk = s.parameter(2, "f32", [])
+    d = s.op("uniform_dequantize", [p], "f32", [r, c])
+    bb = s.broadcast_in_dim(b, [0], "f32", [r, c])
+    kb = s.broadcast_in_dim(kk, [], "f32", [r, c])
+    y = s.binary("add", s.binary("add", d, bb, "f32", [r, c]), kb, "f32", [r, c])
+    s.op("uniform_quantize", [y], "s8", [r, c], quant=W.quant_type("s8", s_out, z_out, qdim=1))
+    ps = [q, brow, k]
+    got, f = run_gpu(s.nodes, ps)
+    src = f.source()
+    assert "#define HF_PIPE 0" not in src and f.plan()["n_partitions"] == 1
+    assert_bitexact(got, oracle.evaluate(s.nodes, ps), "s8")
+
+
+def test_quantized_add_pipelined_full():
+    """The per-tensor quantized add of i8[4096,4096] (pipelined, sixteen rows
+    a thread), whole output bit-exact."""
+    spec, params, _ = W.quantized_add_i8()
+    got, f = run_gpu(spec.nodes, params)
+    assert "#define HF_PIPE 0" not in f.source()
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "s8")
+
+
 @pytest.mark.parametrize("r,c", [(37, 160), (5, 48), (3, 2), (300, 4096)])
 def test_quant_s4_small(r, c):
     """The per-axis requantize with si4 storage in and out: bytes bit-exact."""
