@@ -19,7 +19,11 @@ quantized series as well).  The first two also run with NaN, +-inf and +-0
 in the inputs (NaN positions compare, other elements bitwise).  A sixth
 series puts one exp, log or tanh among exactly rounding ops and compares
 within the bound the result allows (half of it with special values in the
-inputs).
+inputs).  A seventh series is 8-bit arithmetic for the pipelined loop:
+per-tensor and per-axis dequantize of s8/u8 storage with arbitrary scales,
+a bias broadcast along random dims, and a per-tensor or per-axis quantize
+to s8/u8; both sides round each op once in f32 and divide by the scale, so
+it is bit-exact too.
 
 The CPU test plans and compiles every case for gfx950 (and runs the oracle on
 all but the big ones); the GPU tests run them.
@@ -41,6 +45,7 @@ N_RANK = 24         # seeds 6000.. : rank 4-6 with size-1 dims
 N_WRANK = 24        # seeds 7000.. : the pad/concatenate/quantized series at rank 4-5
 N_SPECIAL = 24      # seeds 8000.. : the first two series with NaN, +-inf and +-0 in the inputs
 N_TRANS = 48        # seeds 5000.. : one exp, log or tanh, compared within its bound
+N_Q8 = 48           # seeds 9000.. : 8-bit dequantize / bias / quantize loops
 BATCH = 24
 
 
@@ -233,6 +238,56 @@ def random_wide_case(seed, high_rank=False):
     return s, params
 
 
+_ZP8 = {"s8": 0, "u8": 128}  # centre of the zero points drawn
+
+
+def random_q8_case(seed):
+    """(spec, params): one to three s8/u8 parameters dequantized per tensor or
+    per axis (scales in [0.001, 0.05], zero points near the storage centre),
+    combined by add, subtract, maximum or minimum with an optional f32 bias
+    broadcast along a random subset of dims, and quantized per tensor or per
+    axis to s8/u8, in a random layout shared by the inputs (and usually the
+    output): the fusions that take the software-pipelined loop."""
+    g = W.rng(seed)
+    rank = int(g.integers(1, 5))
+    while True:
+        if g.random() < 0.3:
+            dims = [int(g.integers(1, 6)) for _ in range(rank - 1)] + [int(g.choice([16, 32, 48, 64, 4096, 8192]))]
+            g.shuffle(dims)
+        else:
+            dims = [int(g.choice([1, 3, 7, 16, 32, 48, 64, 112, 257, 1000, 1024, 4096])) for _ in range(rank)]
+        if 1 <= math.prod(dims) <= 3_000_000:
+            break
+    layout = _layout(g, rank)
+    s = W.Spec()
+    params, vals = [], []
+
+    def qtype(st, smin, smax, spread):
+        if g.random() < 0.45:
+            return W.quant_type(st, [float(g.uniform(smin, smax))], [_ZP8[st] + int(g.integers(-spread, spread + 1))])
+        qd = int(g.integers(rank))
+        return W.quant_type(st, [float(x) for x in g.uniform(smin, smax, dims[qd])],
+                            [_ZP8[st] + int(z) for z in g.integers(-spread, spread + 1, dims[qd])], qdim=qd)
+    for _ in range(int(g.integers(1, 4))):
+        st = str(g.choice(["s8", "u8"]))
+        x = s.parameter(len(params), st, dims, layout, quant=qtype(st, 0.001, 0.05, 20))
+        params.append(_storage_values(g, st, math.prod(dims)))
+        vals.append(s.op("uniform_dequantize", [x], "f32", dims))
+    if g.random() < 0.6:
+        bd = sorted(int(d) for d in g.choice(rank, int(g.integers(0, rank + 1)), replace=False))
+        bdims = [dims[d] for d in bd]
+        b = s.parameter(len(params), "f32", bdims)
+        params.append(W.normal_f32(g, math.prod(bdims), 0.1))
+        vals.append(s.broadcast_in_dim(b, bd, "f32", dims))
+    r = vals[0]
+    for v in vals[1:]:
+        r = s.binary(str(g.choice(["add", "subtract", "maximum", "minimum"])), r, v, "f32", dims)
+    st = str(g.choice(["s8", "u8"]))
+    s.op("uniform_quantize", [r], st, dims, m2m=layout if g.random() < 0.7 else None,
+         quant=qtype(st, 0.005, 0.05, 10))
+    return s, params
+
+
 def random_trans_case(seed, specials=False):
     """(spec, params, check): one exp, log or tanh (f32 or bf16) inside a
     random fusion, between exactly rounding ops.  Its operand is exact
@@ -341,6 +396,8 @@ def _make(seed, series):
         return s, _with_specials(seed, s, params)
     if series in ("wide", "wrank"):
         return random_wide_case(seed, series == "wrank")
+    if series == "q8":
+        return random_q8_case(seed)
     return random_case(seed, series in ("hero", "big"), series == "big", series == "rank")
 
 
@@ -349,7 +406,7 @@ def _cases():
     return ([(1000 + k, "any") for k in range(N_CASES)] + [(2000 + k, "hero") for k in range(N_HERO)]
             + [(3000 + k, "wide") for k in range(N_WIDE)] + [(4000 + k, "big") for k in range(N_BIG)]
             + [(6000 + k, "rank") for k in range(N_RANK)] + [(7000 + k, "wrank") for k in range(N_WRANK)]
-            + [(8000 + k, "special") for k in range(N_SPECIAL)])
+            + [(8000 + k, "special") for k in range(N_SPECIAL)] + [(9000 + k, "q8") for k in range(N_Q8)])
 
 
 def test_random_fusions_plan_and_compile():
@@ -377,13 +434,13 @@ def test_random_fusions_plan_and_compile():
         if h and series != "big":  # the big cases' oracle runs with their GPU test
             oracle.evaluate(s.nodes, params)
     ran = sum(1 for h in heroes_of if h)
-    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL
+    total = N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL + N_Q8
     assert ran >= total * 2 // 3, (ran, total - ran)
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL) // BATCH))
+@pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL + N_Q8) // BATCH))
 def test_random_fusions_gpu(batch):
     import compiler_hlo_amd as H
     for seed, series in _cases()[batch * BATCH:(batch + 1) * BATCH]:
