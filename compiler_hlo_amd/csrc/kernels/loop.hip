@@ -10,9 +10,8 @@
 // HF_UNROLL rows (hf_loop_eval_fetch), then computes and stores them, so the
 // loads of all those rows are in flight together.
 //
-//
-// With HF_PIPE > 0 (fusions that read column data) the thread's HF_NR rows
-// run as a software pipeline instead: the row-invariant loads first
+// With HF_PIPE > 0 (the planner's choice for 8-bit streams) the thread's
+// HF_NR rows run as a software pipeline instead: the row-invariant loads first
 // (hf_loop_inv), then the first HF_PIPE rows' loads; each row is computed and
 // stored as soon as its own data is in, and the load of the row HF_PIPE
 // further on is issued in its place.  The compute of a row then waits for
