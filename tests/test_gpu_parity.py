@@ -58,10 +58,12 @@ def test_quant_full():
     say("clamped fraction", clamped)
 
 
-@pytest.mark.parametrize("r,c", [(1030, 4096), (4091, 4096), (4096, 4096), (257, 8192), (64, 1024)])
+@pytest.mark.parametrize("r,c", [(1030, 4096), (4091, 4096), (4096, 4096), (257, 8192), (64, 1024),
+                                 (1, 16), (5, 48)])
 def test_quant_pipelined_rows(r, c):
     """The per-axis requantize on the pipelined loop (8-bit streams): row
-    counts that leave the last row of some threads past the end, and grids
+    counts that leave the last row of some threads past the end, threads
+    with no row at all (fewer rows than a workgroup's row slots), and grids
     of one to sixteen rows a thread; bit-exact."""
     spec, params, _ = W.quant_dequant_bias_requant(r, c, seed=90 + r % 7)
     got, f = run_gpu(spec.nodes, params)
