@@ -472,6 +472,30 @@ def test_slice_validation():
     assert st(computed_start)[0] == "HF_ERR_INVALID"
 
 
+def test_loop_pipeline_choice():
+    """The loop's software pipeline goes to single-partition fusions of 8-bit
+    streams with 16 elements a lane: the per-axis requantize (six rows in
+    flight, sixteen rows a thread, 256 workgroups) and the quantized add (four
+    in flight); GELU, the si4 requantize and C1 keep the plain loop.  In the
+    pipelined source the column data load into their own struct (hf_I_),
+    pinned after the first row, and the compute takes it."""
+    def macros(spec):
+        src = H.Fusion(spec.nodes, mode="compile").source()
+        return {k: int(v) for k, v in re.findall(r"#define (HF_PIPE|HF_NR|HF_RSTEP) (\d+)", src)}, src
+    m, src = macros(W.quant_dequant_bias_requant()[0])
+    assert (m["HF_PIPE"], m["HF_NR"], m["HF_RSTEP"]) == (6, 16, 256)
+    assert plan_of(W.quant_dequant_bias_requant()[0])["grid_blocks"] == 256
+    assert "struct hf_I_" in src and "hf_loop_inv_pin(I)" in src and 'asm volatile("" : "+v"' in src
+    m, _ = macros(W.quantized_add_i8()[0])
+    assert (m["HF_PIPE"], m["HF_NR"]) == (4, 16)
+    for mk in (W.gelu_bf16, W.quant_dequant_bias_requant_s4, W.loop_log_transpose_add):
+        m, src = macros(mk()[0])
+        assert m["HF_PIPE"] == 0 and "struct hf_I_" not in src, mk.__name__
+    # a row count that leaves some threads one row short: 16 rows at most
+    m, _ = macros(W.quant_dequant_bias_requant(4091, 4096)[0])
+    assert (m["HF_NR"], m["HF_RSTEP"]) == (16, 256) and 15 * 256 < 4091
+
+
 def test_slice_plans():
     """A slice keeps 128-bit lanes when its start along the minor dim is a
     multiple of the vector width and counts only the elements it reads; a
