@@ -178,7 +178,6 @@ class Gen {
     return s.empty() ? "0" : s;
   }
 
-  // dim of E that is the lane variable (or -1)
   // Where a load goes: the fetch struct R (streaming operands; every load of
   // a hero that fetches whole steps ahead), the row-invariant struct I
   // (pipelined loop), or the compute function itself (small arrays, hoisted
@@ -217,6 +216,7 @@ class Gen {
     return true;
   }
 
+  // dim of E that is the lane variable (or -1)
   static int lane_dim(const Index &E, int lane) {
     if (lane < 0) return -1;
     for (size_t d = 0; d < E.size(); ++d)
