@@ -819,6 +819,36 @@ def test_largest_four_bit_array():
     del q, got
 
 
+def test_largest_pipelined_loop():
+    """The per-axis requantize of s8[32767, 65536] (2^31 - 65536 bytes in and
+    out) on the pipelined loop: byte offsets reach their maximum, and the
+    last of a thread's sixteen rows lies past the end for one row slot.
+    Sampled outputs, bit-exact."""
+    n0, n1 = 32767, 65536
+    say("largest pipelined loop", n0, n1)
+    g = W.rng(94)
+    q = np.frombuffer(bytearray(g.bytes(n0 * n1)), np.int8)
+    scales = W.uniform_f32(g, n1, 0.001, 0.05)
+    zps = W.integers(g, n1, -20, 20, np.int64)
+    bias = W.normal_f32(g, n1, 0.1)
+    s = W.Spec()
+    p = s.parameter(0, "s8", [n0, n1], quant=W.quant_type("s8", scales, zps, qdim=1))
+    b = s.parameter(1, "f32", [n1])
+    d = s.op("uniform_dequantize", [p], "f32", [n0, n1])
+    y = s.binary("add", d, s.broadcast_in_dim(b, [1], "f32", [n0, n1]), "f32", [n0, n1])
+    s.op("uniform_quantize", [y], "s8", [n0, n1], quant=W.quant_type("s8", [0.02], [0]))
+    got, f = run_gpu(s.nodes, [q, bias])
+    src = f.source()
+    assert f.plan()["hero"] == "loop" and "#define HF_PIPE 0" not in src
+    assert "#define HF_NR 16" in src
+    pts = np.stack([g.integers(0, n0, 20000), g.integers(0, n1, 20000)], 1)
+    pts = np.concatenate([pts, [[0, 0], [n0 - 1, n1 - 1], [n0 - 1, 0], [0, n1 - 1]]])
+    want, _ = oracle.evaluate_points(s.nodes, [q, bias], pts)
+    lin = pts[:, 0] * n1 + pts[:, 1]
+    assert np.array_equal(got[lin].astype(np.float64), want)
+    del q, got
+
+
 # --------------------------------------------------------------------------
 # index transforms: reverse, iota, pad, concatenate
 # --------------------------------------------------------------------------
