@@ -98,10 +98,13 @@ def copy_case(dtype, dims):
             x = W.normal_f32(g, n)
         elif dtype == "s8":
             x = W.integers(g, n, -128, 127, np.int8)
+        elif dtype == "s4":
+            x = W.integers(g, (n + 1) // 2, 0, 255, np.uint8)
         else:
             x = W.normal_bf16(g, n)
         name = "copy_%s_%s" % (dtype, "x".join(map(str, dims)))
-        return spec, [x], {"name": name, "elements": n, "bytes": 2 * n * W.nbytes_of(dtype)}
+        nbytes = (n + 1) // 2 if dtype == "s4" else n * W.nbytes_of(dtype)
+        return spec, [x], {"name": name, "elements": n, "bytes": 2 * nbytes}
     return make
 
 
@@ -140,6 +143,7 @@ def workload_makers():
         "copy_f32_4096x4096": (copy_case("f32", [4096, 4096]), {}, None),
         "copy_bf16_64x512x1024": (copy_case("bf16", [64, 512, 1024]), {}, None),
         "copy_s8_4096x4096": (copy_case("s8", [4096, 4096]), {}, None),
+        "copy_s4_4096x4096": (copy_case("s4", [4096, 4096]), {}, None),
         "copy_s8_8192x8192": (copy_case("s8", [8192, 8192]), {}, None),
         "copy_s8_16384x32768": (copy_case("s8", [16384, 32768]), {}, None),
         "iota_s32_1": (iota_case(1), {}, None),

@@ -520,7 +520,9 @@ Plan plan_loop(const Graph &g, Ctx c) {
   // 16 rows).  GELU in bf16 (VALU-bound), the f32 pad/reverse/concatenate
   // and si4 streams (2 bytes a lane) ran 8-12% slower pipelined and keep
   // the loop above.
-  const bool pipe = c.part_root.size() == 1 && wbits_all == 8 && V * 8 == 128 && env_ll("HF_LOOP_PIPE", 1) > 0;
+  const bool pipe_any = c.part_root.size() == 1 && c.lane >= 0 && !c.general;
+  const bool pipe = (pipe_any && wbits_all == 8 && V * 8 == 128 && env_ll("HF_LOOP_PIPE", 1) > 0) ||
+                    (pipe_any && std::getenv("HF_LOOP_PIPE") && env_ll("HF_LOOP_PIPE", 0) > 0);
   long long per = small ? 4 : 1;
   long long target = env_ll("HF_LOOP_WGS", nch * ceil_div(ceil_div(rows, rpb), per));
   if (pipe && !std::getenv("HF_LOOP_WGS"))

@@ -114,6 +114,28 @@ def test_quantized_add_pipelined_full():
     assert_bitexact(got, oracle.evaluate(spec.nodes, params), "s8")
 
 
+@pytest.mark.parametrize("case", ["gelu_bf16", "s4_requantize", "pad_reverse_concat_f32", "quantized_add_3_lanes"])
+def test_pipeline_forced_by_its_knob(case, monkeypatch):
+    """HF_LOOP_PIPE set above zero puts any single-partition loop on the
+    pipeline, whatever its types and lane width: bf16 with a tanh, si4 with
+    column data, f32 index transforms, and 8-bit rows of three lanes.  A
+    grid of a few workgroups gives seven rows a thread, four in flight, the
+    last row past the end for some threads.  Bit-exact against the oracle."""
+    monkeypatch.setenv("HF_LOOP_PIPE", "4")
+    spec, params, wgs, dt = {
+        "gelu_bf16": lambda: (*W.gelu_bf16(1, 2053, 512)[:2], 80, "bf16"),
+        "s4_requantize": lambda: (*W.quant_dequant_bias_requant_s4(2053, 512, seed=95)[:2], 160, "u8"),
+        "pad_reverse_concat_f32": lambda: (*W.pad_reverse_concat_f32(1001, 256, 1050, seed=96)[:2], 80, "f32"),
+        "quantized_add_3_lanes": lambda: (*W.quantized_add_i8(2053, 24, seed=97)[:2], 4, "s8"),
+    }[case]()
+    monkeypatch.setenv("HF_LOOP_WGS", str(wgs))
+    got, f = run_gpu(spec.nodes, params)
+    src = f.source()
+    say("forced pipeline", case, [l for l in src.splitlines() if l.startswith(("#define HF_PIPE", "#define HF_NR"))])
+    assert "#define HF_PIPE 4" in src and "#define HF_NR 7" in src
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), dt)
+
+
 @pytest.mark.parametrize("r,c", [(37, 160), (5, 48), (3, 2), (300, 4096)])
 def test_quant_s4_small(r, c):
     """The per-axis requantize with si4 storage in and out: bytes bit-exact."""
