@@ -166,9 +166,10 @@ def _storage_values(g, dt, n):
 
 def random_wide_case(seed, high_rank=False):
     """(spec, params): f32 values built by pad, concatenate and per-tensor or
-    per-axis dequantize (power-of-two scales, so every value and sum stays
-    exact), combined by exact elementwise ops, ending in a quantize to an 8-
-    or 4-bit type, a reduce, or neither."""
+    per-axis dequantize (power-of-two scales, so every value is exact, and
+    so is every sum whose terms stay small against their lowest bits),
+    combined by exact elementwise ops, ending in a quantize to an 8- or 4-bit
+    type, a reduce, or neither."""
     g = W.rng(seed)
     rank = int(g.integers(4, 6)) if high_rank else int(g.integers(1, 4))
     sizes = [1, 2, 3, 4, 6, 9, 16] if high_rank else [2, 3, 6, 9, 16, 31, 64, 100]
@@ -439,6 +440,78 @@ def test_random_fusions_plan_and_compile():
     assert all(heroes[h] >= 5 for h in ("loop", "transpose", "row_reduce", "column_reduce")), heroes
 
 
+def _low_bit(x: np.ndarray) -> np.ndarray:
+    """Value of the lowest set bit of each finite nonzero f32 in x."""
+    m, e = np.frexp(np.abs(x.astype(np.float64)))
+    mi = (m * 2.0 ** 24).astype(np.int64)
+    return np.ldexp((mi & -mi).astype(np.float64), e - 24)
+
+
+def check_random_result(got, s, params):
+    """Bit-exact against the oracle.  The one exception is an f32 sum whose
+    terms do not make every partial sum exact: all terms are multiples of
+    their smallest low bit q, so any partial sum below 2^24 q is exact in
+    f32 and every summation order gives the oracle's rounded exact sum; an
+    output whose sum of |terms| reaches 2^24 q may differ from it by at most
+    (n - 1) 2^-24 sum|terms| for n terms (any order, Operation semantics,
+    "Reduce": the order of a float sum is left to the implementation)."""
+    root = s.nodes[-1]
+    dt = root["dtype"]
+    want = oracle.evaluate(s.nodes, params)
+    try:
+        assert_bitexact(got, want, "u8" if dt in ("s4", "u4") else dt)
+        return
+    except AssertionError:
+        if not (root["op"] == "reduce" and root["reducer"] == "add" and dt == "f32"):
+            raise
+    terms = oracle.evaluate(s.nodes, params, root=root["operands"][0]).view(np.float32)
+    fin = terms[np.isfinite(terms) & (terms != 0)]
+    q = _low_bit(fin).min() if fin.size else np.inf
+    dims = root["dims"]
+    n_out = math.prod(dims)
+    n_terms = terms.size // max(n_out, 1)
+    idx = np.indices(dims).reshape(len(dims), -1).T if dims else np.zeros((1, 0), np.int64)
+    _, aux = oracle.evaluate_points(s.nodes, params, idx)
+    m2m = root.get("m2m") or list(range(len(dims) - 1, -1, -1))
+    lin, stride = np.zeros(len(idx), np.int64), 1
+    for d in m2m:
+        lin += idx[:, d] * stride
+        stride *= dims[d]
+    g = got.view(np.float32)[lin].astype(np.float64)
+    w = want.view(np.float32)[lin].astype(np.float64)
+    bad = np.flatnonzero(~((g == w) | (np.isnan(g) & np.isnan(w))))
+    total, exact = aux[bad, 0], aux[bad, 1]
+    assert np.all(np.isfinite(total)) and np.all(total >= 2.0 ** 24 * q), (
+        "outputs whose partial sums are all exact differ", bad[:5], g[bad[:5]], w[bad[:5]])
+    assert np.all(np.abs(g[bad] - exact) <= (n_terms - 1) * 2.0 ** -24 * total), (
+        "sums outside the summation bound", bad[:5], g[bad[:5]], exact[:5])
+
+
+def test_sum_checker_accepts_only_what_the_order_allows():
+    """check_random_result on oracle results with a planted change: a sum of
+    65,536 terms in steps of 1/8 that reach 9.5 M in magnitude (its exact
+    value, -7917890.625, lies between two f32 values, and a different order
+    may give either) passes one ulp off but not 10^6 off; a sum whose terms
+    keep every partial sum exact fails one ulp off."""
+    s, params = _make(20129, "wide")
+    want = oracle.evaluate(s.nodes, params)
+    check_random_result(want.copy(), s, params)
+    off = want.view(np.uint32).copy()
+    off[0] += 1
+    check_random_result(off.view(np.float32), s, params)
+    far = want.copy()
+    far[0] += np.float32(1e6)
+    with pytest.raises(AssertionError):
+        check_random_result(far, s, params)
+    s, params = _make(3001, "wide")
+    want = oracle.evaluate(s.nodes, params)
+    check_random_result(want.copy(), s, params)
+    off = want.view(np.uint32).copy()
+    off[0] += 1
+    with pytest.raises(AssertionError):
+        check_random_result(off.view(np.float32), s, params)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("batch", range((N_CASES + N_HERO + N_WIDE + N_BIG + N_RANK + N_WRANK + N_SPECIAL + N_Q8) // BATCH))
 def test_random_fusions_gpu(batch):
@@ -451,8 +524,7 @@ def test_random_fusions_gpu(batch):
             continue
         print("random fusion seed", seed, [nd["op"] for nd in s.nodes], flush=True)
         got, f = run_gpu(s.nodes, params)
-        dt = s.nodes[-1]["dtype"]
-        assert_bitexact(got, oracle.evaluate(s.nodes, params), "u8" if dt in ("s4", "u4") else dt)
+        check_random_result(got, s, params)
 
 
 def test_random_transcendental_fusions_plan_and_check_oracle():
