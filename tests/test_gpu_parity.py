@@ -696,6 +696,17 @@ def test_argmax(dims, rdim, dtype):
     assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32")
 
 
+def test_argmax_rows_full():
+    """The argmax over the rows of bf16[8192, 8192] ~ N(0,1) at full size, in
+    the launch configuration the benchmark times: all 8,192 indices
+    bit-exact."""
+    spec, params, _ = W.argmax_rows_bf16()
+    say("argmax rows full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    assert f.plan()["hero"] == "row_reduce"
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "s32")
+
+
 def test_argmax_nan_and_init_ties():
     nan, ninf = np.float32("nan"), np.float32("-inf")
     rows = np.array([[1, nan, 3, nan, 3], [nan] * 5, [ninf, ninf, 2, ninf, ninf], [ninf] * 5], np.float32)
@@ -989,6 +1000,20 @@ def test_reduce_epilogue_mean():
     assert f.plan()["hero"] == "row_reduce"
     want = np.asarray(oracle.evaluate(s.nodes, [x]), np.float64)
     bound = 1e-5 * np.abs(x.reshape(rows, n)).astype(np.float64).sum(1) / n + np.spacing(np.abs(want).astype(np.float32))
+    assert (np.abs(np.asarray(got, np.float64) - want) <= bound).all()
+
+
+def test_row_mean_full():
+    """The row mean of f32[16384, 4096] at full size, in the launch
+    configuration the benchmark times: every row within the summation bound
+    plus the division's rounding."""
+    spec, params, _ = W.row_mean_f32()
+    say("row mean full")
+    got, f = run_gpu(spec.nodes, params, reps=2)
+    assert f.plan()["hero"] == "row_reduce"
+    x = params[0].reshape(16384, 4096)
+    want = np.asarray(oracle.evaluate(spec.nodes, params), np.float64)
+    bound = 1e-5 * np.abs(x).astype(np.float64).sum(1) / 4096 + np.spacing(np.abs(want).astype(np.float32))
     assert (np.abs(np.asarray(got, np.float64) - want) <= bound).all()
 
 
