@@ -373,6 +373,34 @@ def test_exp_bf16_exhaustive():
     assert np.all(np.isnan(out[~fin & np.isnan(x)]))
 
 
+@pytest.mark.parametrize("op,ref", [("tanh", np.tanh), ("log", np.log)])
+def test_tanh_log_bf16_exhaustive(op, ref):
+    """bf16 tanh and log over all 65536 inputs are the RNE of the exact value:
+    within half a bf16 ulp (plus 1e-6 of one, for numpy's float64 error) of
+    numpy's float64 result, the sign and zero of tanh kept (tanh(-0) = -0),
+    log of a negative number NaN, log(+-0) = -inf, tanh(+-inf) = +-1."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = oracle.bf16_bits_to_f32(allbits)
+    s = Spec()
+    p = s.parameter(0, "bf16", [65536])
+    s.unary(op, p, "bf16", [65536])
+    out = oracle.bf16_bits_to_f32(ev(s, [allbits]))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        want = ref(x.astype(np.float64))
+    for xi, r, e in zip(x.tolist(), out.tolist(), want.tolist()):
+        if math.isnan(e):
+            assert math.isnan(r), (xi, r)
+        elif math.isinf(e) or e == 0.0:
+            assert r == e and math.copysign(1.0, r) == math.copysign(1.0, e), (xi, r, e)
+        else:
+            ulp = 2.0 ** (max(math.frexp(r)[1] - 1, -126) - 7)
+            assert abs(e - r) <= ulp * (0.5 + 1e-6), (xi, r, e)
+    if op == "tanh":
+        m = ~np.isnan(x)
+        assert np.array_equal(np.signbit(out[m]), np.signbit(x[m]))
+        assert out[allbits == 0x7F80][0] == 1.0 and out[allbits == 0xFF80][0] == -1.0
+
+
 # IEEE 754-2019 maximum and minimum over {NaN, -0, +0, -inf, +inf, 1.5},
 # written out by hand (row = lhs, column = rhs): NaN propagates from either
 # side, and -0 orders below +0.
