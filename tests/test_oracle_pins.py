@@ -401,6 +401,33 @@ def test_tanh_log_bf16_exhaustive(op, ref):
         assert out[allbits == 0x7F80][0] == 1.0 and out[allbits == 0xFF80][0] == -1.0
 
 
+@pytest.mark.parametrize("op,ref", [("exponential", np.exp), ("tanh", np.tanh), ("log", np.log)])
+def test_exp_tanh_log_f16_exhaustive(op, ref):
+    """f16 exp, tanh and log over all 65536 inputs are the RNE of the exact
+    value: within half an f16 ulp (subnormal spacing 2^-24 below 2^-14) of
+    numpy's float64 result, with overflow to +inf past the largest f16
+    (65504, rounding boundary 65520), and the signs, zeros, infinities and
+    NaNs of each op's definition."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = allbits.view(np.float16).astype(np.float32)
+    s = Spec()
+    p = s.parameter(0, "f16", [65536])
+    s.unary(op, p, "f16", [65536])
+    out = ev(s, [allbits]).view(np.float16).astype(np.float64)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        want = ref(x.astype(np.float64))
+    for xi, r, e in zip(x.tolist(), out.tolist(), want.tolist()):
+        if math.isnan(e):
+            assert math.isnan(r), (xi, r)
+        elif math.isinf(e) or abs(e) >= 65520.0:
+            assert math.isinf(r) and (r > 0) == (e > 0), (xi, r, e)
+        elif e == 0.0:
+            assert r == e and math.copysign(1.0, r) == math.copysign(1.0, e), (xi, r, e)
+        else:
+            ulp = 2.0 ** (max(math.frexp(abs(r) if r else 2.0 ** -24)[1] - 1, -14) - 10)
+            assert abs(e - r) <= ulp * (0.5 + 1e-6), (xi, r, e)
+
+
 # IEEE 754-2019 maximum and minimum over {NaN, -0, +0, -inf, +inf, 1.5},
 # written out by hand (row = lhs, column = rhs): NaN propagates from either
 # side, and -0 orders below +0.
