@@ -1336,6 +1336,35 @@ def test_tanh_bf16_exhaustive():
     assert_bitexact(got, oracle.evaluate(s.nodes, [allbits]), "bf16")
 
 
+@pytest.mark.parametrize("dt,op", [("bf16", "log"), ("f16", "exponential"), ("f16", "tanh"), ("f16", "log")])
+def test_16_bit_transcendentals_exhaustive(dt, op):
+    """Every 16-bit input of the 16-bit transcendentals not covered above:
+    within one ulp of the oracle's correctly rounded value (the f32 result of
+    the device function rounds once more to the 16-bit type), NaN where the
+    oracle has NaN.  The count of inputs one ulp off is reported."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = W.Spec()
+    p = s.parameter(0, dt, [65536])
+    s.unary(op, p, dt, [65536])
+    got, _ = run_gpu(s.nodes, [allbits])
+    d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), dt, 1)
+    say("%s %s: %d of 65536 inputs 1 ulp off" % (dt, op, int((d > 0).sum())))
+
+
+def test_tanh_f32_sample():
+    """f32 tanh (tanhf) on 2^20 inputs of every magnitude from 2^-12 to 8 and
+    the special values: within 2 ulp of the oracle's correctly rounded value."""
+    g = W.rng(44)
+    x = (g.standard_normal(1 << 20) * np.exp2(g.integers(-12, 4, 1 << 20))).astype(np.float32)
+    x[:8] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -20.0, 20.0]
+    s = W.Spec()
+    p = s.parameter(0, "f32", [x.size])
+    s.unary("tanh", p, "f32", [x.size])
+    got, _ = run_gpu(s.nodes, [x])
+    d = assert_ulp(got, oracle.evaluate(s.nodes, [x]), "f32", 2)
+    say("tanh ulp histogram", np.bincount(d.astype(np.int64)))
+
+
 def test_exp_log_f32_sample():
     g = W.rng(43)
     for op, x in (("exponential", g.uniform(-103, 89, 1 << 20).astype(np.float32)),
