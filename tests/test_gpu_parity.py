@@ -1341,14 +1341,17 @@ def test_16_bit_transcendentals_exhaustive(dt, op):
     """Every 16-bit input of the 16-bit transcendentals not covered above:
     within one ulp of the oracle's correctly rounded value (the f32 result of
     the device function rounds once more to the 16-bit type), NaN where the
-    oracle has NaN.  The count of inputs one ulp off is reported."""
+    oracle has NaN, and no more inputs one ulp off than measured."""
     allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     s = W.Spec()
     p = s.parameter(0, dt, [65536])
     s.unary(op, p, dt, [65536])
     got, _ = run_gpu(s.nodes, [allbits])
     d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), dt, 1)
-    say("%s %s: %d of 65536 inputs 1 ulp off" % (dt, op, int((d > 0).sum())))
+    off = int((d > 0).sum())
+    say("%s %s: %d of 65536 inputs 1 ulp off" % (dt, op, off))
+    # measured: bf16 log 0, f16 exp 2, f16 tanh 0 (correctly rounded), f16 log 4
+    assert off <= {("bf16", "log"): 0, ("f16", "exponential"): 2, ("f16", "tanh"): 0, ("f16", "log"): 4}[dt, op]
 
 
 def test_tanh_f32_sample():
