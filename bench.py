@@ -142,6 +142,7 @@ def workload_makers():
         "argmax_rows_bf16": (W.argmax_rows_bf16, {}, None),
         "copy_f32_4096x4096": (copy_case("f32", [4096, 4096]), {}, None),
         "copy_bf16_64x512x1024": (copy_case("bf16", [64, 512, 1024]), {}, None),
+        "copy_f32_4250x128": (copy_case("f32", [4250, 128]), {}, None),
         "copy_s8_4096x4096": (copy_case("s8", [4096, 4096]), {}, None),
         "copy_s4_4096x4096": (copy_case("s4", [4096, 4096]), {}, None),
         "copy_s8_8192x8192": (copy_case("s8", [8192, 8192]), {}, None),
