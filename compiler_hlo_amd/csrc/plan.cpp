@@ -660,10 +660,15 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // between W-neighbouring tiles: those go to one XCD (order 3).
     const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0 ? 3 : in_row_bytes >= 8192 ? 2 : 0);
     // Threads per tile: one 128-bit vector per thread and phase for the
-    // narrow tiles above; otherwise 512 (one or two vectors each) when both
-    // phases of a full tile divide evenly among them, else 256.
+    // narrow tiles above; otherwise 512 when the larger phase of a full tile
+    // divides evenly among them (the other phase may leave some idle), else
+    // 256.  The 32x32 tiles of small grids whose phases hold 512 and 256
+    // vectors (2- or 1-wide loads, 4-wide stores) ran 9-14% shorter on the
+    // GPU with 512 threads than with 256: the pages' 3-D example 3.88 ->
+    // 3.36 us, f32[300,334] and f32[1000,333] transposed 3.55 -> 3.22 and
+    // 3.77 -> 3.36 us (kernel trace).
     const long long lv = (long long)tu * (tw / vin), sv = (long long)tw * (tu / vout);
-    int tb = lv % 512 == 0 && sv % 512 == 0 ? 512 : 256;
+    int tb = std::max(lv, sv) % 512 == 0 ? 512 : 256;
     if (narrow && lv == 1024 && sv == 1024) tb = 1024;
     const int tblock = (int)env_ll("HF_TR_BLOCK", tb);
     P.ctx.push_back(ld);
