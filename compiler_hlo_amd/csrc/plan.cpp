@@ -802,7 +802,12 @@ Plan plan_reduce(const Graph &g) {
     long long pipe = 0;
     if (rr == 1 && tpr == block && kv % block == 0 && kv / block <= 8 && op != HF_REDUCER_ARGMAX)
       pipe = env_ll("HF_ROW_PIPE", 0) ? 1 : 0;
-    long long target = env_ll("HF_ROW_WGS", 8192);
+    // Whole-row workgroups: one per row step, up to 65536 (C3's 10,240 rows
+    // took 56.2 us in 10,240 workgroups against 57.2 us in 8192 that loop
+    // over the rows, the f32 row mean of 16,384 rows 38.7 against 39.2 us;
+    // 4096 or fewer workgroups lost 5-13% on C3).  Several rows per
+    // workgroup keep a grid-stride loop over 8192 workgroups.
+    long long target = env_ll("HF_ROW_WGS", tpr == block ? 65536 : 8192);
     P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb * rr), target));
     const long long pipe_k = ceil_div(J, P.grid);  // rows per workgroup
     if (pipe_k > 1024) pipe = 0;
