@@ -410,6 +410,24 @@ def test_row_reduce_full_every_row_and_layout_invariant():
     assert np.array_equal(got.view(np.uint32), got2.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows", [65536, 70001])
+def test_row_reduce_one_workgroup_per_row_and_past_the_cap(rows):
+    """Whole-row workgroups take one row each up to 65,536 workgroups; past
+    that the grid strides, so 70,001 rows leave 4,465 workgroups a second
+    row.  Integer-valued f32 rows of 512 (exact sums), bit-exact; a max over
+    the same rows through the same grid."""
+    say("row reduce rows", rows)
+    g = W.rng(54)
+    x = W.integers(g, rows * 512, -1000, 1000, np.int64).astype(np.float32)
+    for red, init in (("add", 0.0), ("max", float("-inf"))):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, 512])
+        s.reduce(p, [1], red, init, "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        assert f.plan()["hero"] == "row_reduce" and f.plan()["grid_blocks"] == 65536
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
 @pytest.mark.parametrize("d0,d2,d3", [(1, 5, 32768), (3, 3, 36864)])
 def test_row_reduce_two_rows_per_step(d0, d2, d3):
     """Rows of eight or more chunks per thread are reduced two per workgroup
