@@ -178,6 +178,42 @@ class Gen {
     return s.empty() ? "0" : s;
   }
 
+  // The condition under which a value read at index E is used.  pad and
+  // concatenate read their operands at a clamped index (hf_clampi(x, lo, hi),
+  // always in range) and select the operand's value only where the clamp
+  // leaves x unchanged: elsewhere the result is the padding value or another
+  // operand.  So a load whose index holds clamps is needed only where every
+  // one of them is the identity; this returns that conjunction ("" when the
+  // index holds no clamp).
+  static std::string clamp_guard(const Index &E) {
+    static const std::string key = "hf_clampi(";
+    std::string g;
+    for (const Term &t : E) {
+      if (t.k != Term::EXPR) continue;
+      for (size_t p = t.e.find(key); p != std::string::npos; p = t.e.find(key, p + 1)) {
+        // the three arguments, split at the commas of depth one
+        std::vector<std::string> arg(1);
+        int depth = 1;
+        size_t q = p + key.size();
+        for (; q < t.e.size() && depth > 0; ++q) {
+          const char ch = t.e[q];
+          if (ch == '(') ++depth;
+          if (ch == ')' && --depth == 0) break;
+          if (ch == ',' && depth == 1) arg.emplace_back();
+          else arg.back() += ch;
+        }
+        if (depth != 0 || arg.size() != 3) fail(HF_ERR_UNSUPPORTED, "codegen: unreadable clamp in an index");
+        for (std::string &a : arg) {
+          const size_t b0 = a.find_first_not_of(' '), b1 = a.find_last_not_of(' ');
+          a = b0 == std::string::npos ? a : a.substr(b0, b1 - b0 + 1);
+        }
+        if (!g.empty()) g += " && ";
+        g += "(" + arg[0] + ") >= (" + arg[1] + ") && (" + arg[0] + ") <= (" + arg[2] + ")";
+      }
+    }
+    return g;
+  }
+
   // Where a load goes: the fetch struct R (streaming operands; every load of
   // a hero that fetches whole steps ahead), the row-invariant struct I
   // (pipelined loop), or the compute function itself (small arrays, hoisted
@@ -243,17 +279,22 @@ class Gen {
     std::string m = dst.name;
     std::ostringstream &ld_os = dst.os;
     auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
+    const std::string guard = clamp_guard(E);
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
       decl(ctype(dt), 0);
-      ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
+      if (guard.empty()) ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
+      else ld_os << "  if (" << guard << ") " << m << " = " << ptr << "[" << off << "]; else " << m << " = 0;\n";
       b.os << "  { const " << reg << " s = " << elem_value(dt, m) << ";\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
     } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V * es >= 4 && E[ld].add % V == 0 &&
                E[ld].dyn.empty()) {  // contiguous and aligned: raw vector load
       const int nb = V * es;
       decl("hf_u32", nb / 4);
+      if (!guard.empty()) ld_os << "  if (" << guard << ")";
       ld_os << "  hf_raw_ld<" << nb << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off << ") * "
             << es << ", " << m << ");\n";
+      if (!guard.empty())
+        ld_os << "  else {\n#pragma unroll\n    for (int k = 0; k < " << nb / 4 << "; ++k) " << m << "[k] = 0u;\n  }\n";
       switch (dt) {
         case HF_F32: b.os << "  hf_unpack_f32<" << V << ">(" << m << ", " << v << ");\n"; break;
         case HF_S32: b.os << "  hf_unpack_i32<" << V << ">(" << m << ", " << v << ");\n"; break;
@@ -266,7 +307,8 @@ class Gen {
     } else {  // one load per lane
       decl(ctype(dt), V);
       ld_os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << m
-            << "[l] = " << ptr << "[o + l * " << st[ld] << "]; }\n";
+            << "[l] = " << (guard.empty() ? "" : "(" + guard + ") ? ") << ptr << "[o + l * " << st[ld] << "]"
+            << (guard.empty() ? "" : " : 0") << "; }\n";
       b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = "
            << elem_value(dt, m + "[l]") << ";\n";
     }
@@ -293,27 +335,34 @@ class Gen {
     std::ostringstream &ld_os = dst.os;
     auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
     const std::string bytes = "((const unsigned char *)" + ptr + ")";
+    const std::string guard = clamp_guard(E);
+    const std::string gq = guard.empty() ? "" : "(" + guard + ") ? ";
+    const std::string gz = guard.empty() ? "" : " : 0";
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
       decl("unsigned char", 0);
-      ld_os << "  " << m << " = " << bytes << "[(" << off << ") >> 1];\n";
+      ld_os << "  " << m << " = " << gq << bytes << "[(" << off << ") >> 1]" << gz << ";\n";
       b.os << "  { const int s = hf_nibble<" << sgn << ">(" << m << ", (" << off << ") & 1);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s; }\n";
     } else if (st[ld] == 1 && t.dims[ld] % V == 0 && V % 2 == 0 && E[ld].add % V == 0 && E[ld].dyn.empty()) {
       decl("hf_u32", (V + 7) / 8);
       if (V >= 8) {
+        if (!guard.empty()) ld_os << "  if (" << guard << ")";
         ld_os << "  hf_raw_ld<" << V / 2 << (stream && nt_loads_ ? ", true" : "") << ">(" << ptr << ", (long)(" << off
               << ") / 2, " << m << ");\n";
+        if (!guard.empty())
+          ld_os << "  else {\n#pragma unroll\n    for (int k = 0; k < " << (V / 2) / 4 << "; ++k) " << m
+                << "[k] = 0u;\n  }\n";
       } else {  // 2 or 4 elements: one byte or one aligned 16-bit word
         const char *w = V == 4 ? "unsigned short" : "unsigned char";
-        ld_os << "  " << m << "[0] = (hf_u32)*(const " << w << " *)((const unsigned char *)" << ptr << " + (long)(" << off
-              << ") / 2);\n";
+        ld_os << "  " << m << "[0] = " << gq << "(hf_u32)*(const " << w << " *)((const unsigned char *)" << ptr
+              << " + (long)(" << off << ") / 2)" << gz << ";\n";
       }
       b.os << "  { int s[" << V << "];\n    hf_unpack_n<" << V << ", " << sgn << ">(" << m << ", s);\n";
       b.os << "#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v << "[l] = s[l]; }\n";
     } else {  // one element per lane
       decl("unsigned char", V);
       ld_os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << m
-            << "[l] = " << bytes << "[(o + l * " << st[ld] << ") >> 1]; }\n";
+            << "[l] = " << gq << bytes << "[(o + l * " << st[ld] << ") >> 1]" << gz << "; }\n";
       b.os << "  { const int o = " << off << ";\n#pragma unroll\n    for (int l = 0; l < " << V << "; ++l) " << v
            << "[l] = hf_nibble<" << sgn << ">(" << m << "[l], (o + l * " << st[ld] << ") & 1); }\n";
     }
