@@ -495,7 +495,10 @@ Plan plan_loop(const Graph &g, Ctx c) {
   // quantization parameters, a broadcast bias) shares that column data among
   // the waves through L1, and each thread keeps it in registers over four
   // rows, whose loads it issues together.
-  const long long tpr_cap = env_ll("HF_LOOP_TPR", 64);
+  // (128 lanes for one element a lane: reverse and concatenate along the
+  // minor dim of f32[4096,4096] took 27.7 and 55.1 us against 29.4 and 59.2
+  // with 64.)
+  const long long tpr_cap = env_ll("HF_LOOP_TPR", V == 1 ? 128 : 64);
   if (cols_v >= tpr_cap) {
     tpr = tpr_cap;
     rpb = block / tpr;
@@ -524,6 +527,14 @@ Plan plan_loop(const Graph &g, Ctx c) {
   const bool pipe = (pipe_any && wbits_all == 8 && V * 8 == 128 && env_ll("HF_LOOP_PIPE", 1) > 0) ||
                     (pipe_any && std::getenv("HF_LOOP_PIPE") && env_ll("HF_LOOP_PIPE", 0) > 0);
   long long per = small ? 4 : 1;
+  // One element a lane (an index map that moves with the lane: reverse, pad
+  // or concatenate along the minor dim, or an odd minor dim): up to eight
+  // rows a thread, their loads issued together, while at least 1024
+  // workgroups remain.  With one row a thread, reverse, pad and
+  // concatenate along the minor dim of f32[4096,4096] ran at 3.1-3.5 TB/s;
+  // with eight, 4.6-4.9 TB/s (reverse 38.5 -> 27.7 us, concatenate of two
+  // 83.9 -> 55.1 us, with the 128-lane row segments above).
+  if (V == 1) per = std::max<long long>(per, std::min<long long>(8, nch * ceil_div(rows, rpb) / 1024));
   long long target = env_ll("HF_LOOP_WGS", nch * ceil_div(ceil_div(rows, rpb), per));
   if (pipe && !std::getenv("HF_LOOP_WGS"))
     target = nch * std::max(ceil_div(256, nch), ceil_div(ceil_div(rows, rpb), 16));
@@ -537,7 +548,7 @@ Plan plan_loop(const Graph &g, Ctx c) {
   P.empty = rt.numel() == 0;
   P.macros = {{"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", rows}, {"HF_COLS_V", cols_v},
               {"HF_TPR", tpr}, {"HF_RPB", rpb}, {"HF_NCH", nch},
-              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", small ? 4 : 2)},
+              {"HF_UNROLL", env_ll("HF_LOOP_UNROLL", V == 1 && per > 1 ? per : small ? 4 : 2)},
               {"HF_PIPE", pd}, {"HF_RSTEP", rstep}, {"HF_NR", nr}};
   P.info.vector_elems = V;
   P.info.elements = rt.numel();
