@@ -137,6 +137,7 @@ def workload_makers():
         "gelu_bf16": (W.gelu_bf16, {}, None),
         "transpose3d_exp_abs": (W.transpose3d_exp_abs, {}, None),
         "pad_reverse_concat_f32": (W.pad_reverse_concat_f32, {}, None),
+        "pad_reverse_concat_minor_f32": (W.pad_reverse_concat_minor_f32, {}, None),
         "quantized_add_i8": (W.quantized_add_i8, {}, None),
         "row_mean_f32": (W.row_mean_f32, {}, None),
         "argmax_rows_bf16": (W.argmax_rows_bf16, {}, None),
@@ -437,7 +438,7 @@ def main():
         others = ["copy_f32_4096x4096", "copy_bf16_64x512x1024", "loop_log_transpose_add",
                   "row_reduce_exp_add_bf16", "column_reduce_max_f32", "column_reduce_max_f32_colmajor",
                   "quant_dequant_bias_requant", "quant_dequant_bias_requant_s4", "gelu_bf16",
-                  "transpose3d_exp_abs", "pad_reverse_concat_f32",
+                  "transpose3d_exp_abs", "pad_reverse_concat_f32", "pad_reverse_concat_minor_f32",
                   "quantized_add_i8", "row_mean_f32", "argmax_rows_bf16"]
         for key in others:
             mk, kw, tr = makers[key]

@@ -1000,6 +1000,18 @@ def test_index_transforms_on_major_dims_vectorize():
     assert_bitexact(got, oracle.evaluate(s.nodes, [xs]), "f32")
 
 
+def test_pad_reverse_concat_minor_full():
+    """pad, reverse and concatenate along the minor dim (one element a lane,
+    eight rows a thread, loads guarded by the selects): small ragged shapes
+    and the benchmark's f32[4096, 2040 + 8 + 2048], whole output bit-exact."""
+    for dims in ((3, 5, 7), (37, 100, 64), (4096, 2040, 2048)):
+        say("pad reverse concat minor", dims)
+        spec, params, _ = W.pad_reverse_concat_minor_f32(*dims, seed=84 + dims[0] % 5)
+        got, f = run_gpu(spec.nodes, params)
+        assert f.plan()["hero"] == "loop"
+        assert_bitexact(got, oracle.evaluate(spec.nodes, params), "f32")
+
+
 # --------------------------------------------------------------------------
 # elementwise epilogues after a reduce
 # --------------------------------------------------------------------------

@@ -301,6 +301,24 @@ def pad_reverse_concat_f32(n0=4096, n1=4096, m0=2048, seed=9):
         "bytes": 4 * (n0 * n1 + m0 * n1 + (n0 + 2 + m0) * n1)}
 
 
+def pad_reverse_concat_minor_f32(n0=4096, n1=2040, m1=2048, seed=14):
+    """The same transforms along the minor dim: out = concatenate([pad(x,
+    low [0,4], high [0,4]), reverse(y, {1})], 1) with x f32[n0,n1], y
+    f32[n0,m1] ~ N(0,1), out f32[n0, n1 + 8 + m1] (every output element's
+    index map moves with the lane)."""
+    g = rng(seed)
+    s = Spec()
+    x = s.parameter(0, "f32", [n0, n1])
+    y = s.parameter(1, "f32", [n0, m1])
+    z = s.constant(0.0, "f32", [])
+    p = s.pad(x, z, [0, 4], [0, 4], [0, 0], "f32", [n0, n1 + 8])
+    r = s.reverse(y, [1], "f32", [n0, m1])
+    s.concatenate([p, r], 1, "f32", [n0, n1 + 8 + m1])
+    return s, [normal_f32(g, n0 * n1), normal_f32(g, n0 * m1)], {
+        "name": "pad_reverse_concat_minor_f32", "elements": n0 * (n1 + 8 + m1),
+        "bytes": 4 * (n0 * n1 + n0 * m1 + n0 * (n1 + 8 + m1))}
+
+
 def quantized_add_i8(r=4096, c=4096, seed=10):
     """out = add(a, b) on per-tensor quantized i8[r,c] tensors (scales 0.05 and
     0.02, zero points 3 and -7), quantized to scale 0.04, zero point 1."""
