@@ -260,6 +260,30 @@ class Gen {
     return -1;
   }
 
+  // s with every occurrence of the lane variable (the token i<lane>) replaced
+  // by (i<lane> + l): an index expression evaluated at lane l of a vector.
+  static std::string lane_sub(const std::string &s, int lane) {
+    if (lane < 0) return s;
+    const std::string v = "i" + std::to_string(lane);
+    std::string r;
+    size_t p = 0;
+    for (size_t q = s.find(v); q != std::string::npos; q = s.find(v, q + 1)) {
+      const size_t e = q + v.size();
+      if ((q > 0 && std::isalnum((unsigned char)s[q - 1])) || (e < s.size() && std::isdigit((unsigned char)s[e]))) continue;
+      r += s.substr(p, q - p) + "(" + v + " + l)";
+      p = e;
+    }
+    return r + s.substr(p);
+  }
+  // Whether an index expression of E uses the lane variable other than as a
+  // plain term of its own (then its lanes are read one by one).
+  static bool lane_in_expr(const Index &E, int lane) {
+    if (lane < 0) return false;
+    for (const Term &t : E)
+      if (t.k == Term::EXPR && lane_sub(t.e, lane) != t.e) return true;
+    return false;
+  }
+
   // Load of an array (parameter or per-axis quantization array) of element
   // type dt and shape t, at index E, into a new V-lane register array.  A
   // streaming operand's raw load goes to the fetch function (and the hero's
@@ -280,6 +304,16 @@ class Gen {
     std::ostringstream &ld_os = dst.os;
     auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
     const std::string guard = clamp_guard(E);
+    if (V > 1 && lane_in_expr(E, b.lane)) {  // each lane's element read on its own
+      decl(ctype(dt), V);
+      const std::string g = lane_sub(guard, b.lane);
+      ld_os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << m << "[l] = "
+            << (g.empty() ? "" : "(" + g + ") ? ") << ptr << "[" << lane_sub(off, b.lane) << "]"
+            << (g.empty() ? "" : " : 0") << ";\n";
+      b.os << "#pragma unroll\n  for (int l = 0; l < " << V << "; ++l) " << v << "[l] = "
+           << elem_value(dt, m + "[l]") << ";\n";
+      return v;
+    }
     if (ld < 0 || t.dims[ld] <= 1) {  // does not move with the lane
       decl(ctype(dt), 0);
       if (guard.empty()) ld_os << "  " << m << " = " << ptr << "[" << off << "];\n";
@@ -334,6 +368,7 @@ class Gen {
     std::string m = dst.name;
     std::ostringstream &ld_os = dst.os;
     auto decl = [&](const std::string &type, int count) { declare(b, dst, type, count); };
+    if (V > 1 && lane_in_expr(E, b.lane)) fail(HF_ERR_UNSUPPORTED, "codegen: a 4-bit array read lane by lane");
     const std::string bytes = "((const unsigned char *)" + ptr + ")";
     const std::string guard = clamp_guard(E);
     const std::string gq = guard.empty() ? "" : "(" + guard + ") ? ";
@@ -500,7 +535,7 @@ class Gen {
           break;
         case HF_IOTA: {  // the index along iota_dimension
           const Term &tm = E[nd.attr[0]];
-          const std::string i = term_str(tm) + (tm.k == Term::VAR && tm.var == b.lane ? " + l" : "");
+          const std::string i = b.V > 1 ? lane_sub(term_str(tm), b.lane) : term_str(tm);
           v = fresh(b, n);
           if (reg_is_float(t)) lanes(b, v, "float", rnd(t.dt, "(float)(" + i + ")"));
           else lanes(b, v, "int", i);
@@ -513,7 +548,8 @@ class Gen {
           for (int d = 0; d < r; ++d) {
             const long long lo = nd.attr[d], hi = nd.attr[r + d], step = nd.attr[2 * r + d] + 1;
             if (lo == 0 && hi == 0 && step == 1) continue;
-            const std::string k = "(" + term_str(E[d]) + " - (" + std::to_string(lo) + "))";
+            const std::string k = "(" + (b.V > 1 ? lane_sub(term_str(E[d]), b.lane) : term_str(E[d])) + " - (" +
+                                  std::to_string(lo) + "))";
             pred += std::string(pred.empty() ? "" : " && ") + "(" + k + " >= 0 && " + k + " % " +
                     std::to_string(step) + " == 0 && " + k + " / " + std::to_string(step) + " < " +
                     std::to_string(ot.dims[d]) + ")";
@@ -528,8 +564,9 @@ class Gen {
           long long off = 0;
           for (int o : nd.opd) end.push_back(off += g_.nodes[o].t.dims[cd]);
           std::string e = a.back() + "[l]";
+          const std::string ic = b.V > 1 ? lane_sub(term_str(E[cd]), b.lane) : term_str(E[cd]);
           for (int k = (int)a.size() - 2; k >= 0; --k)
-            e = "(" + term_str(E[cd]) + " < " + std::to_string(end[k]) + ") ? " + a[k] + "[l] : (" + e + ")";
+            e = "(" + ic + " < " + std::to_string(end[k]) + ") ? " + a[k] + "[l] : (" + e + ")";
           v = fresh(b, n);
           lanes(b, v, rtype(t), e);
           break;

@@ -463,7 +463,20 @@ Plan plan_loop(const Graph &g, Ctx c) {
     if (q.qdim >= 0) small = true;
   int V = 1;
   int wbits_all = 0;  // widest of the result and the streaming inputs, in bits
-  if (c.lane >= 0 && !c.general) {
+  // An index map that moves with the lane (reverse, pad, concatenate or a
+  // strided slice along the minor dim, a reshape that reorders it) still
+  // gets vector lanes when the context is one partition of whole-byte types
+  // with no per-axis arrays: each lane's element is then read on its own
+  // (the index evaluated at lane base + l), and the result is stored as one
+  // vector.
+  bool gather = c.lane >= 0 && c.general && c.part_root.size() <= 1 && !is_nibble(rt.dt) &&
+                env_ll("HF_LOOP_GATHER", 1) > 0;
+  for (auto &pr : c.param_reads)
+    if (is_nibble(g.nodes[pr.first].t.dt)) gather = false;
+  for (const Quant &q : g.quants)
+    if (q.qdim >= 0) gather = false;
+  c.gather = gather;
+  if (c.lane >= 0 && (!c.general || gather)) {
     // 128-bit lanes for the widest of the result and the streaming inputs,
     // except where every stream is 4-bit and column data is read: 32 elements
     // a lane then make few, register-heavy waves for what is mostly VALU work

@@ -38,7 +38,8 @@ Index identity_index(int rank);
 // (XLA:GPU Emitters, "Indexing transforms").  Sets *general when the map
 // changes how the lane variable `lane` moves through memory (a div/mod
 // reshape; reverse, pad or concatenate of the lane's dim; lane < 0: of any
-// dim): such a context runs one element per lane.
+// dim): such a context runs one element per lane, or, as a loop (Ctx::gather),
+// reads each lane's element on its own.
 Index operand_index(const Graph &g, int n, int k, const Index &E, bool *general, int lane = -1);
 
 // Physical stride (in elements) of every logical dim of t.
@@ -53,7 +54,8 @@ struct Ctx {
   int leaf = -1;
   int lane = -1;
   int V = 1;
-  bool general = false;                       // a div/mod reshape was met
+  bool general = false;                       // an index map moves with the lane (or a div/mod reshape was met)
+  bool gather = false;                        // general, yet V lanes: each lane's element read on its own
   std::vector<std::set<std::string>> maps;    // distinct index maps per node
   std::vector<char> in_ctx;
   std::vector<std::pair<int, Index>> param_reads;
