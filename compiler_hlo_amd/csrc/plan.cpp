@@ -856,8 +856,12 @@ Plan plan_reduce(const Graph &g) {
     int rl = block / cl;
     long long cb = (long long)cl * V;
     long long ncb = ceil_div(Cc, cb);
+    // Segments of at least 128 rows (16 a row lane, two batches of loads):
+    // with 4096 workgroups f32[4096,4096] got 32-row segments and took
+    // 19.8 us, with 128-row ones (1024 workgroups) 13.8 us; at 2048 and
+    // 8192 rows 128-row segments were also the fastest choice measured.
     long long target = env_ll("HF_COL_WGS", 4096);
-    long long segs = std::max<long long>(1, std::min(target / ncb, ceil_div(Rr, rl)));
+    long long segs = std::max<long long>(1, std::min(target / ncb, ceil_div(Rr, std::getenv("HF_COL_WGS") ? rl : 128)));
     long long rs = Rr > 0 ? ceil_div(Rr, segs) : 0;
     segs = rs > 0 ? ceil_div(Rr, rs) : 1;
     P.grid = ncb * segs;
