@@ -803,13 +803,20 @@ Plan plan_reduce(const Graph &g) {
     c.V = V;
     long long kv = K / V;
     int block, tpr;
-    if (kv >= 64) {
+    const long long wave_rows = env_ll("HF_ROW_WAVE_ROWS", 256);
+    if (kv >= wave_rows || (kv >= 64 && std::getenv("HF_ROW_BLOCK"))) {
       // 512 threads per row; 256 for max/argmax, whose per-row finish (a
       // pair reduction and a serial combine over the waves) weighs more
       // (measured 71% -> 80% of peak on bf16[8192,8192]; the float paths
       // lost 1-20% at 256)
       block = (int)std::min<long long>(env_ll("HF_ROW_BLOCK", op == HF_REDUCER_ARGMAX ? 256 : 512), pow2_floor(kv));
       tpr = block;
+    } else if (kv >= 64) {
+      // rows of 64 to 255 vectors: one wave per row, four rows per
+      // workgroup (a row per workgroup of one or two waves left the
+      // workgroups too small)
+      block = 256;
+      tpr = 64;
     } else {
       block = 256;
       tpr = pow2_ceil(std::max<long long>(1, kv));
@@ -862,6 +869,10 @@ Plan plan_reduce(const Graph &g) {
     // 8192 rows 128-row segments were also the fastest choice measured.
     long long target = env_ll("HF_COL_WGS", 4096);
     long long segs = std::max<long long>(1, std::min(target / ncb, ceil_div(Rr, std::getenv("HF_COL_WGS") ? rl : 128)));
+    // At most 256 segments: the fold reads every segment of a column, and a
+    // few narrow columns over many rows otherwise got thousands of them
+    // (f32[1048576,16] 29.3 -> 14.0 us, f32[262144,64] 21.3 -> 13.8 us).
+    if (!std::getenv("HF_COL_WGS")) segs = std::min<long long>(segs, 256);
     long long rs = Rr > 0 ? ceil_div(Rr, segs) : 0;
     segs = rs > 0 ? ceil_div(Rr, rs) : 1;
     P.grid = ncb * segs;

@@ -414,18 +414,40 @@ def test_row_reduce_full_every_row_and_layout_invariant():
 def test_row_reduce_one_workgroup_per_row_and_past_the_cap(rows):
     """Whole-row workgroups take one row each up to 65,536 workgroups; past
     that the grid strides, so 70,001 rows leave 4,465 workgroups a second
-    row.  Integer-valued f32 rows of 512 (exact sums), bit-exact; a max over
+    row.  Integer-valued f32 rows of 1024 (exact sums), bit-exact; a max over
     the same rows through the same grid."""
     say("row reduce rows", rows)
     g = W.rng(54)
-    x = W.integers(g, rows * 512, -1000, 1000, np.int64).astype(np.float32)
+    x = W.integers(g, rows * 1024, -1000, 1000, np.int64).astype(np.float32)
     for red, init in (("add", 0.0), ("max", float("-inf"))):
         s = W.Spec()
-        p = s.parameter(0, "f32", [rows, 512])
+        p = s.parameter(0, "f32", [rows, 1024])
         s.reduce(p, [1], red, init, "f32", [rows])
         got, f = run_gpu(s.nodes, [x])
         assert f.plan()["hero"] == "row_reduce" and f.plan()["grid_blocks"] == 65536
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+
+
+@pytest.mark.parametrize("rows,cols", [(70001, 256), (4099, 512), (37, 1020), (8, 1024)])
+def test_row_reduce_one_wave_per_row(rows, cols):
+    """Rows of 64 to 255 vectors take one wave each, four rows a workgroup,
+    over at most 8192 workgroups (a grid stride past them; a last step with
+    fewer rows than its four slots): sum, max and argmax of integer-valued
+    f32 (exact, with many ties), bit-exact."""
+    say("row reduce one wave per row", rows, cols)
+    g = W.rng(55 + cols % 7)
+    x = W.integers(g, rows * cols, -20, 20, np.int64).astype(np.float32)
+    for red in ("add", "max", "argmax"):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, cols])
+        if red == "argmax":
+            s.argmax(p, 1, [rows, cols])
+        else:
+            s.reduce(p, [1], red, 0.0 if red == "add" else float("-inf"), "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        if cols // 4 < 256:
+            assert f.plan()["block_threads"] == 256 and "#define HF_TPR 64" in f.source()
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32" if red == "argmax" else "f32")
 
 
 @pytest.mark.parametrize("d0,d2,d3", [(1, 5, 32768), (3, 3, 36864)])
