@@ -11,15 +11,95 @@
 // along the rows) is loop-invariant across rows.
 // HF_TPR < 64: short rows; HF_BLOCK/HF_TPR rows per workgroup step, reduced
 // within lane groups by cross-lane shuffles.
+// HF_RSEG > 1: a few long rows; each row splits into HF_RSEG segments of
+// HF_SEGKV vectors, one per workgroup step.  Each workgroup writes its
+// segment's partial to the workspace ([HF_RSEG][HF_ROWS] values, then as
+// many indices for max/argmax), and the fold kernel (HF_FOLD_NAME, launched
+// next on the same stream) combines each row's partials in segment order.
 //
 // Provided by the generated code: HF_OP, HF_BLOCK, HF_V, HF_ROWS, HF_KV
-// (vectors per row), HF_TPR, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
+// (vectors per row), HF_TPR, HF_RSEG, HF_SEGKV, hf_regs_t, hf_rr_eval_fetch(A, row, kv, R),
 // hf_rr_eval(A, row, kv, R, x) (HF_V floats), hf_rr_store(A, row, acc); for max/argmax
 // (HF_OP 3) HF_ARG_V0 and hf_rr_store_arg(A, row, index) (which writes the
 // index init where the index is still HF_ARG_NONE).
 extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_PARAMS) {
   const HfArgs A = HF_ARGS_INIT;
+#if HF_RSEG > 1
+  {
+    constexpr int NB = 8;  // loads in flight per thread
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #if HF_OP == 3
+    __shared__ float sm[HF_BLOCK / 64];
+    __shared__ int sk[HF_BLOCK / 64];
+#else
+    __shared__ float sp[HF_BLOCK / 64];
+#endif
+    for (int w = blockIdx.x; w < HF_ROWS * HF_RSEG; w += gridDim.x) {
+      const int row = w / HF_RSEG, seg = w % HF_RSEG;
+      const int kv0 = seg * HF_SEGKV;
+      const int kv1 = kv0 + HF_SEGKV < HF_KV ? kv0 + HF_SEGKV : HF_KV;
+#if HF_OP == 3
+      float m = HF_ARG_V0;
+      int k = HF_ARG_NONE;
+#else
+      float acc[HF_V];
+#pragma unroll
+      for (int v = 0; v < HF_V; ++v) acc[v] = hf_red_identity<HF_OP>();
+#endif
+      for (int base = kv0; base < kv1; base += NB * HF_BLOCK) {
+        hf_regs_t R[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int kv = base + b * HF_BLOCK + (int)threadIdx.x;
+          if (kv < kv1) hf_rr_eval_fetch(A, row, kv, R[b]);
+        }
+        HF_LOADS_ISSUED();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int kv = base + b * HF_BLOCK + (int)threadIdx.x;
+          if (kv < kv1) {
+            float x[HF_V];
+            hf_rr_eval(A, row, kv, R[b], x);
+#pragma unroll
+            for (int v = 0; v < HF_V; ++v) {
+#if HF_OP == 3
+              hf_arg_step(m, k, x[v], kv * HF_V + v);
+#else
+              acc[v] = hf_red<HF_OP>(acc[v], x[v]);
+#endif
+            }
+          }
+        }
+      }
+#if HF_OP == 3
+      hf_arg_wave_reduce(m, k);
+      if (lane == 0) {
+        sm[wave] = m;
+        sk[wave] = k;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        for (int q = 1; q < HF_BLOCK / 64; ++q) hf_arg_combine(m, k, sm[q], sk[q]);
+        ((float *)A.ws)[(long)seg * HF_ROWS + row] = m;
+        ((int *)A.ws)[(long)HF_RSEG * HF_ROWS + (long)seg * HF_ROWS + row] = k;
+      }
+#else
+      float s = acc[0];
+#pragma unroll
+      for (int v = 1; v < HF_V; ++v) s = hf_red<HF_OP>(s, acc[v]);
+      s = hf_wave_reduce<HF_OP>(s);
+      if (lane == 0) sp[wave] = s;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float t = sp[0];
+        for (int q = 1; q < HF_BLOCK / 64; ++q) t = hf_red<HF_OP>(t, sp[q]);
+        ((float *)A.ws)[(long)seg * HF_ROWS + row] = t;
+      }
+#endif
+      __syncthreads();  // the partials' LDS slots are reused next step
+    }
+  }
+#elif HF_OP == 3
   // max/argmax: the index of element (row, kv, v) along the reduced dim is
   // kv * HF_V + v; each lane visits its elements in increasing index order.
   constexpr int RPB = HF_BLOCK / HF_TPR;
@@ -256,5 +336,45 @@ extern "C" __global__ __launch_bounds__(HF_BLOCK) void HF_KERNEL_NAME(HF_KERNEL_
     if (sub == 0 && row < HF_ROWS) hf_rr_store(A, row, s);
   }
 #endif
-#endif  // HF_OP == 3
+#endif  // HF_RSEG > 1, HF_OP == 3
 }
+
+#if HF_RSEG > 1
+// The fold: one workgroup per row.  Thread t combines the row's partials of
+// segments t, t + 256, ... in order; the waves reduce theirs with DPP and
+// thread 0 combines the four waves in order, then applies the reduce's init
+// and epilogue (hf_rr_store).  A fixed tree: the same result every launch.
+extern "C" __global__ __launch_bounds__(256) void HF_FOLD_NAME(HF_KERNEL_PARAMS) {
+  const HfArgs A = HF_ARGS_INIT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+#if HF_OP == 3
+  __shared__ float pm[4];
+  __shared__ int pk[4];
+  float m = HF_ARG_V0;
+  int k = HF_ARG_NONE;
+  for (int q = threadIdx.x; q < HF_RSEG; q += 256)
+    hf_arg_combine(m, k, ((const float *)A.ws)[(long)q * HF_ROWS + row],
+                   ((const int *)A.ws)[(long)HF_RSEG * HF_ROWS + (long)q * HF_ROWS + row]);
+  hf_arg_wave_reduce(m, k);
+  if (lane == 0) {
+    pm[wave] = m;
+    pk[wave] = k;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) hf_arg_combine(m, k, pm[w], pk[w]);
+    hf_rr_store_arg(A, row, k);
+  }
+#else
+  __shared__ float part[4];
+  float s = hf_red_identity<HF_OP>();
+  for (int q = threadIdx.x; q < HF_RSEG; q += 256) s = hf_red<HF_OP>(s, ((const float *)A.ws)[(long)q * HF_ROWS + row]);
+  s = hf_wave_reduce<HF_OP>(s);
+  if (lane == 0) part[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    hf_rr_store(A, row, hf_red<HF_OP>(hf_red<HF_OP>(part[0], part[1]), hf_red<HF_OP>(part[2], part[3])));
+#endif
+}
+#endif

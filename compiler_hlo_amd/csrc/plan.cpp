@@ -822,13 +822,31 @@ Plan plan_reduce(const Graph &g) {
       tpr = pow2_ceil(std::max<long long>(1, kv));
     }
     long long rpb = tpr == block ? 1 : block / tpr;
+    // A few long rows: each row splits into segments of at least eight
+    // chunks a thread (one batch of loads), one segment per workgroup, so
+    // that about 2048 workgroups run; a fold kernel then combines each row's
+    // partials in segment order.  f32[16,1048576] summed in 141 us with one
+    // workgroup per row (8 workgroups, two rows each).
+    long long segs = 1, segkv = kv;
+    if (tpr == block && env_ll("HF_ROW_SEGS", 1) > 0) {
+      const long long want = ceil_div(2048, std::max<long long>(J, 1));
+      segs = std::min(want, kv / ((long long)block * 8));
+      if (segs >= 2) {
+        segkv = ceil_div(ceil_div(kv, segs), (long long)block) * block;
+        segs = ceil_div(kv, segkv);
+      }
+      if (segs < 2) {
+        segs = 1;
+        segkv = kv;
+      }
+    }
     // Whole-row workgroups whose rows split into equal chunks take several
     // rows per step: their loads go out together, and what the prologue reads
     // along the row (a broadcast bias) is loaded once for all of them.
     // Two rows per step for rows of eight or more chunks per thread (measured
     // faster there; shorter rows gained nothing or lost).
     long long rr = 1;
-    if (tpr == block && kv % block == 0 && op != HF_REDUCER_ARGMAX)
+    if (segs == 1 && tpr == block && kv % block == 0 && op != HF_REDUCER_ARGMAX)
       rr = std::max<long long>(1, std::min<long long>(env_ll("HF_ROW_RPS", kv / block >= 8 ? 2 : 1), 4));
     long long pipe = 0;
     if (rr == 1 && tpr == block && kv % block == 0 && kv / block <= 8 && op != HF_REDUCER_ARGMAX)
@@ -839,14 +857,18 @@ Plan plan_reduce(const Graph &g) {
     // 4096 or fewer workgroups lost 5-13% on C3).  Several rows per
     // workgroup keep a grid-stride loop over 8192 workgroups.
     long long target = env_ll("HF_ROW_WGS", tpr == block ? 65536 : 8192);
-    P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb * rr), target));
+    P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb * rr) * segs, target));
     const long long pipe_k = ceil_div(J, P.grid);  // rows per workgroup
-    if (pipe_k > 1024) pipe = 0;
+    if (pipe_k > 1024 || segs > 1) pipe = 0;
     P.block = block;
     P.lds_bytes = tpr == block ? (block / 64) * 8 * (int)rr : 0;
+    if (segs > 1) {
+      P.ws_bytes = J * segs * (op == HF_REDUCER_ARGMAX ? 8 : 4);  // max/argmax: value and index
+      P.fold_grid = J;  // one fold workgroup per row
+    }
     P.macros = {{"HF_OP", op}, {"HF_BLOCK", block}, {"HF_V", V}, {"HF_ROWS", J},
                 {"HF_KV", kv}, {"HF_TPR", tpr}, {"HF_RR_ROWS", rr}, {"HF_RR_PIPE", pipe},
-                {"HF_RR_PIPE_K", std::max<long long>(1, pipe_k)}};
+                {"HF_RR_PIPE_K", std::max<long long>(1, pipe_k)}, {"HF_RSEG", segs}, {"HF_SEGKV", segkv}};
     P.info.vector_elems = V;
     P.info.rows = J;
     P.info.cols = K;

@@ -428,6 +428,56 @@ def test_row_reduce_one_workgroup_per_row_and_past_the_cap(rows):
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 1 << 20), (1, 3 * (1 << 20) + 4), (5, 100003), (3, 1 << 22)])
+def test_row_reduce_split_rows(rows, cols):
+    """A few long rows split over workgroups, each a segment of the row, and
+    a fold kernel that combines each row's partials in order: sum, max and
+    argmax of integer-valued f32 (exact, many ties and equal maxima in
+    different segments), bit-exact; an odd row length (one element a lane,
+    ragged last segment); a mean (the epilogue after the fold); and a second
+    launch of the same handle with new values (the workspace is rewritten)."""
+    say("row reduce split rows", rows, cols)
+    g = W.rng(56 + rows)
+    x = W.integers(g, rows * cols, -50, 50, np.int64).astype(np.float32)
+    for red in ("add", "max", "argmax"):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, cols])
+        if red == "argmax":
+            s.argmax(p, 1, [rows, cols])
+        else:
+            s.reduce(p, [1], red, 0.0 if red == "add" else float("-inf"), "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        assert "#define HF_RSEG 1\n" not in f.source() and f.plan()["workspace_bytes"] > 0
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32" if red == "argmax" else "f32")
+        if red == "argmax":
+            x2 = x.copy()
+            x2[::7] = 49.0  # new maxima, in every segment
+            got2, _ = run_gpu(s.nodes, [x2], fusion=f)
+            assert_bitexact(got2, oracle.evaluate(s.nodes, [x2]), "s32")
+    y = W.normal_f32(g, rows * cols)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [rows, cols])
+    r = s.reduce(p, [1], "add", 0.0, "f32", [rows])
+    s.binary("divide", r, s.constant(float(cols), "f32", [rows]), "f32", [rows])
+    got, f = run_gpu(s.nodes, [y])
+    want = np.asarray(oracle.evaluate(s.nodes, [y]), np.float64)
+    bound = 1e-5 * np.abs(y.reshape(rows, cols)).astype(np.float64).sum(1) / cols + np.spacing(np.abs(want).astype(np.float32))
+    assert (np.abs(np.asarray(got, np.float64) - want) <= bound).all()
+
+
+def test_reduce_of_every_dim_splits_its_one_row():
+    """A reduce over every dim of f32[4096,4096] (one output, one row of
+    16.8 M elements): 1024 segments and the fold; integer values, exact."""
+    g = W.rng(57)
+    x = W.integers(g, 4096 * 4096, -8, 8, np.int64).astype(np.float32)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4096, 4096])
+    s.reduce(p, [0, 1], "add", 0.0, "f32", [])
+    got, f = run_gpu(s.nodes, [x])
+    assert f.plan()["hero"] == "row_reduce" and f.plan()["grid_blocks"] >= 1024
+    assert got.reshape(-1)[0] == np.float32(x.astype(np.float64).sum())
+
+
 @pytest.mark.parametrize("rows,cols", [(70001, 256), (4099, 512), (37, 1020), (8, 1024)])
 def test_row_reduce_one_wave_per_row(rows, cols):
     """Rows of 64 to 255 vectors take one wave each, four rows a workgroup,
