@@ -300,9 +300,10 @@ hf_status hf_fusion_source(const hf_fusion *f, char *buf, size_t cap, size_t *le
  * device buffer of at least hf_plan_info.workspace_bytes bytes, 16-byte
  * aligned, overlapping neither the result nor a parameter.  Its contents on
  * entry do not matter and are undefined afterwards.  It may be NULL when
- * workspace_bytes is 0 (every plan except a column reduce whose reduced
- * extent is split into several segments).  Two launches in flight at the same
- * time need two workspaces.
+ * workspace_bytes is 0 (every plan except a reduce whose reduced extent is
+ * split into several segments: a column reduce over many rows, a row reduce
+ * of a few long rows).  Two launches in flight at the same time need two
+ * workspaces.
  *
  * stream is a hipStream_t (NULL = the null stream).  The launch is
  * asynchronous and allocates nothing; a fault inside the kernel surfaces at
