@@ -880,7 +880,10 @@ Plan plan_reduce(const Graph &g) {
     long long Cc = J, Rr = K;
     // 32 column lanes: 128-bit lanes over 512-byte row segments, 8 row lanes
     // (measured 73% -> 76% of peak on f32[16384,4096] against 64 lanes)
-    int cl = (int)std::min<long long>(env_ll("HF_COL_CL", 32), pow2_ceil(ceil_div(Cc, V)));
+    // (16 column lanes for 2048 columns or fewer: f32[16384,1024] took
+    // 18.9 us with 32 lanes (128-row segments) and 13.7 with 16, and
+    // f32[8192,2048] 14.1 against 13.7; 32 lanes stay for wider arrays.)
+    int cl = (int)std::min<long long>(env_ll("HF_COL_CL", Cc <= 2048 ? 16 : 32), pow2_ceil(ceil_div(Cc, V)));
     int block = 256;
     int rl = block / cl;
     long long cb = (long long)cl * V;
