@@ -682,7 +682,11 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // bits (and so their HBM channels); a diagonal order then spreads both.
     // Input rows that are not whole 128-byte lines share their edge lines
     // between W-neighbouring tiles: those go to one XCD (order 3).
-    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0 ? 3 : in_row_bytes >= 8192 ? 2 : 0);
+    // (Rows of 32 KiB or more go back to U fastest: f32[1024,16384] took
+    // 27.5 us diagonal and 24.8 U fastest, f32[256,65536] 25.6 and 23.7.)
+    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0                          ? 3
+                                                  : in_row_bytes >= 8192 && in_row_bytes < 32768 ? 2
+                                                                                                 : 0);
     // Threads per tile: one 128-bit vector per thread and phase for the
     // narrow tiles above; otherwise 512 when the larger phase of a full tile
     // divides evenly among them (the other phase may leave some idle), else
