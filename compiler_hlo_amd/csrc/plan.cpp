@@ -656,11 +656,18 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // phase (1024 threads), measured 68% -> 72% of peak on f32[4096,4096]
     // and 68% -> 71% on f32[8192,2048]; other strides and 2-byte types keep
     // 64x64 (the narrow tile lost 2% on f32[4160,4160] and more on bf16).
-    const bool pow2_rows = in_row_bytes >= 8192 && (in_row_bytes & (in_row_bytes - 1)) == 0;
-    const bool narrow = pow2_rows && vin == 4 && vout == 4;
+    // Shorter power-of-two rows (512 B to 4 KiB) take it too when it makes
+    // 2048 workgroups or more: f32[65536,256] 26.6 -> 24.2 us,
+    // f32[131072,128] 28.6 -> 24.2, f32[32768,1024] 54.0 -> 46.8; rows of
+    // 2 KiB tie or lose a little (f32[32768,512] 23.9 -> 24.0 us,
+    // f32[16384,512] 13.0 -> 13.2), and f32[4096,1024], a grid of 1024, ran
+    // 7.7 us with 64x64 tiles and 7.9 narrow.
+    const long long nb = rt.numel() / (DU * DW);
+    const bool pow2_rows = in_row_bytes >= 512 && (in_row_bytes & (in_row_bytes - 1)) == 0;
+    const bool narrow = pow2_rows && vin == 4 && vout == 4 &&
+                        (in_row_bytes >= 8192 || nb * ceil_div(DU, 32) * ceil_div(DW, 128) >= 2048);
     int tu = (int)std::min<long long>(env_ll("HF_TR_TU", narrow ? 32 : 64), pow2_ceil(DU));
     int tw = (int)std::min<long long>(env_ll("HF_TR_TW", narrow ? 128 : 64), pow2_ceil(DW));
-    long long nb = rt.numel() / (DU * DW);
     // A tiling that would leave fewer than two workgroups per CU (256 CUs)
     // takes the pages' 32x32 tile instead: abs(transpose(exp x, {2,1,0})) on
     // f32[20,160,170] ran 4.70 us with 64x64 tiles (150 workgroups) and
@@ -679,14 +686,19 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // Tile order.  U-tiles fastest keeps the writes of concurrent workgroups
     // spread over the output.  When the input rows of a tile lie 8 KiB or
     // more apart, the reads of U-consecutive tiles share their low address
-    // bits (and so their HBM channels); a diagonal order then spreads both.
-    // Input rows that are not whole 128-byte lines share their edge lines
-    // between W-neighbouring tiles: those go to one XCD (order 3).
-    // (Rows of 32 KiB or more go back to U fastest: f32[1024,16384] took
-    // 27.5 us diagonal and 24.8 U fastest, f32[256,65536] 25.6 and 23.7.)
-    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0                          ? 3
-                                                  : in_row_bytes >= 8192 && in_row_bytes < 32768 ? 2
-                                                                                                 : 0);
+    // bits (and so their HBM channels); a diagonal order then spreads both,
+    // as long as there are at least half as many U-tiles as W-tiles.  With
+    // fewer, the U shift repeats within the W-tiles that run together, and
+    // their writes share channels: U fastest again (f32[1024,16384] 27.5 us
+    // diagonal, 24.8 U fastest; f32[2048,16384], with twice the U-tiles,
+    // 47.6 and 53.2).  Narrow tiles on 4 KiB rows run W fastest
+    // (f32[16384,1024] 24.1 us against 25.7).  Input rows that are not whole
+    // 128-byte lines share their edge lines between W-neighbouring tiles:
+    // those go to one XCD (order 3).
+    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0   ? 3
+                                                  : in_row_bytes >= 8192    ? (ntw <= 2 * ntu ? 2 : 0)
+                                                  : narrow && in_row_bytes == 4096 ? 1
+                                                                                   : 0);
     // Threads per tile: one 128-bit vector per thread and phase for the
     // narrow tiles above; otherwise 512 when the larger phase of a full tile
     // divides evenly among them (the other phase may leave some idle), else

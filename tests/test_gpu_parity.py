@@ -288,14 +288,25 @@ def test_transpose_exp_small(n0, n1):
 
 @pytest.mark.parametrize("dims,perm,tile,block", [([100, 2048], [1, 0], (128, 32), 1024),
                                                   ([3, 36, 4096], [0, 2, 1], (128, 32), 1024),
-                                                  ([8, 2048], [1, 0], (128, 8), 256)])
+                                                  ([8, 2048], [1, 0], (128, 8), 256),
+                                                  ([16380, 1024], [1, 0], (128, 32), 1024),
+                                                  ([65536, 256], [1, 0], (128, 32), 1024),
+                                                  ([8, 4100, 256], [0, 2, 1], (128, 32), 1024),
+                                                  ([2052, 8192], [1, 0], (128, 32), 1024),
+                                                  ([1000, 32768], [1, 0], (128, 32), 1024),
+                                                  ([1000, 1024], [1, 0], (32, 32), 256)])
 def test_transpose_narrow_tiles(dims, perm, tile, block):
     """f32 transposes whose input rows lie a power of two (>= 8 KiB) apart take
     tiles 128 wide in the load and up to 32 in the store, with 1024 threads
-    when each thread then moves one vector per phase.  Ragged U extents (100,
-    36) take the bounds-checked path.  The exp before the tile is checked
-    against the oracle and bitwise against the same exp through the loop hero,
-    transposed on the host."""
+    when each thread then moves one vector per phase; rows of 512 B to 4 KiB
+    do too when that makes 2048 workgroups or more (f32[1000,1024] would make
+    256 and takes 32x32 tiles).  The tile orders run here: W fastest (4 KiB
+    rows), diagonal (f32[2052,8192]), U fastest (f32[65536,256],
+    f32[1000,32768]).
+    Ragged U extents (100, 36, 16380, 4100, 2052, 1000) take the
+    bounds-checked path.  The exp before the tile is checked against the
+    oracle and bitwise against the same exp through the loop hero, transposed
+    on the host."""
     say("transpose narrow tiles", dims, perm)
     n = int(np.prod(dims))
     out_dims = [dims[p] for p in perm]
