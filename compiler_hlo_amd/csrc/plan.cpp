@@ -871,8 +871,11 @@ Plan plan_reduce(const Graph &g) {
     // took 56.2 us in 10,240 workgroups against 57.2 us in 8192 that loop
     // over the rows, the f32 row mean of 16,384 rows 38.7 against 39.2 us;
     // 4096 or fewer workgroups lost 5-13% on C3).  Several rows per
-    // workgroup keep a grid-stride loop over 8192 workgroups.
-    long long target = env_ll("HF_ROW_WGS", tpr == block ? 65536 : 8192);
+    // workgroup keep a grid-stride loop over 2048 workgroups of 256 threads,
+    // one full round of 32 waves on each of the 256 CUs: summing rows of 16
+    // to 512 f32 (64 MiB) took 11.4-12.0 us there against 12.9-13.5 with
+    // 8192 workgroups and 11.9-12.3 with 4096 (3072: 12.2-13.1 us).
+    long long target = env_ll("HF_ROW_WGS", tpr == block ? 65536 : 2048);
     P.grid = std::max<long long>(1, std::min(ceil_div(J, rpb * rr) * segs, target));
     const long long pipe_k = ceil_div(J, P.grid);  // rows per workgroup
     if (pipe_k > 1024 || segs > 1) pipe = 0;

@@ -492,7 +492,7 @@ def test_reduce_of_every_dim_splits_its_one_row():
 @pytest.mark.parametrize("rows,cols", [(70001, 256), (4099, 512), (37, 1020), (8, 1024)])
 def test_row_reduce_one_wave_per_row(rows, cols):
     """Rows of 64 to 255 vectors take one wave each, four rows a workgroup,
-    over at most 8192 workgroups (a grid stride past them; a last step with
+    over at most 2048 workgroups (a grid stride past them; a last step with
     fewer rows than its four slots): sum, max and argmax of integer-valued
     f32 (exact, with many ties), bit-exact."""
     say("row reduce one wave per row", rows, cols)
@@ -508,6 +508,27 @@ def test_row_reduce_one_wave_per_row(rows, cols):
         got, f = run_gpu(s.nodes, [x])
         if cols // 4 < 256:
             assert f.plan()["block_threads"] == 256 and "#define HF_TPR 64" in f.source()
+        assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32" if red == "argmax" else "f32")
+
+
+@pytest.mark.parametrize("rows,cols", [(262147, 64), (1048583, 16), (300001, 12)])
+def test_row_reduce_many_short_rows(rows, cols):
+    """Rows of fewer than 64 vectors share a wave (16, 4 and 3 vectors a
+    row: 16, 64 and 64 rows a workgroup) over 2048 workgroups, each looping
+    over 2 to 9 steps of rows, the last one partly empty: sum, max and argmax
+    of integer-valued f32 (exact, with many ties), bit-exact."""
+    say("row reduce many short rows", rows, cols)
+    g = W.rng(57 + cols)
+    x = W.integers(g, rows * cols, -20, 20, np.int64).astype(np.float32)
+    for red in ("add", "max", "argmax"):
+        s = W.Spec()
+        p = s.parameter(0, "f32", [rows, cols])
+        if red == "argmax":
+            s.argmax(p, 1, [rows, cols])
+        else:
+            s.reduce(p, [1], red, 0.0 if red == "add" else float("-inf"), "f32", [rows])
+        got, f = run_gpu(s.nodes, [x])
+        assert f.plan()["hero"] == "row_reduce" and f.plan()["grid_blocks"] == 2048
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32" if red == "argmax" else "f32")
 
 
