@@ -684,20 +684,21 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     long long ntu = ceil_div(DU, tu), ntw = ceil_div(DW, tw);
     int pitch = tu + 1;
     // Tile order.  U-tiles fastest keeps the writes of concurrent workgroups
-    // spread over the output.  When the input rows of a tile lie 8 KiB or
+    // spread over the output.  When the input rows of a tile lie 4 KiB or
     // more apart, the reads of U-consecutive tiles share their low address
     // bits (and so their HBM channels); a diagonal order then spreads both,
     // as long as there are at least half as many U-tiles as W-tiles.  With
     // fewer, the U shift repeats within the W-tiles that run together, and
     // their writes share channels: U fastest again (f32[1024,16384] 27.5 us
     // diagonal, 24.8 U fastest; f32[2048,16384], with twice the U-tiles,
-    // 47.6 and 53.2).  Narrow tiles on 4 KiB rows run W fastest
-    // (f32[16384,1024] 24.1 us against 25.7).  Input rows that are not whole
-    // 128-byte lines share their edge lines between W-neighbouring tiles:
-    // those go to one XCD (order 3).
-    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0   ? 3
-                                                  : in_row_bytes >= 8192    ? (ntw <= 2 * ntu ? 2 : 0)
+    // 47.6 and 53.2).  (Rows of 4 KiB: bf16[16384,2048] took 28.0 us U
+    // fastest and 24.4 diagonal.)  Narrow tiles on 4 KiB rows run W fastest
+    // (f32[16384,1024] 24.1 us against 24.4 diagonal).  Input rows that are
+    // not whole 128-byte lines share their edge lines between
+    // W-neighbouring tiles: those go to one XCD (order 3).
+    const long long order = env_ll("HF_TR_ORDER", in_row_bytes % 128 != 0          ? 3
                                                   : narrow && in_row_bytes == 4096 ? 1
+                                                  : in_row_bytes >= 4096           ? (ntw <= 2 * ntu ? 2 : 0)
                                                                                    : 0);
     // Threads per tile: one 128-bit vector per thread and phase for the
     // narrow tiles above; otherwise 512 when the larger phase of a full tile
