@@ -630,6 +630,57 @@ def test_transpose_tile_arithmetic_of_the_pages_example():
     assert p["cols"] == 3200 and p["grid_blocks"] == -(-3200 // 32) * -(-170 // 32) == 600
 
 
+# (dtype, input dims, permutation) -> (TU, TW, threads, tile order)
+# order: 0 U-tiles fastest, 1 W-tiles fastest, 2 diagonal, 3 XCD-contiguous
+TRANSPOSE_GEOMETRY = [
+    ("f32", [4096, 4096], [1, 0], (32, 128, 1024, 2)),     # 16 KiB rows: narrow, diagonal
+    ("f32", [1024, 16384], [1, 0], (32, 128, 1024, 0)),    # 128 W-tiles, 32 U-tiles: U fastest
+    ("f32", [2048, 16384], [1, 0], (32, 128, 1024, 2)),    # 128 W-tiles, 64 U-tiles: diagonal
+    ("f32", [16384, 1024], [1, 0], (32, 128, 1024, 1)),    # narrow on 4 KiB rows: W fastest
+    ("f32", [65536, 256], [1, 0], (32, 128, 1024, 0)),     # narrow on 1 KiB rows
+    ("f32", [32768, 512], [1, 0], (32, 128, 1024, 0)),
+    ("f32", [4096, 1024], [1, 0], (64, 64, 512, 2)),       # narrow would make 1024 WGs
+    ("f32", [4160, 4160], [1, 0], (64, 64, 512, 2)),       # not a power of two
+    ("f32", [20, 160, 170], [2, 1, 0], (32, 32, 512, 3)),  # rows of 680 B; small grid
+    ("bf16", [16384, 2048], [1, 0], (64, 64, 512, 2)),     # 4 KiB rows: diagonal
+    ("bf16", [64, 512, 1024], [0, 2, 1], (64, 64, 512, 0)),  # 2 KiB rows
+    ("bf16", [2048, 16384], [1, 0], (64, 64, 512, 0)),     # 256 W-tiles, 32 U-tiles
+]
+
+
+@pytest.mark.parametrize("dt,dims,perm,want", TRANSPOSE_GEOMETRY,
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, list) else str(v))
+def test_transpose_geometry_choice(dt, dims, perm, want):
+    """Tile shape, threads and tile order as measured best: the narrow
+    32x128 tile for 4-byte types with power-of-two rows (of 512 B to 4 KiB
+    only when it makes 2048 workgroups or more), the diagonal order from
+    4 KiB rows while the U-tiles number at least half the W-tiles, U fastest
+    otherwise, W fastest for the narrow tile on 4 KiB rows, and the
+    XCD-contiguous order for rows that are not whole 128-byte lines."""
+    s = W.Spec()
+    x = s.parameter(0, dt, dims)
+    e = s.unary("exponential", x, dt, dims)
+    s.transpose(e, perm, dt, [dims[p] for p in perm])
+    src = H.Fusion(s.nodes, mode="compile").source()
+    m = {k: int(v) for k, v in re.findall(r"#define (HF_TU|HF_TW|HF_BLOCK|HF_ORDER) (\d+)", src)}
+    assert (m["HF_TU"], m["HF_TW"], m["HF_BLOCK"], m["HF_ORDER"]) == want
+
+
+@pytest.mark.parametrize("dims,grid,block", [([65536, 256], 2048, 256), ([262144, 64], 2048, 256),
+                                             ([1048576, 16], 2048, 256), ([300, 256], 75, 256),
+                                             ([16384, 1024], 16384, 256), ([10240, 4096], 10240, 512)])
+def test_row_reduce_grid_choice(dims, grid, block):
+    """Row reduces: whole-row workgroups one per row (up to 65,536); rows of
+    fewer than 256 vectors share workgroups of 256 threads, which loop over
+    the rows in a grid of at most 2048 (one round of 32 waves on each of the
+    256 CUs)."""
+    s = W.Spec()
+    p = s.parameter(0, "f32", dims)
+    s.reduce(p, [1], "add", 0.0, "f32", [dims[0]])
+    pl = plan_of(s)
+    assert pl["hero"] == "row_reduce" and (pl["grid_blocks"], pl["block_threads"]) == (grid, block)
+
+
 # --------------------------------------------------------------------------
 # code generation and compilation for gfx950
 # --------------------------------------------------------------------------
