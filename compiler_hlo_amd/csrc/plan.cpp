@@ -657,7 +657,8 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     // and 68% -> 71% on f32[8192,2048]; other strides and 2-byte types keep
     // 64x64 (the narrow tile lost 2% on f32[4160,4160] and more on bf16).
     // Shorter power-of-two rows (512 B to 4 KiB) take it too when it makes
-    // 2048 workgroups or more: f32[65536,256] 26.6 -> 24.2 us,
+    // 2048 workgroups or more of whole 32-wide U extents (the shapes
+    // measured): f32[65536,256] 26.6 -> 24.2 us,
     // f32[131072,128] 28.6 -> 24.2, f32[32768,1024] 54.0 -> 46.8; rows of
     // 2 KiB tie or lose a little (f32[32768,512] 23.9 -> 24.0 us,
     // f32[16384,512] 13.0 -> 13.2), and f32[4096,1024], a grid of 1024, ran
@@ -665,7 +666,7 @@ bool try_transpose(const Graph &g, const Ctx &loop, Plan *out) {
     const long long nb = rt.numel() / (DU * DW);
     const bool pow2_rows = in_row_bytes >= 512 && (in_row_bytes & (in_row_bytes - 1)) == 0;
     const bool narrow = pow2_rows && vin == 4 && vout == 4 &&
-                        (in_row_bytes >= 8192 || nb * ceil_div(DU, 32) * ceil_div(DW, 128) >= 2048);
+                        (in_row_bytes >= 8192 || (DU >= 32 && nb * ceil_div(DU, 32) * ceil_div(DW, 128) >= 2048));
     int tu = (int)std::min<long long>(env_ll("HF_TR_TU", narrow ? 32 : 64), pow2_ceil(DU));
     int tw = (int)std::min<long long>(env_ll("HF_TR_TW", narrow ? 128 : 64), pow2_ceil(DW));
     // A tiling that would leave fewer than two workgroups per CU (256 CUs)

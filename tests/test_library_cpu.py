@@ -639,6 +639,7 @@ TRANSPOSE_GEOMETRY = [
     ("f32", [16384, 1024], [1, 0], (32, 128, 1024, 1)),    # narrow on 4 KiB rows: W fastest
     ("f32", [65536, 256], [1, 0], (32, 128, 1024, 0)),     # narrow on 1 KiB rows
     ("f32", [32768, 512], [1, 0], (32, 128, 1024, 0)),
+    ("f32", [4096, 8, 256], [0, 2, 1], (8, 64, 256, 0)),   # U extent 8: no narrow tile
     ("f32", [4096, 1024], [1, 0], (64, 64, 512, 2)),       # narrow would make 1024 WGs
     ("f32", [4160, 4160], [1, 0], (64, 64, 512, 2)),       # not a power of two
     ("f32", [20, 160, 170], [2, 1, 0], (32, 32, 512, 3)),  # rows of 680 B; small grid
@@ -653,7 +654,8 @@ TRANSPOSE_GEOMETRY = [
 def test_transpose_geometry_choice(dt, dims, perm, want):
     """Tile shape, threads and tile order as measured best: the narrow
     32x128 tile for 4-byte types with power-of-two rows (of 512 B to 4 KiB
-    only when it makes 2048 workgroups or more), the diagonal order from
+    only when it makes 2048 workgroups or more over U extents of 32 or
+    more), the diagonal order from
     4 KiB rows while the U-tiles number at least half the W-tiles, U fastest
     otherwise, W fastest for the narrow tile on 4 KiB rows, and the
     XCD-contiguous order for rows that are not whole 128-byte lines."""
