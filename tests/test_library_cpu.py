@@ -496,6 +496,30 @@ def test_loop_pipeline_choice():
     assert (m["HF_NR"], m["HF_RSTEP"]) == (16, 256) and 15 * 256 < 4091
 
 
+def test_loop_rows_per_thread_choice():
+    """A loop that holds small arrays in registers over its rows: four rows a
+    thread for per-axis quantization data (the s4 requantize: 4096
+    workgroups), two for a broadcast f32 bias and one for a bf16 one, which
+    leaves x + bias with the grid of the plain elementwise loop (f32: half
+    of it)."""
+    def bias(dt, bdim):
+        s = W.Spec()
+        x = s.parameter(0, dt, [4096, 4096])
+        b = s.parameter(1, dt, [4096])
+        s.binary("add", x, s.broadcast_in_dim(b, [bdim], dt, [4096, 4096]), dt, [4096, 4096])
+        return s
+
+    def neg(dt):
+        s = W.Spec()
+        s.unary("negate", s.parameter(0, dt, [4096, 4096]), dt, [4096, 4096])
+        return s
+    assert plan_of(neg("f32"))["grid_blocks"] == 16384 and plan_of(neg("bf16"))["grid_blocks"] == 8192
+    for bdim in (0, 1):
+        assert plan_of(bias("f32", bdim))["grid_blocks"] == 8192
+        assert plan_of(bias("bf16", bdim))["grid_blocks"] == 8192
+    assert plan_of(W.quant_dequant_bias_requant_s4()[0])["grid_blocks"] == 4096
+
+
 def test_slice_plans():
     """A slice keeps 128-bit lanes when its start along the minor dim is a
     multiple of the vector width and counts only the elements it reads; a
