@@ -294,7 +294,8 @@ def test_transpose_exp_small(n0, n1):
                                                   ([8, 4100, 256], [0, 2, 1], (128, 32), 1024),
                                                   ([2052, 8192], [1, 0], (128, 32), 1024),
                                                   ([1000, 32768], [1, 0], (128, 32), 1024),
-                                                  ([1000, 1024], [1, 0], (32, 32), 256)])
+                                                  ([1000, 1024], [1, 0], (32, 32), 256),
+                                                  ([100004, 128], [1, 0], (128, 32), 1024)])
 def test_transpose_narrow_tiles(dims, perm, tile, block):
     """f32 transposes whose input rows lie a power of two (>= 8 KiB) apart take
     tiles 128 wide in the load and up to 32 in the store, with 1024 threads
@@ -303,8 +304,8 @@ def test_transpose_narrow_tiles(dims, perm, tile, block):
     256 and takes 32x32 tiles).  The tile orders run here: W fastest (4 KiB
     rows), diagonal (f32[2052,8192]), U fastest (f32[65536,256],
     f32[1000,32768]).
-    Ragged U extents (100, 36, 16380, 4100, 2052, 1000) take the
-    bounds-checked path.  The exp before the tile is checked against the
+    Ragged U extents (100, 36, 16380, 4100, 2052, 1000, 100004) take the
+    bounds-checked path; rows of 128 floats are a single W-tile.  The exp before the tile is checked against the
     oracle and bitwise against the same exp through the loop hero, transposed
     on the host."""
     say("transpose narrow tiles", dims, perm)
@@ -363,6 +364,18 @@ def test_transpose_bf16_small(b, m, n):
     say("transpose bf16", b, m, n)
     spec, params, _ = W.transpose_bf16_021(b, m, n, seed=30 + m)
     got, _ = run_gpu(spec.nodes, params)
+    assert_bitexact(got, oracle.evaluate(spec.nodes, params), "bf16")
+
+
+@pytest.mark.parametrize("b,m,n,order", [(1, 4100, 2048, 2), (2, 1000, 16384, 0)])
+def test_transpose_bf16_tile_orders(b, m, n, order):
+    """bf16 transposes in the diagonal order (rows of 4 KiB, 65 U-tiles for
+    32 W-tiles, the last U-tile ragged) and in U-fastest order (rows of
+    32 KiB, 256 W-tiles for 16 U-tiles), bit-exact against the oracle."""
+    say("transpose bf16 tile order", b, m, n, order)
+    spec, params, _ = W.transpose_bf16_021(b, m, n, seed=31 + order)
+    got, f = run_gpu(spec.nodes, params)
+    assert f"#define HF_ORDER {order}\n" in f.source()
     assert_bitexact(got, oracle.evaluate(spec.nodes, params), "bf16")
 
 
