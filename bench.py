@@ -240,8 +240,9 @@ SETTLE_SECONDS = 0.25
 def settle(cases, seconds=SETTLE_SECONDS):
     """Run the cases, untimed, for `seconds` of wall time.  After an idle gap
     (a kernel compile, a host-side step) the GPU's clocks take a few tens of
-    milliseconds of load to return to their sustained level: measured on C3,
-    the first ~25 ms of launches ran 10-30% slower.  A timing that starts cold
+    milliseconds of load to return to their sustained level: measured on the
+    row sum of exp(x) + bias over bf16[8,1,1280,16384], the first ~25 ms of
+    launches ran 10-30% slower.  A timing that starts cold
     measures that ramp instead of the kernel."""
     import torch
     stream = torch.cuda.current_stream()

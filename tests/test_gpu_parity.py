@@ -380,8 +380,8 @@ def test_transpose_bf16_tile_orders(b, m, n, order):
 
 
 def test_transpose_bf16_full():
-    """C2b at full size: all 33,554,432 outputs against the oracle's whole
-    evaluation, bit-exact."""
+    """The {0,2,1} transpose of bf16[64,512,1024] at full size: all
+    33,554,432 outputs against the oracle's whole evaluation, bit-exact."""
     spec, params, _ = W.transpose_bf16_021()
     say("transpose bf16 full")
     got, f = run_gpu(spec.nodes, params, reps=2)
@@ -417,9 +417,10 @@ def test_row_reduce_small(d0, d2, d3):
 
 
 def test_row_reduce_full_every_row_and_layout_invariant():
-    """C3 at full size: every one of the 10,240 sums within 1e-5 * sum|y| of
-    the oracle's long-double sum (the oracle runs on the host's cores in
-    parallel, a chunk of rows per thread)."""
+    """The row sum of exp(x) + bias over bf16[8,1,1280,16384] at full size:
+    every one of the 10,240 sums within 1e-5 * sum|y| of the oracle's
+    long-double sum (the oracle runs on the host's cores in parallel, a chunk
+    of rows per thread)."""
     import time
     spec, params, _ = W.row_reduce_exp_add_bf16()
     say("row reduce full")
@@ -1469,7 +1470,8 @@ def test_exp_bf16_exhaustive():
     d = assert_ulp(got, oracle.evaluate(s.nodes, [allbits]), "bf16", 1)
     off = int((d > 0).sum())
     say("bf16 exp: %d of 65536 inputs 1 ulp off" % off)
-    # measured: 2 inputs; more would move C3's sums and the bf16 exp fusions
+    # measured: 2 inputs; more would move the bf16 exp + bias row sums and the
+    # bf16 exp fusions
     assert off <= 2, off
 
 

@@ -476,9 +476,10 @@ def test_loop_pipeline_choice():
     """The loop's software pipeline goes to single-partition fusions of 8-bit
     streams with 16 elements a lane: the per-axis requantize (six rows in
     flight, sixteen rows a thread, 256 workgroups) and the quantized add (four
-    in flight); GELU, the si4 requantize and C1 keep the plain loop.  In the
-    pipelined source the column data load into their own struct (hf_I_),
-    pinned after the first row, and the compute takes it."""
+    in flight); GELU, the si4 requantize and log(x) + transpose(log(x)) keep
+    the plain loop.  In the pipelined source the column data load into their
+    own struct (hf_I_), pinned after the first row, and the compute takes
+    it."""
     def macros(spec):
         src = H.Fusion(spec.nodes, mode="compile").source()
         return {k: int(v) for k, v in re.findall(r"#define (HF_PIPE|HF_NR|HF_RSTEP) (\d+)", src)}, src
