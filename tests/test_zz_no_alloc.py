@@ -1,9 +1,9 @@
 """hf_fusion_launch_noalloc, the launch that allocates nothing: its output
 equals hf_fusion_launch's (with a caller workspace) bit for bit, on two
 calls in a row, the second with a smaller input, through the C ABI.  The
-column reduces below are split into segments, so their launches use the
-library's scratch memory; a loop needs none.  A plan whose workspace
-exceeds the scratch memory is rejected."""
+column reduces and the row reduces of a few long rows below are split into
+segments, so their launches use the library's scratch memory; a loop needs
+none.  A plan whose workspace exceeds the scratch memory is rejected."""
 import numpy as np
 import pytest
 
@@ -73,6 +73,32 @@ def test_noalloc_sum_and_argmax_and_no_workspace():
     got, ref, f = _both(spec, params)
     assert f.workspace_bytes == 0
     assert np.array_equal(got, ref)
+
+
+def test_noalloc_split_rows():
+    """Row reduces of a few long rows, split into segments whose partials
+    (for argmax, values and indices) go to the scratch: an integer-valued
+    sum of f32[16,1048576] (exact in any order), then the argmax of the
+    smaller f32[4,262144]."""
+    g = W.rng(505)
+    print("noalloc: row sum f32[16,1048576] split", flush=True)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [16, 1048576])
+    s.reduce(p, [1], "add", 0.0, "f32", [16])
+    x = g.integers(-4, 4, 16 * 1048576, endpoint=True).astype(np.float32)
+    got, ref, f = _both(s, [x])
+    assert f.plan()["hero"] == "row_reduce" and f.workspace_bytes > 0
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "f32")
+    print("noalloc: row argmax f32[4,262144] split", flush=True)
+    s = W.Spec()
+    p = s.parameter(0, "f32", [4, 262144])
+    s.argmax(p, 1, [4, 262144])
+    x = W.normal_f32(g, 4 * 262144)
+    got, ref, f = _both(s, [x])
+    assert f.plan()["hero"] == "row_reduce" and f.workspace_bytes > 0
+    assert np.array_equal(got, ref)
+    assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32")
 
 
 def test_noalloc_rejects_a_workspace_beyond_the_scratch(monkeypatch):
