@@ -869,10 +869,15 @@ Plan plan_reduce(const Graph &g) {
     // rows per step: their loads go out together, and what the prologue reads
     // along the row (a broadcast bias) is loaded once for all of them.
     // Two rows per step for rows of eight or more chunks per thread (measured
-    // faster there; shorter rows gained nothing or lost).
+    // faster there; two or four chunks gained nothing or lost: f32[4096,4096]
+    // 11.08 -> 11.13 us, f32[2048,8192] 11.07 -> 11.44), and for rows of one
+    // chunk per thread, whose single load a thread leaves HBM waiting:
+    // f32[8192,2048] 11.95 -> 11.12 us, f32[16384,1024] 11.44 -> 11.04,
+    // f32[32768,1024] 20.69 -> 20.34.
     long long rr = 1;
     if (segs == 1 && tpr == block && kv % block == 0 && op != HF_REDUCER_ARGMAX)
-      rr = std::max<long long>(1, std::min<long long>(env_ll("HF_ROW_RPS", kv / block >= 8 ? 2 : 1), 4));
+      rr = std::max<long long>(
+          1, std::min<long long>(env_ll("HF_ROW_RPS", kv / block >= 8 || kv == block ? 2 : 1), 4));
     long long pipe = 0;
     if (rr == 1 && tpr == block && kv % block == 0 && kv / block <= 8 && op != HF_REDUCER_ARGMAX)
       pipe = env_ll("HF_ROW_PIPE", 0) ? 1 : 0;

@@ -439,14 +439,15 @@ def test_row_reduce_full_every_row_and_layout_invariant():
 def test_row_reduce_one_workgroup_per_row_and_past_the_cap(rows):
     """Whole-row workgroups take one row each up to 65,536 workgroups; past
     that the grid strides, so 70,001 rows leave 4,465 workgroups a second
-    row.  Integer-valued f32 rows of 1024 (exact sums), bit-exact; a max over
-    the same rows through the same grid."""
+    row.  Integer-valued f32 rows of 1028 (257 chunks over 256 threads, so
+    one row a step; exact sums), bit-exact; a max over the same rows
+    through the same grid."""
     say("row reduce rows", rows)
     g = W.rng(54)
-    x = W.integers(g, rows * 1024, -1000, 1000, np.int64).astype(np.float32)
+    x = W.integers(g, rows * 1028, -1000, 1000, np.int64).astype(np.float32)
     for red, init in (("add", 0.0), ("max", float("-inf"))):
         s = W.Spec()
-        p = s.parameter(0, "f32", [rows, 1024])
+        p = s.parameter(0, "f32", [rows, 1028])
         s.reduce(p, [1], red, init, "f32", [rows])
         got, f = run_gpu(s.nodes, [x])
         assert f.plan()["hero"] == "row_reduce" and f.plan()["grid_blocks"] == 65536
@@ -548,16 +549,16 @@ def test_row_reduce_many_short_rows(rows, cols):
 
 @pytest.mark.parametrize("d0,d2,d3", [(1, 5, 32768), (3, 3, 36864)])
 def test_row_reduce_two_rows_per_step(d0, d2, d3):
-    """Rows of eight or more chunks per thread are reduced two per workgroup
-    step: odd row counts leave one row in the last step, and 36864 (nine
-    chunks) leaves a partial batch of loads."""
+    """Rows of eight or more chunks per thread, and rows of exactly one, are
+    reduced two per workgroup step: odd row counts leave one row in the last
+    step, and 36864 (nine chunks) leaves a partial batch of loads."""
     say("row reduce two rows per step", d0, d2, d3)
     spec, params, _ = W.row_reduce_exp_add_bf16(d0, d2, d3, seed=50 + d2)
     got, f = run_gpu(spec.nodes, params)
     assert "#define HF_RR_ROWS 2" in f.source()
     _check_sum(got, spec, params, [[a, 0, c] for a in range(d0) for c in range(d2)])
     g = W.rng(51)
-    for rows, cols, red in ((37, 16384, "max"), (7, 20480, "add")):
+    for rows, cols, red in ((37, 16384, "max"), (7, 20480, "add"), (4097, 2048, "add"), (4099, 1024, "max")):
         x = W.integers(g, rows * cols, -1000, 1000, np.int64).astype(np.float32)  # exact sums
         s = W.Spec()
         p = s.parameter(0, "f32", [rows, cols])

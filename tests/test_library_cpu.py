@@ -695,12 +695,15 @@ def test_transpose_geometry_choice(dt, dims, perm, want):
 
 @pytest.mark.parametrize("dims,grid,block", [([65536, 256], 2048, 256), ([262144, 64], 2048, 256),
                                              ([1048576, 16], 2048, 256), ([300, 256], 75, 256),
-                                             ([16384, 1024], 16384, 256), ([10240, 4096], 10240, 512)])
+                                             ([16384, 1024], 8192, 256), ([8192, 2048], 4096, 512),
+                                             ([4096, 4096], 4096, 512), ([10240, 4096], 10240, 512),
+                                             ([2048, 16384], 1024, 512)])
 def test_row_reduce_grid_choice(dims, grid, block):
-    """Row reduces: whole-row workgroups one per row (up to 65,536); rows of
-    fewer than 256 vectors share workgroups of 256 threads, which loop over
-    the rows in a grid of at most 2048 (one round of 32 waves on each of the
-    256 CUs)."""
+    """Row reduces: whole-row workgroups one per row step (up to 65,536),
+    two rows a step where each thread holds one chunk of a row or eight and
+    more, one row otherwise; rows of fewer than 256 vectors share workgroups
+    of 256 threads, which loop over the rows in a grid of at most 2048 (one
+    round of 32 waves on each of the 256 CUs)."""
     s = W.Spec()
     p = s.parameter(0, "f32", dims)
     s.reduce(p, [1], "add", 0.0, "f32", [dims[0]])
