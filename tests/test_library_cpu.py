@@ -521,6 +521,24 @@ def test_loop_rows_per_thread_choice():
     assert plan_of(W.quant_dequant_bias_requant_s4()[0])["grid_blocks"] == 4096
 
 
+def test_lane_moving_maps_keep_vector_lanes_and_guard_their_loads():
+    """concatenate(pad(x), reverse(y)) along the minor dim of f32[4096,4096]:
+    the index maps move with the lane, yet the loop keeps 4-wide lanes and
+    reads each lane's element on its own (index at lane base + l); every
+    load whose index holds a pad or concatenate clamp is issued only where
+    each clamp is the identity, and fills zeros elsewhere."""
+    spec = W.pad_reverse_concat_minor_f32()[0]
+    f = H.Fusion(spec.nodes, mode="compile")
+    p, src = f.plan(), f.source()
+    assert p["hero"] == "loop" and p["vector_elems"] == 4
+    lanes = [ln.strip() for ln in src.splitlines() if ln.strip().startswith("for (int l = 0; l < 4; ++l) R.")]
+    assert len(lanes) == 2, lanes
+    for ln in lanes:
+        assert "(i1 + l)" in ln and "? A.p" in ln and ln.endswith(": 0;"), ln
+    # y is read only where the concatenate's clamp on it is the identity
+    assert "((i1 + l) - 2048) >= (0) && ((i1 + l) - 2048) <= (2047)" in lanes[1]
+
+
 def test_slice_plans():
     """A slice keeps 128-bit lanes when its start along the minor dim is a
     multiple of the vector width and counts only the elements it reads; a
