@@ -729,6 +729,30 @@ def test_row_reduce_grid_choice(dims, grid, block):
     assert pl["hero"] == "row_reduce" and (pl["grid_blocks"], pl["block_threads"]) == (grid, block)
 
 
+@pytest.mark.parametrize("dims,grid,rows_per_seg,cols_per_wg", [
+    ([16384, 4096], 4096, 128, 128),   # 32 column lanes of 4; 128 segments of 128 rows
+    ([4096, 4096], 1024, 128, 128),    # segments of at least 128 rows
+    ([16384, 1024], 2048, 128, 64),    # 2048 columns or fewer: 16 column lanes
+    ([65536, 256], 1024, 256, 64),     # at most 256 segments
+    ([262144, 64], 256, 1024, 64),
+    ([1048576, 16], 256, 4096, 16),    # 4 column lanes cover the 16 columns
+    ([100, 4096], 32, 100, 128),       # one segment: no workspace, no fold
+])
+def test_column_reduce_geometry_choice(dims, grid, rows_per_seg, cols_per_wg):
+    """Column reduces: workgroups of 128 columns (32 lanes of four) or, for
+    2048 columns or fewer, of 64; the rows split into at most 256 segments
+    of at least 128 rows, toward 4096 workgroups; a workspace of one partial
+    per segment and column only when there are two segments or more."""
+    s = W.Spec()
+    p = s.parameter(0, "f32", dims)
+    s.reduce(p, [0], "max", float("-inf"), "f32", [dims[1]])
+    pl = plan_of(s)
+    assert pl["hero"] == "column_reduce"
+    assert (pl["grid_blocks"], pl["tile_rows"], pl["tile_cols"]) == (grid, rows_per_seg, cols_per_wg)
+    segs = -(-dims[0] // rows_per_seg)
+    assert pl["workspace_bytes"] == (segs * dims[1] * 4 if segs > 1 else 0)
+
+
 # --------------------------------------------------------------------------
 # code generation and compilation for gfx950
 # --------------------------------------------------------------------------
