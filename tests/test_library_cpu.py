@@ -753,6 +753,30 @@ def test_column_reduce_geometry_choice(dims, grid, rows_per_seg, cols_per_wg):
     assert pl["workspace_bytes"] == (segs * dims[1] * 4 if segs > 1 else 0)
 
 
+@pytest.mark.parametrize("dims,red,segs,grid,ws", [
+    ([16, 1048576], "add", 64, 1024, 16 * 64 * 4),
+    ([1, 16777216], "add", 1024, 1024, 1024 * 4),    # one row: 1024 segments
+    ([64, 65536], "add", 4, 256, 64 * 4 * 4),        # segments of one batch of loads at least
+    ([4, 262144], "argmax", 32, 128, 4 * 32 * 8),    # values and indices
+    ([2048, 4096], "add", 1, 2048, 0),               # enough rows: no split
+])
+def test_row_reduce_split_choice(dims, red, segs, grid, ws):
+    """A few long rows split into segments toward 2048 workgroups, each
+    segment at least eight chunks a thread; the workspace holds a partial
+    per row and segment (with its index for argmax), folded by one
+    workgroup per row."""
+    s = W.Spec()
+    p = s.parameter(0, "f32", dims)
+    if red == "argmax":
+        s.argmax(p, 1, dims)
+    else:
+        s.reduce(p, [1], "add", 0.0, "f32", [dims[0]])
+    f = H.Fusion(s.nodes, mode="compile")
+    pl, src = f.plan(), f.source()
+    assert "#define HF_RSEG %d\n" % segs in src
+    assert (pl["grid_blocks"], pl["workspace_bytes"]) == (grid, ws)
+
+
 # --------------------------------------------------------------------------
 # code generation and compilation for gfx950
 # --------------------------------------------------------------------------
