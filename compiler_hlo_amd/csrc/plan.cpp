@@ -511,7 +511,14 @@ Plan plan_loop(const Graph &g, Ctx c) {
   // (128 lanes for one element a lane: reverse and concatenate along the
   // minor dim of f32[4096,4096] took 27.7 and 55.1 us against 29.4 and 59.2
   // with 64.)
-  const long long tpr_cap = env_ll("HF_LOOP_TPR", V == 1 ? 128 : 64);
+  // (Rows of 2 MiB or more take whole-workgroup row segments again: four
+  // waves on four such rows read at equal offsets megabytes apart.  A negate
+  // over f32[4,4194304], [8,2097152], [16,1048576] and [32,524288] took
+  // 27.2, 25.7, 24.8 and 24.5 us with 64 lanes and 22.7-23.0 with 256, and
+  // bf16[16,1048576] 14.0 against 13.1; rows of 1 MiB lost 1-2% with 256
+  // lanes: f32[64,262144] 22.6 -> 22.9 us, bf16[32,524288] 12.8 -> 13.0.)
+  const bool long_rows = V > 1 && DL * (long long)wbits_all / 8 >= (2LL << 20);
+  const long long tpr_cap = env_ll("HF_LOOP_TPR", V == 1 ? 128 : long_rows ? 256 : 64);
   if (cols_v >= tpr_cap) {
     tpr = tpr_cap;
     rpb = block / tpr;

@@ -526,6 +526,26 @@ def test_row_reduce_one_wave_per_row(rows, cols):
         assert_bitexact(got, oracle.evaluate(s.nodes, [x]), "s32" if red == "argmax" else "f32")
 
 
+@pytest.mark.parametrize("dt,rows,cols", [("f32", 7, 524292), ("bf16", 5, 1048580), ("f32", 3, 512004)])
+def test_loop_long_rows(dt, rows, cols):
+    """Rows of 2 MiB or more run whole-workgroup row segments (256 lanes);
+    x + a broadcast bias along the row, with an odd row count and a ragged
+    last segment, bit-exact against the oracle (rows of 2 MiB + 16 and
+    2 MiB + 8 bytes; f32 rows of 2,048,016 bytes keep 64 lanes)."""
+    say("loop long rows", dt, rows, cols)
+    g = W.rng(58 + rows)
+    s = W.Spec()
+    x = s.parameter(0, dt, [rows, cols])
+    b = s.parameter(1, dt, [cols])
+    s.binary("add", x, s.broadcast_in_dim(b, [1], dt, [rows, cols]), dt, [rows, cols])
+    mk = W.normal_f32 if dt == "f32" else W.normal_bf16
+    params = [mk(g, rows * cols), mk(g, cols)]
+    got, f = run_gpu(s.nodes, params)
+    lanes = 256 if cols * (4 if dt == "f32" else 2) >= 2 << 20 else 64
+    assert f.plan()["hero"] == "loop" and "#define HF_TPR %d\n" % lanes in f.source()
+    assert_bitexact(got, oracle.evaluate(s.nodes, params), dt)
+
+
 @pytest.mark.parametrize("rows,cols", [(262147, 64), (1048583, 16), (300001, 12)])
 def test_row_reduce_many_short_rows(rows, cols):
     """Rows of fewer than 64 vectors share a wave (16, 4 and 3 vectors a

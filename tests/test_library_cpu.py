@@ -519,6 +519,12 @@ def test_loop_rows_per_thread_choice():
         assert plan_of(bias("f32", bdim))["grid_blocks"] == 8192
         assert plan_of(bias("bf16", bdim))["grid_blocks"] == 8192
     assert plan_of(W.quant_dequant_bias_requant_s4()[0])["grid_blocks"] == 4096
+    # rows of 2 MiB or more: whole-workgroup row segments (256 lanes)
+    for dt, rows, cols, lanes in (("f32", 16, 1 << 20, 256), ("f32", 64, 1 << 18, 64),
+                                  ("bf16", 16, 1 << 20, 256), ("bf16", 32, 1 << 19, 64)):
+        s = W.Spec()
+        s.unary("negate", s.parameter(0, dt, [rows, cols]), dt, [rows, cols])
+        assert "#define HF_TPR %d\n" % lanes in H.Fusion(s.nodes, mode="compile").source()
 
 
 def test_lane_moving_maps_keep_vector_lanes_and_guard_their_loads():
